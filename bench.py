@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""FP32 GEMM throughput on one MI355X, through the C ABI.
+
+One step is one call of gemm_f32 (C = A x B, row-major FP32) on the
+workload's operands, which are resident in HBM before timing starts.  The
+default workload is M = N = K = 8192 with uniform[-1, 1) inputs from seed 0.
+
+Prints ONE JSON line with the throughput (TFLOP/s = 2 M N K / time), the
+dominant kernel's roofline position (measured live with HIP events on the
+stream the kernel runs on), the oracle timed on the host's cores on a bounded
+sample of the same workload, and a parity check of the timed output.
+
+Other modes (results on stderr / in a file, not the contract line):
+  --stages   time every kernel stage (naive, LDS-tiled, register-blocked,
+             MFMA) on the workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP32_MATRIX_TFLOPS = 157.3  # MI355X: 256 CU x 4 SIMD x 64 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "FP32 GEMM TFLOP/s at M=N=K=8192 on 1 MI355X; % of FP32 matrix peak"
+KERNEL_SOURCES = ["dense_fp32_gemm_row_amd/csrc/mfma.hip",
+                  "dense_fp32_gemm_row_amd/csrc/gemm_internal.h"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_fingerprint(config_name: str) -> str:
+    h = hashlib.sha256(config_name.encode())
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, config_name: str) -> float | None:
+    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled against a copy kernel of known size), as recorded in
+    profiles/; None when no record exists or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config_name}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    fp = re.search(r"kernel_fingerprint:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not fp or not val or fp.group(1) != kernel_fingerprint(config_name):
+        return None
+    return float(val.group(1))
+
+
+def time_launches(fn, steps: int, warmup: int, stream):
+    """Runs fn() warmup times, then `steps` times with an event pair around
+    each launch on `stream`.  Returns (total_ms, per-launch ms list)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total = starts[0].elapsed_time(ends[-1])
+    return total, per
+
+
+def cpu_baseline(A, B, target_s: float) -> dict:
+    """The oracle, as it stands, on a bounded sample of rows of the same
+    product, timed with the host's default OpenMP thread count."""
+    import numpy as np
+
+    import oracle
+
+    M, K = A.shape
+    N = B.shape[1]
+    threads = oracle.default_threads()
+    probe = list(range(threads))
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, rows=probe, threads=threads)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n = int(min(M, max(threads, target_s / max(per_row, 1e-9))))
+    n = max(threads, n - n % threads) if n < M else M
+    rng_rows = sorted(set(np.linspace(0, M - 1, n).astype(np.int64).tolist()))
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, rows=rng_rows, threads=threads)
+    t = time.perf_counter() - t0
+    flops = 2.0 * len(rng_rows) * N * K
+    return {
+        "value": round(flops / t / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(rng_rows)} of {M} output rows (evenly spaced), each a full "
+                  f"{K}x{N} sweep; {t:.1f} s wall, FP64 accumulation",
+    }
+
+
+def parity_check(A, B, C) -> dict:
+    """Sampled rows against the oracle plus a Freivalds projection."""
+    import numpy as np
+
+    import oracle
+
+    M, K = A.shape
+    rng = np.random.default_rng(1)
+    rows = sorted(set([0, M - 1] + [int(r) for r in rng.integers(0, M, size=14)]))
+    _, ref = oracle.gemm(A, B, rows=rows, return_f64=True)
+    got = C[rows].astype(np.float64)
+    max_err = float(np.abs(got - ref).max())
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    x = rng.choice([-1.0, 1.0], size=B.shape[1])
+    fr_ref = A.astype(np.float64) @ (B.astype(np.float64) @ x)
+    fr = float(np.linalg.norm(C.astype(np.float64) @ x - fr_ref) / np.linalg.norm(fr_ref))
+    ok = (not np.isnan(C).any()) and max_err <= 1e-4 * math.sqrt(K) and rel <= 1e-5 and fr <= 1e-5
+    return {"rows": len(rows), "max_abs_err": max_err, "rel_fro": rel, "freivalds": fr,
+            "tol_max": 1e-4 * math.sqrt(K), "tol_rel": 1e-5, "ok": bool(ok)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="square8192")
+    ap.add_argument("--variant", default=None, help="naive|lds|regblock|mfma (default: library choice)")
+    ap.add_argument("--config", default=None, help="configuration name of the variant")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--stages", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from dense_fp32_gemm_row_amd import binding
+    from dense_fp32_gemm_row_amd.workloads import WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    binding.load()
+    w = WORKLOADS[args.workload]
+    M, N, K = w.M, w.N, w.K
+    log(f"workload {w.name}: M={M} N={N} K={K} dist={w.dist}")
+    A, B = workload_inputs(w.name)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.empty((M, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    flops = 2.0 * M * N * K
+
+    if args.stages:
+        return run_stages(args, w, A, B, dA, dB, dC, stream, flops)
+
+    if args.variant is None:
+        v, c = binding.gemm_f32_select(M, N, K, K, N, N)
+    else:
+        v = binding.VARIANTS[args.variant]
+        if args.config:
+            c = binding.config_id(v, args.config)
+        elif v == binding.VARIANT_MFMA:
+            c = binding.gemm_f32_select(M, N, K, K, N, N)[1]
+        else:
+            c = 0
+    cname = binding.gemm_f32_config_name(v, c)
+    log(f"kernel {cname}")
+
+    if args.variant is None:
+        fn = lambda: binding.gemm(dA, dB, dC)  # noqa: E731  (gemm_f32)
+    else:
+        fn = lambda: binding.gemm(dA, dB, dC, variant=v, config=c)  # noqa: E731
+
+    total_ms, per = time_launches(fn, args.steps, args.warmup, stream)
+    ms_step = total_ms / args.steps
+    avg_launch_ms = sum(per) / len(per)
+    value = flops * args.steps / (total_ms / 1e3) / 1e12
+    achieved = flops / (avg_launch_ms / 1e3) / 1e12
+    log(f"{args.steps} steps: {ms_step:.3f} ms/step, {value:.2f} TFLOP/s "
+        f"(avg launch {avg_launch_ms:.3f} ms, min {min(per):.3f}, max {max(per):.3f})")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_FP32_MATRIX_TFLOPS, 2),
+        "config": {"workload": w.name, "M": M, "N": N, "K": K, "dist": w.dist, "seed": w.seed,
+                   "layout": "row-major A, B, C", "kernel": cname, "parallelism": "none"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_FP32_MATRIX_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
+            "traffic": read_traffic(w.name, cname),
+            "kernel": cname,
+            "avg_launch_ms": round(avg_launch_ms, 4),
+            "flops_per_launch": flops,
+        },
+    }
+
+    rc = 0
+    if not args.no_check:
+        C = dC.cpu().numpy()
+        result["parity"] = parity_check(A, B, C)
+        log(f"parity {result['parity']}")
+        if not result["parity"]["ok"]:
+            rc = 1
+        del C
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
+        log(f"cpu baseline {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return rc
+
+
+def run_stages(args, w, A, B, dA, dB, dC, stream, flops) -> int:
+    """Per-stage timing: every compiled configuration of every variant."""
+    from dense_fp32_gemm_row_amd import binding
+
+    out = []
+    for v in range(4):
+        for c in range(binding.gemm_f32_config_count(v)):
+            name = binding.gemm_f32_config_name(v, c)
+            steps = args.steps if v >= 2 else max(2, min(args.steps, 3))
+            fn = lambda: binding.gemm(dA, dB, dC, variant=v, config=c)  # noqa: E731
+            total, per = time_launches(fn, steps, 1, stream)
+            avg = sum(per) / len(per)
+            tf = flops / (avg / 1e3) / 1e12
+            rec = {"workload": w.name, "variant": v, "config": name, "avg_ms": round(avg, 4),
+                   "min_ms": round(min(per), 4), "tflops": round(tf, 3),
+                   "pct_peak": round(100 * tf / PEAK_FP32_MATRIX_TFLOPS, 2)}
+            out.append(rec)
+            log(json.dumps(rec))
+    print(json.dumps({"stages": out}), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,236 @@
+// C-ABI entry points of libgemm_f32.so (declared in include/gemm_f32.h).
+//
+// The host workflow of "Tiled GEMM: Matrix Multiplication in CUDA",
+// section 6 (allocate, copy in, launch asynchronously, copy back, free) is
+// split at the launch: the caller owns allocation, copies and
+// synchronisation; this library validates the arguments, picks a kernel and
+// enqueues it on the caller's stream.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/gemm_f32.h"
+#include "gemm_internal.h"
+#include "tune_table.inc"
+
+namespace gemm_f32_impl {
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(float *__restrict__ C, int M, int N,
+                                                        int64_t ldc) {
+    const int64_t total = static_cast<int64_t>(M) * N;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t i = e / N, j = e - i * N;
+        C[i * ldc + j] = 0.0f;
+    }
+}
+
+const ConfigEntry *configs_of(int variant, int *count) {
+    switch (variant) {
+        case GEMM_F32_VARIANT_NAIVE: return naive_configs(count);
+        case GEMM_F32_VARIANT_LDS: return lds_configs(count);
+        case GEMM_F32_VARIANT_REGBLOCK: return regblock_configs(count);
+        case GEMM_F32_VARIANT_MFMA: return mfma_configs(count);
+        default: *count = 0; return nullptr;
+    }
+}
+
+int find_config(int variant, const char *name) {
+    int n = 0;
+    const ConfigEntry *c = configs_of(variant, &n);
+    for (int i = 0; i < n; ++i)
+        if (std::strcmp(c[i].name, name) == 0) return i;
+    return -1;
+}
+
+// Byte range [lo, hi) spanned by a rows x cols row-major matrix.
+struct Span {
+    uintptr_t lo, hi;
+};
+Span span_of(const void *p, int64_t rows, int64_t cols, int64_t ld) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    if (rows == 0 || cols == 0) return {lo, lo};
+    const uint64_t elems = static_cast<uint64_t>(rows - 1) * static_cast<uint64_t>(ld) +
+                           static_cast<uint64_t>(cols);
+    return {lo, lo + elems * sizeof(float)};
+}
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+int validate_sizes(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+    constexpr int64_t kMax = 0x7fffffff;
+    if (M < 0 || N < 0 || K < 0) return fail(GEMM_F32_EINVAL, "negative size M=%lld N=%lld K=%lld",
+                                             (long long)M, (long long)N, (long long)K);
+    if (M > kMax || N > kMax || K > kMax)
+        return fail(GEMM_F32_EINVAL, "size above 2^31-1 (M=%lld N=%lld K=%lld)", (long long)M,
+                    (long long)N, (long long)K);
+    if (lda < (K > 1 ? K : 1)) return fail(GEMM_F32_EINVAL, "lda=%lld < max(1, K=%lld)", (long long)lda, (long long)K);
+    if (ldb < (N > 1 ? N : 1)) return fail(GEMM_F32_EINVAL, "ldb=%lld < max(1, N=%lld)", (long long)ldb, (long long)N);
+    if (ldc < (N > 1 ? N : 1)) return fail(GEMM_F32_EINVAL, "ldc=%lld < max(1, N=%lld)", (long long)ldc, (long long)N);
+    // Largest flat element index must stay addressable with 64-bit offsets.
+    const int64_t kLdMax = (int64_t{1} << 62) / (kMax + 1);
+    if (lda > kLdMax || ldb > kLdMax || ldc > kLdMax)
+        return fail(GEMM_F32_EINVAL, "leading dimension above %lld", (long long)kLdMax);
+    return GEMM_F32_OK;
+}
+
+int validate(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+             int64_t ldb, const float *C, int64_t ldc) {
+    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
+    if (rc != GEMM_F32_OK) return rc;
+    if (M == 0 || N == 0) return GEMM_F32_OK;
+    const bool need_a = M > 0 && K > 0, need_b = K > 0 && N > 0;
+    if (C == nullptr) return fail(GEMM_F32_EINVAL, "C is NULL with M*N > 0");
+    if (need_a && A == nullptr) return fail(GEMM_F32_EINVAL, "A is NULL with M*K > 0");
+    if (need_b && B == nullptr) return fail(GEMM_F32_EINVAL, "B is NULL with K*N > 0");
+    if (reinterpret_cast<uintptr_t>(C) % 4 || (need_a && reinterpret_cast<uintptr_t>(A) % 4) ||
+        (need_b && reinterpret_cast<uintptr_t>(B) % 4))
+        return fail(GEMM_F32_EINVAL, "pointer not 4-byte aligned");
+    const Span sc = span_of(C, M, N, ldc);
+    if (need_a && overlaps(sc, span_of(A, M, K, lda)))
+        return fail(GEMM_F32_EINVAL, "C overlaps A");
+    if (need_b && overlaps(sc, span_of(B, K, N, ldb)))
+        return fail(GEMM_F32_EINVAL, "C overlaps B");
+    return GEMM_F32_OK;
+}
+
+// The tile configuration gemm_f32 uses for a shape: an exact entry of the
+// tuned table if there is one, else the rule-based choice below.
+void select_config(int64_t M, int64_t N, int64_t K, int *variant, int *config) {
+    for (const TuneEntry &e : kTuneTable) {
+        if (e.M == M && e.N == N && e.K == K) {
+            const int id = find_config(e.variant, e.config);
+            if (id >= 0) {
+                *variant = e.variant;
+                *config = id;
+                return;
+            }
+        }
+    }
+    // Rules: fewer, larger tiles once the grid fills the chip several times
+    // over; small tiles for small or ragged problems.
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const char *name = kDefaultSmall;
+    if (t256 >= 512) name = kDefaultLarge;
+    else if (t128 >= 256) name = kDefaultMedium;
+    *variant = GEMM_F32_VARIANT_MFMA;
+    *config = find_config(GEMM_F32_VARIANT_MFMA, name);
+    if (*config < 0) *config = 0;
+}
+
+int run(int variant, int config_id, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+        const float *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
+    clear_error();
+    int count = 0;
+    const ConfigEntry *cfgs = configs_of(variant, &count);
+    if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant);
+    if (config_id < -1 || config_id >= count)
+        return fail(GEMM_F32_ENOKERNEL, "variant %d has no configuration %d", variant, config_id);
+    int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    if (rc != GEMM_F32_OK) return rc;
+    if (M == 0 || N == 0) return GEMM_F32_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (K == 0) {
+        err = launch_zero_fill(C, static_cast<int>(M), static_cast<int>(N), ldc, s);
+    } else {
+        if (config_id == -1) {
+            int v = 0;
+            select_config(M, N, K, &v, &config_id);
+            if (v != variant) config_id = 0;
+        }
+        const Problem p{static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), A, lda, B,
+                        ldb, C, ldc};
+        err = cfgs[config_id].launch(p, s);
+    }
+    if (err != hipSuccess)
+        return fail(GEMM_F32_EHIP, "launch failed: %s", hipGetErrorString(err));
+    return GEMM_F32_OK;
+}
+
+}  // namespace
+
+hipError_t launch_zero_fill(float *C, int M, int N, int64_t ldc, hipStream_t stream) {
+    const int64_t total = static_cast<int64_t>(M) * N;
+    const int64_t blocks = (total + 255) / 256;
+    const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, stream, C, M, N, ldc);
+    return hipGetLastError();
+}
+
+}  // namespace gemm_f32_impl
+
+using namespace gemm_f32_impl;
+
+extern "C" {
+
+int gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+             int64_t ldb, float *C, int64_t ldc, void *stream) {
+    clear_error();
+    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
+    if (rc != GEMM_F32_OK) return rc;
+    int variant = GEMM_F32_VARIANT_MFMA, config = 0;
+    select_config(M, N, K, &variant, &config);
+    return run(variant, config, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_f32_variant(int variant, int config_id, int64_t M, int64_t N, int64_t K, const float *A,
+                     int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
+                     void *stream) {
+    return run(variant, config_id, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+const char *gemm_f32_strerror(int code) {
+    switch (code) {
+        case GEMM_F32_OK: return "success";
+        case GEMM_F32_EINVAL: return "invalid argument";
+        case GEMM_F32_EHIP: return "HIP runtime error";
+        case GEMM_F32_ENOKERNEL: return "no such kernel variant or configuration";
+        default: return "unknown error code";
+    }
+}
+
+const char *gemm_f32_last_error(void) { return g_last_error; }
+
+int gemm_f32_config_count(int variant) {
+    int n = 0;
+    return configs_of(variant, &n) ? n : GEMM_F32_ENOKERNEL;
+}
+
+const char *gemm_f32_config_name(int variant, int config_id) {
+    int n = 0;
+    const ConfigEntry *c = configs_of(variant, &n);
+    if (c == nullptr || config_id < 0 || config_id >= n) return nullptr;
+    return c[config_id].name;
+}
+
+int gemm_f32_select(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                    int *variant, int *config_id) {
+    clear_error();
+    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
+    if (rc != GEMM_F32_OK) return rc;
+    if (variant == nullptr || config_id == nullptr)
+        return fail(GEMM_F32_EINVAL, "NULL output pointer");
+    select_config(M, N, K, variant, config_id);
+    return GEMM_F32_OK;
+}
+
+int gemm_f32_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Stage 1: one thread per output cell, the whole dot product read from
+// global memory.
+//
+// Prior art: the naive kernel of "Tiled Matrix Multiplication in CUDA",
+// section 5, with the bounds guard of "Tiling and Blocking for Reuse" ("why
+// naive is slow").  Each thread walks row i of A (k moves along the row) and
+// column j of B (k moves down the column) and adds the products into one
+// FP32 register in ascending k with fused multiply-adds.
+//
+// gfx950 mapping.  A workgroup is BX x BY threads; threadIdx.x runs along the
+// columns of C and threadIdx.y along the rows, every row index built from .y
+// parts only and every column index from .x parts only (the axis rule of
+// section 4 of the same page).  With BX = 64 one wavefront covers 64
+// consecutive columns of one row, so its reads of B and its store of C are
+// 256-byte contiguous and its read of A is one broadcast address.
+//
+// Roofline: 2 FLOP per 8 requested bytes (0.25 FLOP/B, "Tiled GEMM: Matrix
+// Multiplication in CUDA", section 1) -- HBM bound on paper; caches serve
+// most of the re-reads in practice.
+
+#include "gemm_internal.h"
+
+namespace gemm_f32_impl {
+namespace {
+
+template <int BX, int BY>
+__global__ __launch_bounds__(BX * BY) void gemm_naive_kernel(
+    int M, int N, int K, const float *__restrict__ A, int64_t lda,
+    const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
+    int tiles_n) {
+    const int tile = blockIdx.x;
+    const int tile_row = tile / tiles_n;
+    const int tile_col = tile - tile_row * tiles_n;
+    const int row = tile_row * BY + threadIdx.y;  // vertical parts only
+    const int col = tile_col * BX + threadIdx.x;  // horizontal parts only
+    if (row >= M || col >= N) return;
+
+    const float *a = A + static_cast<int64_t>(row) * lda;
+    const float *b = B + col;
+    float acc = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        acc = fmaf(a[k], *b, acc);
+        b += ldb;
+    }
+    C[static_cast<int64_t>(row) * ldc + col] = acc;
+}
+
+template <int BX, int BY>
+hipError_t launch_naive(const Problem &p, hipStream_t stream) {
+    const int tiles_n = ceil_div(p.N, BX);
+    const int tiles_m = ceil_div(p.M, BY);
+    const int64_t grid = static_cast<int64_t>(tiles_n) * tiles_m;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gemm_naive_kernel<BX, BY>), dim3(static_cast<unsigned>(grid)),
+                       dim3(BX, BY), 0, stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb,
+                       p.C, p.ldc, tiles_n);
+    return hipGetLastError();
+}
+
+const ConfigEntry kNaiveConfigs[] = {
+    {"naive_64x4", launch_naive<64, 4>, 4, 64, 1},
+    {"naive_16x16", launch_naive<16, 16>, 16, 16, 1},
+    {"naive_64x1", launch_naive<64, 1>, 1, 64, 1},
+};
+
+}  // namespace
+
+const ConfigEntry *naive_configs(int *count) {
+    *count = static_cast<int>(sizeof(kNaiveConfigs) / sizeof(kNaiveConfigs[0]));
+    return kNaiveConfigs;
+}
+
+}  // namespace gemm_f32_impl

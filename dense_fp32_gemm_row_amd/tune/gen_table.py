@@ -1,0 +1,57 @@
+"""Writes csrc/tune_table.inc from tune/table.json (run by the build)."""
+
+from __future__ import annotations
+
+import json
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TABLE = os.path.join(HERE, "table.json")
+OUT = os.path.join(os.path.dirname(HERE), "csrc", "tune_table.inc")
+
+VARIANTS = {"naive": 0, "lds": 1, "regblock": 2, "mfma": 3}
+
+
+def render(table: dict) -> str:
+    lines = [
+        "// Generated from tune/table.json by tune/gen_table.py; edit the JSON.",
+        "#pragma once",
+        "#include <cstdint>",
+        "namespace gemm_f32_impl {",
+        "struct TuneEntry {",
+        "    int64_t M, N, K;",
+        "    int variant;",
+        "    const char *config;",
+        "};",
+        "// Exact shapes; the final entry (M = -1) matches nothing.",
+        "constexpr TuneEntry kTuneTable[] = {",
+    ]
+    for e in table["entries"]:
+        variant = VARIANTS[e["config"].split("_", 1)[0]]
+        lines.append(
+            f'    {{{int(e["M"])}, {int(e["N"])}, {int(e["K"])}, {variant}, "{e["config"]}"}},'
+        )
+    lines += [
+        '    {-1, -1, -1, 3, ""},',
+        "};",
+        f'constexpr const char *kDefaultLarge = "{table["default_large"]}";',
+        f'constexpr const char *kDefaultMedium = "{table["default_medium"]}";',
+        f'constexpr const char *kDefaultSmall = "{table["default_small"]}";',
+        "}  // namespace gemm_f32_impl",
+        "",
+    ]
+    return "\n".join(lines)
+
+
+def main() -> str:
+    with open(TABLE) as f:
+        text = render(json.load(f))
+    old = open(OUT).read() if os.path.exists(OUT) else None
+    if old != text:
+        with open(OUT, "w") as f:
+            f.write(text)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(main())

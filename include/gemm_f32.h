@@ -1,0 +1,146 @@
+/*
+ * gemm_f32.h -- C ABI of libgemm_f32.so: row-major FP32 matrix
+ * multiplication C = A x B on an AMD MI355X (gfx950).
+ *
+ * Operation (every compute entry point):
+ *
+ *   C[i * ldc + j] = sum over k < K of A[i * lda + k] * B[k * ldb + j]
+ *                    for 0 <= i < M, 0 <= j < N.
+ *
+ *   Each output cell is the dot product of row i of A and column j of B
+ *   ("Tiled Matrix Multiplication in CUDA", section 1; "Tiled GEMM: Matrix
+ *   Multiplication in CUDA", section 1).  Matrices are row-major, cell (r, c)
+ *   at flat index r * ld + c ("Tiled Matrix Multiplication in CUDA",
+ *   section 2); A is M x K, B is K x N and C is M x N ("Tiled GEMM: Matrix
+ *   Multiplication in CUDA", section 7.1, rectangular shapes).  The leading
+ *   dimensions lda, ldb, ldc let each operand be a row-major sub-matrix of a
+ *   wider allocation.
+ *
+ * Arithmetic: FP32 multiplies and FP32 accumulation (round to nearest even).
+ * No reduced-precision input formats are used.  The summation order depends
+ * on the kernel, so float results of different kernels agree within
+ * rounding; each kernel is deterministic run to run.  Integer-valued inputs
+ * whose partial sums stay below 2^24 in magnitude give exact results.
+ *
+ * Memory and ownership: A, B and C are device pointers (or any pointer the
+ * GPU can dereference), 4-byte aligned, owned by the caller.  The library
+ * allocates nothing on these calls and keeps no pointer after returning.
+ * C is overwritten in its M x N region only; the padding columns
+ * ldc - N of every row, and everything outside the region, are never read
+ * or written.  C must not overlap A or B.
+ *
+ * Streams and threading: every compute call only enqueues work on `stream`
+ * (a hipStream_t; NULL means the null stream) and returns; the caller
+ * synchronises.  Calls are reentrant.
+ *
+ * Errors: arguments are validated before anything is enqueued; on a
+ * negative return nothing was enqueued, except for GEMM_F32_EHIP, which
+ * reports a failed launch.  The library never aborts.  gemm_f32_last_error()
+ * describes the most recent failure on the calling thread.
+ */
+#ifndef GEMM_F32_H
+#define GEMM_F32_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define GEMM_F32_OK 0
+#define GEMM_F32_EINVAL (-1)    /* invalid sizes, leading dims, pointers */
+#define GEMM_F32_EHIP (-2)      /* a HIP runtime call or launch failed */
+#define GEMM_F32_ENOKERNEL (-3) /* no such variant or tile configuration */
+
+/* Kernel variants, in the order the pages build them up. */
+#define GEMM_F32_VARIANT_NAIVE 0    /* one thread per output cell */
+#define GEMM_F32_VARIANT_LDS 1      /* LDS (shared-memory) tiles, 2 barriers */
+#define GEMM_F32_VARIANT_REGBLOCK 2 /* per-thread register patch, VALU FMA */
+#define GEMM_F32_VARIANT_MFMA 3     /* FP32 matrix cores, double-buffered */
+#define GEMM_F32_NUM_VARIANTS 4
+
+/*
+ * gemm_f32 -- C = A x B with the kernel and tile configuration the library
+ * selects for the shape (a built-in table tuned by measurement on MI355X,
+ * "Tiling and Blocking for Reuse", "choosing the tile size").
+ *
+ *   M, N, K    sizes, 0 <= M, N, K <= 2^31 - 1
+ *   A, lda     M x K operand, lda >= max(1, K)
+ *   B, ldb     K x N operand, ldb >= max(1, N)
+ *   C, ldc     M x N result, ldc >= max(1, N)
+ *   stream     hipStream_t to enqueue on, or NULL
+ *
+ * M == 0 or N == 0: returns GEMM_F32_OK and enqueues nothing.
+ * K == 0: C's M x N region is set to zero (the empty sum).
+ * A pointer may be NULL only when its matrix has no elements.
+ * Returns GEMM_F32_OK, GEMM_F32_EINVAL or GEMM_F32_EHIP.
+ */
+int gemm_f32(int64_t M, int64_t N, int64_t K,
+             const float *A, int64_t lda,
+             const float *B, int64_t ldb,
+             float *C, int64_t ldc,
+             void *stream);
+
+/*
+ * gemm_f32_variant -- the same operation with an explicit kernel.
+ *
+ *   variant    one of GEMM_F32_VARIANT_*
+ *   config_id  index of a compiled tile configuration of that variant
+ *              (0 <= config_id < gemm_f32_config_count(variant)), or -1 for
+ *              the configuration the library would pick for this shape
+ *
+ * The naive kernel follows "Tiled Matrix Multiplication in CUDA", section 5
+ * (with the bounds guard of "Tiling and Blocking for Reuse"); the LDS kernel
+ * follows the phase loop of "Tiled GEMM: Matrix Multiplication in CUDA",
+ * sections 2 and 4, with the zero-filled loads of its section 7.1; the
+ * register-blocked kernel follows "Tiling and Blocking for Reuse", "the next
+ * level: register blocking"; the MFMA kernel adds the double buffering of
+ * "Tiled GEMM: Matrix Multiplication in CUDA", section 8.
+ *
+ * Other arguments and all semantics are those of gemm_f32.  Returns
+ * GEMM_F32_ENOKERNEL for an unknown variant or configuration.
+ */
+int gemm_f32_variant(int variant, int config_id,
+                     int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda,
+                     const float *B, int64_t ldb,
+                     float *C, int64_t ldc,
+                     void *stream);
+
+/* Static description of a return code; never NULL. */
+const char *gemm_f32_strerror(int code);
+
+/*
+ * Detail of the most recent failing call on the calling thread (for example
+ * which argument was invalid); an empty string if none failed.  The pointer
+ * stays valid until the next library call on the same thread.
+ */
+const char *gemm_f32_last_error(void);
+
+/* Number of compiled tile configurations of a variant, or GEMM_F32_ENOKERNEL. */
+int gemm_f32_config_count(int variant);
+
+/*
+ * Name of a tile configuration, e.g. "mfma_256x256x16_w2x2"; NULL when the
+ * variant or configuration does not exist.  Static storage.
+ */
+const char *gemm_f32_config_name(int variant, int config_id);
+
+/*
+ * The variant and configuration gemm_f32 would run for these arguments
+ * (sizes and leading dimensions only; no pointer is dereferenced).
+ * Returns GEMM_F32_OK or GEMM_F32_EINVAL.
+ */
+int gemm_f32_select(int64_t M, int64_t N, int64_t K,
+                    int64_t lda, int64_t ldb, int64_t ldc,
+                    int *variant, int *config_id);
+
+/* ABI version of this header: 1. */
+int gemm_f32_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F32_H */

@@ -1,0 +1,133 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and rejects invalid arguments before touching the device (no compute call
+reaches HIP here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from dense_fp32_gemm_row_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_f32.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_f32\w*)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(b.LIBRARY):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return b.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"gemm_f32", "gemm_f32_variant", "gemm_f32_strerror"} <= set(names)
+    raw = ctypes.CDLL(b.LIBRARY)
+    for name in names:
+        assert hasattr(raw, name), f"{name} declared in gemm_f32.h but not exported"
+
+
+def test_abi_version(lib):
+    assert b.gemm_f32_abi_version() == 1
+
+
+def test_strerror(lib):
+    assert b.gemm_f32_strerror(0) == "success"
+    assert b.gemm_f32_strerror(-1) == "invalid argument"
+    assert b.gemm_f32_strerror(-2) == "HIP runtime error"
+    assert b.gemm_f32_strerror(-3).startswith("no such kernel")
+    assert b.gemm_f32_strerror(12345) == "unknown error code"
+
+
+def test_config_registry(lib):
+    for v in range(4):
+        n = b.gemm_f32_config_count(v)
+        assert n >= 1
+        names = b.config_names(v)
+        assert len(set(names)) == n and all(names)
+        assert b.gemm_f32_config_name(v, n) is None
+        assert b.gemm_f32_config_name(v, -1) is None
+    assert b.gemm_f32_config_count(4) == b.GEMM_F32_ENOKERNEL
+    assert b.config_names(0)[0].startswith("naive")
+    assert all(n.startswith("mfma") for n in b.config_names(3))
+
+
+@pytest.mark.parametrize("shape", [(8192, 8192, 8192), (4096, 4096, 4096), (8192, 14336, 4096),
+                                   (1000, 1023, 777), (256, 256, 256), (1, 1, 1)])
+def test_select_returns_valid_config(lib, shape):
+    M, N, K = shape
+    v, c = b.gemm_f32_select(M, N, K, K, N, N)
+    assert v == b.VARIANT_MFMA
+    assert 0 <= c < b.gemm_f32_config_count(v)
+
+
+# Arguments that must be rejected before anything reaches the device.  Fake
+# addresses are never dereferenced: validation is pure arithmetic.
+BAD = [
+    ("negative M", (-1, 4, 4, 0x1000, 4, 0x2000, 4, 0x3000, 4), "negative"),
+    ("negative K", (4, 4, -2, 0x1000, 4, 0x2000, 4, 0x3000, 4), "negative"),
+    ("M too large", (1 << 31, 4, 4, 0x1000, 4, 0x2000, 4, 0x3000, 4), "2^31"),
+    ("lda < K", (4, 4, 5, 0x1000, 4, 0x2000, 4, 0x3000, 4), "lda"),
+    ("ldb < N", (4, 6, 4, 0x1000, 4, 0x2000, 5, 0x3000, 6), "ldb"),
+    ("ldc < N", (4, 6, 4, 0x1000, 4, 0x2000, 6, 0x3000, 5), "ldc"),
+    ("ld zero", (0, 0, 0, 0, 0, 0, 1, 0, 1), "lda"),
+    ("C NULL", (4, 4, 4, 0x1000, 4, 0x2000, 4, 0, 4), "C is NULL"),
+    ("A NULL", (4, 4, 4, 0, 4, 0x2000, 4, 0x3000, 4), "A is NULL"),
+    ("B NULL", (4, 4, 4, 0x1000, 4, 0, 4, 0x3000, 4), "B is NULL"),
+    ("A misaligned", (4, 4, 4, 0x1002, 4, 0x2000, 4, 0x3000, 4), "aligned"),
+    ("C misaligned", (4, 4, 4, 0x1000, 4, 0x2000, 4, 0x3001, 4), "aligned"),
+    ("C overlaps A", (4, 4, 4, 0x1000, 4, 0x2000, 4, 0x1000 + 60, 4), "overlaps A"),
+    ("C overlaps B", (4, 4, 4, 0x1000, 4, 0x2000, 4, 0x2000 - 4, 4), "overlaps B"),
+    ("C inside B's padding span", (2, 2, 2, 0x1000, 2, 0x2000, 64, 0x2000 + 16, 2), "overlaps B"),
+]
+
+
+@pytest.mark.parametrize("args,detail", [(a, d) for _, a, d in BAD], ids=[n for n, _, _ in BAD])
+def test_invalid_arguments(lib, args, detail):
+    assert b.gemm_f32(*args, None) == b.GEMM_F32_EINVAL
+    assert detail in b.gemm_f32_last_error()
+    for v in range(4):
+        assert b.gemm_f32_variant(v, 0, *args, None) == b.GEMM_F32_EINVAL
+    assert b.gemm_f32_variant(3, -1, *args, None) == b.GEMM_F32_EINVAL
+
+
+def test_empty_products_enqueue_nothing(lib):
+    # M == 0 or N == 0: success without any launch, NULL pointers allowed.
+    assert b.gemm_f32(0, 5, 7, 0, 7, 0, 5, 0, 5, None) == b.GEMM_F32_OK
+    assert b.gemm_f32(5, 0, 7, 0, 7, 0, 1, 0, 1, None) == b.GEMM_F32_OK
+    assert b.gemm_f32_last_error() == ""
+    for v in range(4):
+        assert b.gemm_f32_variant(v, -1, 0, 0, 0, 0, 1, 0, 1, 0, 1, None) == b.GEMM_F32_OK
+
+
+def test_unknown_kernels(lib):
+    args = (4, 4, 4, 0x1000, 4, 0x2000, 4, 0x3000, 4, None)
+    assert b.gemm_f32_variant(4, 0, *args) == b.GEMM_F32_ENOKERNEL
+    assert b.gemm_f32_variant(-1, 0, *args) == b.GEMM_F32_ENOKERNEL
+    n = b.gemm_f32_config_count(3)
+    assert b.gemm_f32_variant(3, n, *args) == b.GEMM_F32_ENOKERNEL
+    assert b.gemm_f32_variant(3, -2, *args) == b.GEMM_F32_ENOKERNEL
+    assert "configuration" in b.gemm_f32_last_error()
+
+
+def test_select_rejects_invalid(lib):
+    with pytest.raises(b.GemmError):
+        b.gemm_f32_select(4, 4, 5, 4, 4, 4)
+
+
+def test_tensor_wrapper_rejects_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    A = torch.zeros(3, 4)
+    B = torch.zeros(4, 5)
+    with pytest.raises(TypeError):
+        b.gemm(A, B)

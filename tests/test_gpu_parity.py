@@ -1,0 +1,258 @@
+"""Parity of every HIP kernel with the CPU oracle, through the C ABI.
+
+Bars: integer-valued inputs bit-exact; float inputs within
+max |C - ref| <= 1e-4 sqrt(K) and relative Frobenius error <= 1e-5 against
+the oracle's FP64 sums; no NaN anywhere.  Full-size shapes run in the launch
+configuration the benchmark times (gemm_f32's own choice) and are checked on
+sampled rows plus a Freivalds projection of the whole product.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_fp32_gemm_row_amd import binding as b
+from dense_fp32_gemm_row_amd.workloads import WORKLOADS, make_inputs, workload_inputs
+from tests import oracle_pins
+from tests.gpu_util import (assert_close, assert_exact, freivalds, log, oracle_rows,
+                            sample_rows, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+ALL_CONFIGS = [(v, c, b.gemm_f32_config_name(v, c)) for v in range(4)
+               for c in range(b.gemm_f32_config_count(v))] if __import__("os").path.exists(
+    b.LIBRARY) else []
+CONFIG_IDS = [name for _, _, name in ALL_CONFIGS]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    b.load()
+    oracle.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def run(A: np.ndarray, B: np.ndarray, variant=None, config=-1, ldc_pad=0):
+    import torch
+
+    M, N = A.shape[0], B.shape[1]
+    dA, dB = to_dev(A), to_dev(B)
+    if ldc_pad:
+        buf = torch.full((M, N + ldc_pad), float("nan"), device="cuda:0")
+        dC = buf[:, :N]
+    else:
+        dC = torch.empty((M, N), device="cuda:0")
+    b.gemm(dA, dB, dC, variant=variant, config=config)
+    return to_host(dC)
+
+
+# --------------------------------------------------------------------------
+# the worked example of the pages, on every kernel configuration
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_worked_example(v, c, name):
+    log(f"worked example on {name}")
+    g = oracle_pins.read_golden()
+    C = run(g["A"], g["B"], v, c)
+    assert_exact(C[:2, :2], g["final_block00"], name)
+    assert_exact(C, oracle.gemm(g["A"], g["B"]), name)
+
+
+# --------------------------------------------------------------------------
+# every configuration: several tiles plus a ragged tail in every dimension
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_ragged_uniform(v, c, name):
+    M, N, K = 300, 277, 129
+    log(f"ragged uniform {M}x{N}x{K} on {name}")
+    A, B = make_inputs(M, N, K, "uniform", seed=5)
+    C = run(A, B, v, c)
+    _, ref64 = oracle.gemm(A, B, return_f64=True)
+    assert_close(C, ref64, K, name)
+
+
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_integer_bit_exact(v, c, name):
+    M, N, K = 257, 263, 131
+    log(f"int4 {M}x{N}x{K} on {name}")
+    A, B = make_inputs(M, N, K, "int4", seed=6)
+    assert_exact(run(A, B, v, c), oracle.gemm(A, B), name)
+
+
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_identity_and_permutation(v, c, name):
+    # bit-exact for any float data; on the matrix cores this also pins the
+    # lane-to-element mapping of operands and accumulators
+    log(f"identity/permutation on {name}")
+    rng = np.random.default_rng(7)
+    A = rng.standard_normal((96, 80), dtype=np.float32)
+    assert_exact(run(A, np.eye(80, dtype=np.float32), v, c), A, name + " A.I")
+    n = 72
+    perm = rng.permutation(n)
+    P = np.zeros((n, n), dtype=np.float32)
+    P[np.arange(n), perm] = 1.0
+    Bm = rng.standard_normal((n, 100), dtype=np.float32)
+    assert_exact(run(P, Bm, v, c), Bm[perm], name + " P.B")
+    expect = np.empty((40, n), np.float32)
+    Am = rng.standard_normal((40, n), dtype=np.float32)
+    expect[:, perm] = Am
+    assert_exact(run(Am, P, v, c), expect, name + " A.P")
+
+
+# --------------------------------------------------------------------------
+# the small workloads in full, library choice and every MFMA configuration
+# --------------------------------------------------------------------------
+
+SMALL = ["square256", "square256_int4", "ragged", "ragged_int4"]
+MFMA_CONFIGS = [(3, c, n) for v, c, n in ALL_CONFIGS if v == 3]
+
+
+@pytest.mark.parametrize("wname", SMALL)
+@pytest.mark.parametrize("kernel", [None] + MFMA_CONFIGS + [(0, -1, "naive"), (1, -1, "lds"),
+                                                            (2, -1, "regblock")],
+                         ids=lambda k: "select" if k is None else k[2])
+def test_small_workloads(wname, kernel):
+    w = WORKLOADS[wname]
+    log(f"{wname} on {'select' if kernel is None else kernel[2]}")
+    A, B = workload_inputs(wname)
+    C = run(A, B) if kernel is None else run(A, B, kernel[0], kernel[1])
+    ref32, ref64 = oracle.gemm(A, B, return_f64=True)
+    if w.dist == "int4":
+        assert_exact(C, ref32, wname)
+    else:
+        assert_close(C, ref64, w.K, wname)
+
+
+# --------------------------------------------------------------------------
+# layout, edges and semantics
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, None], ids=["naive", "lds", "regblock", "mfma", "select"])
+def test_leading_dimensions_and_guard_band(variant):
+    """Operands are sub-matrices of wider allocations (unaligned lda, offset
+    start) and C sits in a NaN-filled buffer: only C's M x N region may
+    change."""
+    import torch
+
+    log(f"leading dims on variant {variant}")
+    rng = np.random.default_rng(8)
+    M, N, K = 211, 190, 97
+    Aw = rng.integers(-4, 5, size=(M, K + 5)).astype(np.float32)
+    Bw = rng.integers(-4, 5, size=(K, N + 8)).astype(np.float32)
+    dAw, dBw = to_dev(Aw), to_dev(Bw)
+    dA = dAw[:, 1:1 + K]      # lda = K + 5, start offset by one float
+    dB = dBw[:, :N]           # ldb = N + 8
+    buf = torch.full((M + 2, N + 13), float("nan"), device="cuda:0")
+    dC = buf[1:1 + M, 3:3 + N]  # ldc = N + 13, guard rows above and below
+    b.gemm(dA, dB, dC, variant=variant)
+    host = to_host(buf)
+    inner = host[1:1 + M, 3:3 + N]
+    assert_exact(inner, oracle.gemm(Aw[:, 1:1 + K], Bw[:, :N]), "leading dims")
+    mask = np.ones_like(host, dtype=bool)
+    mask[1:1 + M, 3:3 + N] = False
+    assert np.isnan(host[mask]).all(), "a write landed outside C's region"
+
+
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_deterministic(v, c, name):
+    log(f"determinism on {name}")
+    A, B = make_inputs(320, 288, 300, "uniform", seed=9)
+    C1 = run(A, B, v, c)
+    C2 = run(A, B, v, c)
+    assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32)), name
+
+
+def test_naive_tiled_regblock_identical():
+    """The naive, LDS-tiled and register-blocked kernels add each cell's
+    products in ascending k with fused multiply-adds, so they agree to the
+    bit ("Tiled Matrix Multiplication in CUDA", section 8)."""
+    log("naive == tiled == register-blocked")
+    A, B = make_inputs(300, 277, 129, "uniform", seed=10)
+    base = run(A, B, 0, 0)
+    for v in (0, 1, 2):
+        for c in range(b.gemm_f32_config_count(v)):
+            assert_exact(run(A, B, v, c), base, b.gemm_f32_config_name(v, c))
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_k_zero_gives_zeros(variant):
+    import torch
+
+    log(f"K = 0 on variant {variant}")
+    dA = torch.empty((7, 0), device="cuda:0")
+    dB = torch.empty((0, 9), device="cuda:0")
+    buf = torch.full((7, 12), float("nan"), device="cuda:0")
+    b.gemm(dA, dB, buf[:, :9], variant=variant)
+    host = to_host(buf)
+    assert (host[:, :9] == 0).all()
+    assert np.isnan(host[:, 9:]).all()
+
+
+def test_empty_m_leaves_output():
+    import torch
+
+    dA = torch.empty((0, 5), device="cuda:0")
+    dB = torch.ones((5, 4), device="cuda:0")
+    out = torch.empty((0, 4), device="cuda:0")
+    b.gemm(dA, dB, out)
+    assert out.shape == (0, 4)
+
+
+def test_runs_on_callers_stream():
+    import torch
+
+    log("non-default stream")
+    A, B = make_inputs(512, 512, 512, "int4", seed=11)
+    dA, dB = to_dev(A), to_dev(B)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        dC = torch.empty((512, 512), device="cuda:0")
+        b.gemm(dA, dB, dC)
+    s.synchronize()
+    assert_exact(dC.cpu().numpy(), oracle.gemm(A, B), "stream")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 300, 70), (300, 1, 70), (33, 65, 1),
+                                   (64, 64, 777), (1000, 8, 8), (2, 3000, 5)])
+def test_degenerate_shapes(shape):
+    M, N, K = shape
+    log(f"degenerate {shape}")
+    A, B = make_inputs(M, N, K, "uniform", seed=12)
+    _, ref64 = oracle.gemm(A, B, return_f64=True)
+    for v in (None, 0, 1, 2, 3):
+        assert_close(run(A, B, v), ref64, K, f"{shape} variant {v}")
+
+
+# --------------------------------------------------------------------------
+# full-size workloads in the benchmark's launch configuration
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wname", ["square4096", "square8192", "ffn"])
+def test_full_size_sampled(wname):
+    import torch
+
+    w = WORKLOADS[wname]
+    log(f"full size {wname} {w.M}x{w.N}x{w.K}")
+    A, B = workload_inputs(wname)
+    dA, dB = to_dev(A), to_dev(B)
+    dC = torch.empty((w.M, w.N), device="cuda:0")
+    b.gemm(dA, dB, dC)
+    C = to_host(dC)
+    del dA, dB, dC
+    assert not np.isnan(C).any()
+    rows = sample_rows(w.M)
+    _, ref64 = oracle_rows(A, B, rows)
+    stats = assert_close(C[rows], ref64, w.K, wname)
+    fr = freivalds(A, B, C)
+    log(f"{wname}: sampled max err {stats['max_err']:.3e} relF {stats['rel_fro']:.3e} "
+        f"freivalds {fr:.3e}")
+    assert fr <= 1e-5, f"Freivalds residual {fr:.3e}"
