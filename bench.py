@@ -149,6 +149,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--stages", action="store_true")
+    ap.add_argument("--stage-variants", default="naive,lds,regblock,mfma",
+                    help="variants that --stages times")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB mebibytes "
+                         "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -165,6 +170,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, args.steps)
     binding.load()
     w = WORKLOADS[args.workload]
     M, N, K = w.M, w.N, w.K
@@ -255,7 +262,8 @@ def run_stages(args, w, A, B, dA, dB, dC, stream, flops) -> int:
     from dense_fp32_gemm_row_amd import binding
 
     out = []
-    for v in range(4):
+    wanted = [binding.VARIANTS[x] for x in args.stage_variants.split(",")]
+    for v in wanted:
         for c in range(binding.gemm_f32_config_count(v)):
             name = binding.gemm_f32_config_name(v, c)
             steps = args.steps if v >= 2 else max(2, min(args.steps, 3))
@@ -269,6 +277,23 @@ def run_stages(args, w, A, B, dA, dB, dC, stream, flops) -> int:
             out.append(rec)
             log(json.dumps(rec))
     print(json.dumps({"stages": out}), flush=True)
+    return 0
+
+
+def copy_calibration(mib: int, steps: int) -> int:
+    """A plain copy of `mib` MiB between two device buffers, `steps` times:
+    each launch reads and writes exactly mib MiB of HBM, the reference that
+    scales the HBM byte counters."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.rand(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    total, per = time_launches(lambda: dst.copy_(src), steps, 1, stream)
+    avg = sum(per) / len(per)
+    print(json.dumps({"copy_mib": mib, "avg_ms": round(avg, 4),
+                      "gbs": round(2 * mib * (1 << 20) / (avg / 1e3) / 1e9, 1)}), flush=True)
     return 0
 
 

@@ -51,6 +51,13 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    # torch ships its own HIP runtime.  Loading torch first makes the
+    # library's libamdhip64.so.7 dependency resolve (by soname) to that copy,
+    # so the library launches into the same runtime that owns torch's memory
+    # and streams.  Loaded the other way round, the process would hold two
+    # HIP runtimes and torch's stream handles would be foreign to ours.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     lib.gemm_f32.restype = _int
     lib.gemm_f32.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]

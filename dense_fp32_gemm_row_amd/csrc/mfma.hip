@@ -49,6 +49,8 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+constexpr int kLdsBytes = 160 * 1024;  // LDS available to one workgroup on gfx950
+
 // Four consecutive floats of one row starting at column `col`: a 16-byte load
 // when the row is 16-byte aligned (VEC), zeros outside [0, limit) and for
 // rows that do not exist (GUARD).
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
     static_assert(BK % 8 == 0, "K step is whole chunks of 8");
     static_assert(LA * 4 * NT == BM * BK && LB * 4 * NT == BK * BN, "even tile split");
     static_assert(LDA_S % 4 == 0 && LDB_S % 4 == 0, "16-byte aligned LDS rows");
+    static_assert(2 * (BM * LDA_S + BK * LDB_S) * 4 <= kLdsBytes, "LDS budget of a workgroup");
 
     __shared__ __align__(16) float sA[2][BM * LDA_S];  // m-major, k contiguous
     __shared__ __align__(16) float sB[2][BK * LDB_S];  // k-major, n contiguous
@@ -210,7 +213,227 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
     }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int GROUP_M>
+// Pipelined variant, with a ring of STAGES (2 or 3) LDS buffers.  Within a
+// K-step the fragments of the next chunk of 8 k are read while the MFMAs of
+// the current chunk run (two register sets, alternating).  With a ring of
+// three LDS buffers, in addition, the tile of K-step
+// t + 1 is complete and published (by the barrier that ended step t - 1)
+// while step t still runs, so each wavefront reads its first operand
+// fragments of step t + 1 before the barrier that ends step t, and the
+// matrix cores restart right after the barrier instead of waiting on LDS.
+//
+// Hazards, with three buffers and b(t) = t mod 3: step t writes tile t + 2 into
+// b(t + 2) = b(t - 1), last read in step t - 1, i.e. before the barrier that
+// ended step t - 1 (write after read); tile t + 2 is first read in step
+// t + 1, after the barrier that ends step t (read after write).  With two
+// buffers the scheme is the one of the first kernel.
+template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool GUARD,
+          bool VEC>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
+    int M, int N, int K, const float *__restrict__ A, int64_t lda,
+    const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
+    int tiles_m, int tiles_n, int group_m) {
+    constexpr int NT = 64 * WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int LA = (BM * BK) / (4 * NT);
+    constexpr int LB = (BK * BN) / (4 * NT);
+    // PADA >= 0: A rows padded by PADA floats.  PADA < 0: unpadded A rows
+    // whose 16-byte slots are permuted by an XOR with a function of the row.
+    constexpr bool SWZ = PADA < 0;
+    constexpr int LDA_S = BK + (SWZ ? 0 : PADA), LDB_S = BN + PADB;
+    constexpr int S = BK / 4;                              // 16-byte slots per A row
+    constexpr int LOG2S = S == 2 ? 1 : S == 4 ? 2 : S == 8 ? 3 : 4;
+    constexpr int KC = BK / 8;  // chunks of 8 k per K-step
+    // LDS read instructions per chunk: one 16-byte read per row block of A,
+    // and the 4 k values of each B column block (pairs of column blocks
+    // 32 floats apart merge into one two-address read).
+    constexpr int kReadsPerChunk = FM + 4 * ((FN + 1) / 2);
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32 x 32 blocks");
+    static_assert(BK % 16 == 0, "an even number of chunks per K-step");
+    constexpr int kMfmaPerChunk = FM * FN * 4;
+    constexpr int kPairs = kReadsPerChunk < kMfmaPerChunk ? kReadsPerChunk : kMfmaPerChunk;
+    static_assert(LA * 4 * NT == BM * BK && LB * 4 * NT == BK * BN, "even tile split");
+    static_assert(LDA_S % 4 == 0 && LDB_S % 4 == 0, "16-byte aligned LDS rows");
+    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS buffers");
+    static_assert(STAGES * (BM * LDA_S + BK * LDB_S) * 4 <= kLdsBytes, "LDS budget of a workgroup");
+
+    __shared__ __align__(16) float sA[STAGES][BM * LDA_S];
+    __shared__ __align__(16) float sB[STAGES][BK * LDB_S];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    int tm, tn;
+    grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    int a_m[LA], a_k[LA], b_k[LB], b_n[LB];
+    const float *a_row[LA];
+    bool a_ok[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int e = tid + i * NT;
+        a_m[i] = e / (BK / 4);
+        a_k[i] = (e % (BK / 4)) * 4;
+        const int gm = m0 + a_m[i];
+        a_ok[i] = gm < M;
+        a_row[i] = A + static_cast<int64_t>(a_ok[i] ? gm : 0) * lda;
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int e = tid + i * NT;
+        b_k[i] = e / (BN / 4);
+        b_n[i] = (e % (BN / 4)) * 4;
+    }
+
+    float4 ra[LA], rb[LB];
+    auto load_global = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+            ra[i] = load_row4<GUARD, VEC>(a_row[i], k0 + a_k[i], K, a_ok[i]);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
+            const int gk = k0 + b_k[i];
+            const bool ok = !GUARD || gk < K;
+            const float *row = B + static_cast<int64_t>(ok ? gk : 0) * ldb + n0;
+            rb[i] = load_row4<GUARD, VEC>(row, b_n[i], N - n0, ok);
+        }
+    };
+    // XOR swizzle of the A tile: slot q of row m is stored at slot
+    // q ^ g(m), g(m) = (r ^ (r >> log2 S)) mod S with r = m mod 32.  A
+    // wavefront's 16-byte reads (32 consecutive rows of one 32-row block, one
+    // slot) and its 16-byte stores (S lanes per row, 64 / S consecutive rows
+    // inside one 32-row block) then hit disjoint banks, whether the LDS
+    // serves 8 or 16 such accesses per cycle.  Depending on m mod 32 only,
+    // g is the same for every 32-row block a lane reads.
+    auto swz = [](int m) { return ((m & 31) ^ ((m & 31) >> LOG2S)) & (S - 1); };
+    int a_st[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+        a_st[i] = a_m[i] * LDA_S + (SWZ ? ((a_k[i] / 4) ^ swz(a_m[i])) * 4 : a_k[i]);
+    auto store_lds = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+            *reinterpret_cast<float4 *>(&sA[buf][a_st[i]]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < LB; ++i)
+            *reinterpret_cast<float4 *>(&sB[buf][b_k[i] * LDB_S + b_n[i]]) = rb[i];
+    };
+
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+    // rows read by this lane are wm * WTM + i * 32 + l32, all congruent to
+    // l32 modulo 32: one swizzle term serves every row block
+    const int a_lds = (wm * WTM + l32) * LDA_S + (SWZ ? 0 : 4 * half);
+    const int g_lane = swz(l32);
+    const int b_lds = (4 * half) * LDB_S + wn * WTN + l32;
+
+    // Two fragment register sets: operands of one chunk of 8 k.
+    float4 fa[2][FM];
+    float fb[2][FN][4];
+    auto read_frag = [&](int set, int buf, int kc) {
+        const float *pa = &sA[buf][a_lds + (SWZ ? ((2 * kc + half) ^ g_lane) * 4 : kc * 8)];
+        const float *pb = &sB[buf][b_lds + kc * 8 * LDB_S];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[set][i] = *reinterpret_cast<const float4 *>(pa + i * 32 * LDA_S);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) fb[set][j][s] = pb[s * LDB_S + j * 32];
+    };
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto mfma_chunk = [&](int set) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const float4 av = fa[set][i];
+                    const float a = s == 0 ? av.x : s == 1 ? av.y : s == 2 ? av.z : av.w;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, fb[set][j][s], acc[i][j], 0, 0, 0);
+                }
+    };
+
+    const int nk = (K + BK - 1) / BK;
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) {
+        if (st < nk) {
+            load_global(st * BK);
+            store_lds(st);
+        }
+    }
+    __syncthreads();
+    read_frag(0, 0, 0);
+
+    int cur = 0;  // t mod STAGES
+    for (int t = 0; t < nk; ++t) {
+        const int nxt = cur == STAGES - 1 ? 0 : cur + 1;
+        const int ahead = cur == 0 ? STAGES - 1 : cur - 1;  // (t + STAGES - 1) mod STAGES
+        if (t + STAGES - 1 < nk) load_global((t + STAGES - 1) * BK);
+        // Branch-free so that the reads stay ahead of the MFMAs they feed
+        // (a branch here lets the compiler sink them back to their use).  With
+        // three buffers the last chunk reads ahead into step t + 1; in the
+        // last step that read is unused and stays inside buffer `nxt`, which
+        // nobody writes in that step.
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            const int set = kc & 1;
+            if (kc + 1 < KC)
+                read_frag(set ^ 1, cur, kc + 1);
+            else if constexpr (STAGES == 3)
+                read_frag(set ^ 1, nxt, 0);
+            mfma_chunk(set);
+            // Issue order for the scheduler: the reads of the next chunk go
+            // out one per MFMA at the start of this chunk, so their latency
+            // hides behind the remaining MFMAs and the matrix pipe never
+            // waits for a burst of reads.
+#pragma unroll
+            for (int r = 0; r < kPairs; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            }
+            if constexpr (kReadsPerChunk > kPairs)
+                __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerChunk - kPairs, 0);
+            if constexpr (kMfmaPerChunk > kPairs)
+                __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk - kPairs, 0);
+        }
+        if (t + STAGES - 1 < nk) store_lds(ahead);
+        if (t + 1 < nk) __syncthreads();
+        // With two buffers the next step's first chunk is readable only now.
+        if constexpr (STAGES == 2) read_frag(0, nxt, 0);
+        cur = nxt;
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int gn = n0 + wn * WTN + j * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gm = m0 + wm * WTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                if (!GUARD || (gm < M && gn < N))
+                    C[static_cast<int64_t>(gm) * ldc + gn] = acc[i][j][r];
+            }
+        }
+    }
+}
+
+// PIPE = 0: the first kernel; PIPE = 2 or 3: the pipelined kernel with that
+// many LDS buffers.
+template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int GROUP_M, int PIPE>
 hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     constexpr int NT = 64 * WM * WN;
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
@@ -219,9 +442,17 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     const bool vec = rows_aligned16(p.A, p.lda) && rows_aligned16(p.B, p.ldb);
     const bool guard = (p.M % BM) || (p.N % BN) || (p.K % BK);
     const dim3 g(static_cast<unsigned>(grid)), b(NT);
-#define GEMM_MFMA_LAUNCH(G, V)                                                                 \
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WM, WN, PADA, PADB, G, V>), g, b, 0, stream, \
-                       p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, GROUP_M)
+#define GEMM_MFMA_LAUNCH(G, V)                                                                  \
+    do {                                                                                        \
+        if constexpr (PIPE > 0)                                                                 \
+            hipLaunchKernelGGL((gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, G, V>), \
+                               g, b, 0, stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,    \
+                               tiles_m, tiles_n, GROUP_M);                                      \
+        else                                                                                    \
+            hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WM, WN, PADA, PADB, G, V>), g, b, 0, \
+                               stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,       \
+                               tiles_m, tiles_n, GROUP_M);                                      \
+    } while (0)
     if (guard) {
         if (vec) GEMM_MFMA_LAUNCH(true, true);
         else GEMM_MFMA_LAUNCH(true, false);
@@ -234,16 +465,39 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
 }
 
 const ConfigEntry kMfmaConfigs[] = {
-    {"mfma_128x128x16_w2x2_pa4_pb0", launch_mfma<128, 128, 16, 2, 2, 4, 0, 8>, 128, 128, 16},
-    {"mfma_128x128x16_w2x2_pa0_pb0", launch_mfma<128, 128, 16, 2, 2, 0, 0, 8>, 128, 128, 16},
-    {"mfma_128x128x16_w2x2_pa4_pb8", launch_mfma<128, 128, 16, 2, 2, 4, 8, 8>, 128, 128, 16},
-    {"mfma_128x128x32_w2x2_pa4_pb0", launch_mfma<128, 128, 32, 2, 2, 4, 0, 8>, 128, 128, 32},
-    {"mfma_256x128x16_w2x2_pa4_pb0", launch_mfma<256, 128, 16, 2, 2, 4, 0, 8>, 256, 128, 16},
-    {"mfma_128x256x16_w2x2_pa4_pb0", launch_mfma<128, 256, 16, 2, 2, 4, 0, 8>, 128, 256, 16},
-    {"mfma_256x256x16_w2x2_pa4_pb0", launch_mfma<256, 256, 16, 2, 2, 4, 0, 8>, 256, 256, 16},
-    {"mfma_256x256x16_w2x4_pa4_pb0", launch_mfma<256, 256, 16, 2, 4, 4, 0, 8>, 256, 256, 16},
-    {"mfma_64x64x16_w2x2_pa4_pb0", launch_mfma<64, 64, 16, 2, 2, 4, 0, 8>, 64, 64, 16},
-    {"mfma_64x64x32_w2x2_pa4_pb0", launch_mfma<64, 64, 32, 2, 2, 4, 0, 8>, 64, 64, 32},
+    // two LDS buffers, one barrier per K-step
+    {"mfma_128x128x16_w2x2_pa4_pb0", launch_mfma<128, 128, 16, 2, 2, 4, 0, 8, 0>, 128, 128, 16},
+    {"mfma_128x128x16_w2x2_pa0_pb0", launch_mfma<128, 128, 16, 2, 2, 0, 0, 8, 0>, 128, 128, 16},
+    {"mfma_128x128x16_w2x2_pa4_pb8", launch_mfma<128, 128, 16, 2, 2, 4, 8, 8, 0>, 128, 128, 16},
+    {"mfma_128x128x32_w2x2_pa4_pb0", launch_mfma<128, 128, 32, 2, 2, 4, 0, 8, 0>, 128, 128, 32},
+    {"mfma_256x128x16_w2x2_pa4_pb0", launch_mfma<256, 128, 16, 2, 2, 4, 0, 8, 0>, 256, 128, 16},
+    {"mfma_128x256x16_w2x2_pa4_pb0", launch_mfma<128, 256, 16, 2, 2, 4, 0, 8, 0>, 128, 256, 16},
+    {"mfma_256x256x16_w2x2_pa4_pb0", launch_mfma<256, 256, 16, 2, 2, 4, 0, 8, 0>, 256, 256, 16},
+    {"mfma_256x256x16_w2x4_pa4_pb0", launch_mfma<256, 256, 16, 2, 4, 4, 0, 8, 0>, 256, 256, 16},
+    {"mfma_256x256x32_w2x4_pa4_pb0", launch_mfma<256, 256, 32, 2, 4, 4, 0, 8, 0>, 256, 256, 32},
+    {"mfma_256x256x16_w4x4_pa4_pb0", launch_mfma<256, 256, 16, 4, 4, 4, 0, 8, 0>, 256, 256, 16},
+    {"mfma_256x256x32_w4x4_pa4_pb0", launch_mfma<256, 256, 32, 4, 4, 4, 0, 8, 0>, 256, 256, 32},
+    {"mfma_64x64x16_w2x2_pa4_pb0", launch_mfma<64, 64, 16, 2, 2, 4, 0, 8, 0>, 64, 64, 16},
+    {"mfma_64x64x32_w2x2_pa4_pb0", launch_mfma<64, 64, 32, 2, 2, 4, 0, 8, 0>, 64, 64, 32},
+    // three LDS buffers, fragments of the next step read before the barrier
+    {"mfma3_256x256x16_w2x4_pa4_pb0", launch_mfma<256, 256, 16, 2, 4, 4, 0, 8, 3>, 256, 256, 16},
+    {"mfma3_256x256x16_w4x4_pa4_pb0", launch_mfma<256, 256, 16, 4, 4, 4, 0, 8, 3>, 256, 256, 16},
+    {"mfma3_128x128x16_w2x2_pa4_pb0", launch_mfma<128, 128, 16, 2, 2, 4, 0, 8, 3>, 128, 128, 16},
+    {"mfma3_256x128x16_w2x2_pa4_pb0", launch_mfma<256, 128, 16, 2, 2, 4, 0, 8, 3>, 256, 128, 16},
+    {"mfma3_128x256x16_w2x2_pa4_pb0", launch_mfma<128, 256, 16, 2, 2, 4, 0, 8, 3>, 128, 256, 16},
+    {"mfma3_64x64x16_w2x2_pa4_pb0", launch_mfma<64, 64, 16, 2, 2, 4, 0, 8, 3>, 64, 64, 16},
+    // two LDS buffers, fragments pipelined within a step
+    {"mfma2p_256x256x32_w2x4_pa4_pb0", launch_mfma<256, 256, 32, 2, 4, 4, 0, 8, 2>, 256, 256, 32},
+    {"mfma2p_256x256x16_w2x4_pa4_pb0", launch_mfma<256, 256, 16, 2, 4, 4, 0, 8, 2>, 256, 256, 16},
+    {"mfma2p_128x128x32_w2x2_pa4_pb0", launch_mfma<128, 128, 32, 2, 2, 4, 0, 8, 2>, 128, 128, 32},
+    // pipelined, A tile XOR-swizzled instead of padded
+    {"mfma3_256x256x16_w4x4_swz_pb0", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3>, 256, 256, 16},
+    {"mfma3_256x256x16_w4x4_swz_pb8", launch_mfma<256, 256, 16, 4, 4, -1, 8, 8, 3>, 256, 256, 16},
+    {"mfma3_256x256x16_w2x4_swz_pb0", launch_mfma<256, 256, 16, 2, 4, -1, 0, 8, 3>, 256, 256, 16},
+    {"mfma3_128x256x32_w2x2_swz_pb0", launch_mfma<128, 256, 32, 2, 2, -1, 0, 8, 3>, 128, 256, 32},
+    {"mfma2p_256x256x32_w4x4_swz_pb0", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2>, 256, 256, 32},
+    {"mfma3_128x128x16_w2x2_swz_pb0", launch_mfma<128, 128, 16, 2, 2, -1, 0, 8, 3>, 128, 128, 16},
+    {"mfma3_64x64x16_w2x2_swz_pb0", launch_mfma<64, 64, 16, 2, 2, -1, 0, 8, 3>, 64, 64, 16},
 };
 
 }  // namespace

@@ -9,7 +9,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TABLE = os.path.join(HERE, "table.json")
 OUT = os.path.join(os.path.dirname(HERE), "csrc", "tune_table.inc")
 
+# configuration names start with their variant's name
 VARIANTS = {"naive": 0, "lds": 1, "regblock": 2, "mfma": 3}
+
+
+def variant_of(config: str) -> int:
+    for prefix, v in VARIANTS.items():
+        if config.startswith(prefix):
+            return v
+    raise ValueError(f"configuration {config!r} names no variant")
 
 
 def render(table: dict) -> str:
@@ -27,7 +35,7 @@ def render(table: dict) -> str:
         "constexpr TuneEntry kTuneTable[] = {",
     ]
     for e in table["entries"]:
-        variant = VARIANTS[e["config"].split("_", 1)[0]]
+        variant = variant_of(e["config"])
         lines.append(
             f'    {{{int(e["M"])}, {int(e["N"])}, {int(e["K"])}, {variant}, "{e["config"]}"}},'
         )
