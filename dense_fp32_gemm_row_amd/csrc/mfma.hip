@@ -227,8 +227,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
 // ended step t - 1 (write after read); tile t + 2 is first read in step
 // t + 1, after the barrier that ends step t (read after write).  With two
 // buffers the scheme is the one of the first kernel.
-template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool GUARD,
-          bool VEC>
+template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
+          bool GUARD, bool VEC>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
@@ -323,6 +323,52 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
             *reinterpret_cast<float4 *>(&sB[buf][b_k[i] * LDB_S + b_n[i]]) = rb[i];
     };
 
+    // Direct global -> LDS loads (global_load_lds_dwordx4): one instruction
+    // moves 64 x 16 bytes into 1 KiB of contiguous LDS, lane L's 16 bytes at
+    // offset 16 L.  The tiles are cut into 1 KiB chunks, dealt round-robin to
+    // the wavefronts, and each lane fetches the global element that belongs
+    // at its LDS slot: for A the inverse of the XOR swizzle, for B the plain
+    // row-major position.  No registers hold the tile in flight and no LDS
+    // store instructions are issued; the barrier's wait on the memory
+    // counter completes the copy.  Only for full, 16-byte-aligned tiles.
+    constexpr int NW = WM * WN;
+    constexpr int CA = BM * BK / 256, CB = BK * BN / 256;  // 1 KiB chunks per tile
+    constexpr int JA = DIRECT ? CA / NW : 1, JB = DIRECT ? CB / NW : 1;
+    static_assert(!DIRECT || (SWZ && PADB == 0 && !GUARD && VEC), "direct loads: unpadded full tiles");
+    static_assert(!DIRECT || (CA % NW == 0 && CB % NW == 0), "whole chunks per wavefront");
+    const float *a_src[JA], *b_src[JB];
+    int a_dst[JA], b_dst[JB];
+    if constexpr (DIRECT) {
+#pragma unroll
+        for (int j = 0; j < JA; ++j) {
+            const int c = wave + j * NW;
+            const int m = c * (64 / S) + lane / S;          // tile row of this lane
+            const int q = (lane % S) ^ swz(m);             // logical slot stored here
+            a_src[j] = A + static_cast<int64_t>(m0 + m) * lda + 4 * q;
+            a_dst[j] = c * 256;
+        }
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+            const int c = wave + j * NW;
+            const int f = c * 256 + lane * 4;              // float offset in the B tile
+            b_src[j] = B + static_cast<int64_t>(f / BN) * ldb + n0 + f % BN;
+            b_dst[j] = c * 256;
+        }
+    }
+    // (address-space casts: global source, LDS destination)
+    typedef const __attribute__((address_space(1))) void *gptr_t;
+    typedef __attribute__((address_space(3))) void *lptr_t;
+    auto load_direct = [&](int k0, int buf) {
+#pragma unroll
+        for (int j = 0; j < JA; ++j)
+            __builtin_amdgcn_global_load_lds((gptr_t)(a_src[j] + k0), (lptr_t)(&sA[buf][a_dst[j]]),
+                                             16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+            __builtin_amdgcn_global_load_lds((gptr_t)(b_src[j] + static_cast<int64_t>(k0) * ldb),
+                                             (lptr_t)(&sB[buf][b_dst[j]]), 16, 0, 0);
+    };
+
     const int half = lane >> 5;
     const int l32 = lane & 31;
     // rows read by this lane are wm * WTM + i * 32 + l32, all congruent to
@@ -370,8 +416,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st) {
         if (st < nk) {
-            load_global(st * BK);
-            store_lds(st);
+            if constexpr (DIRECT) {
+                load_direct(st * BK, st);
+            } else {
+                load_global(st * BK);
+                store_lds(st);
+            }
         }
     }
     __syncthreads();
@@ -381,7 +431,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
     for (int t = 0; t < nk; ++t) {
         const int nxt = cur == STAGES - 1 ? 0 : cur + 1;
         const int ahead = cur == 0 ? STAGES - 1 : cur - 1;  // (t + STAGES - 1) mod STAGES
-        if (t + STAGES - 1 < nk) load_global((t + STAGES - 1) * BK);
+        if (t + STAGES - 1 < nk) {
+            if constexpr (DIRECT) load_direct((t + STAGES - 1) * BK, ahead);
+            else load_global((t + STAGES - 1) * BK);
+        }
         // Branch-free so that the reads stay ahead of the MFMAs they feed
         // (a branch here lets the compiler sink them back to their use).  With
         // three buffers the last chunk reads ahead into step t + 1; in the
@@ -409,7 +462,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
             if constexpr (kMfmaPerChunk > kPairs)
                 __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk - kPairs, 0);
         }
-        if (t + STAGES - 1 < nk) store_lds(ahead);
+        if constexpr (!DIRECT)
+            if (t + STAGES - 1 < nk) store_lds(ahead);
         if (t + 1 < nk) __syncthreads();
         // With two buffers the next step's first chunk is readable only now.
         if constexpr (STAGES == 2) read_frag(0, nxt, 0);
@@ -432,8 +486,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
 }
 
 // PIPE = 0: the first kernel; PIPE = 2 or 3: the pipelined kernel with that
-// many LDS buffers.
-template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int GROUP_M, int PIPE>
+// many LDS buffers.  DIRECT: direct global -> LDS loads where the shape
+// allows (full tiles, 16-byte-aligned rows), register staging otherwise.
+template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int GROUP_M, int PIPE,
+          bool DIRECT = false>
 hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     constexpr int NT = 64 * WM * WN;
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
@@ -442,23 +498,24 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     const bool vec = rows_aligned16(p.A, p.lda) && rows_aligned16(p.B, p.ldb);
     const bool guard = (p.M % BM) || (p.N % BN) || (p.K % BK);
     const dim3 g(static_cast<unsigned>(grid)), b(NT);
-#define GEMM_MFMA_LAUNCH(G, V)                                                                  \
+#define GEMM_MFMA_LAUNCH(D, G, V)                                                               \
     do {                                                                                        \
         if constexpr (PIPE > 0)                                                                 \
-            hipLaunchKernelGGL((gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, G, V>), \
-                               g, b, 0, stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,    \
-                               tiles_m, tiles_n, GROUP_M);                                      \
+            hipLaunchKernelGGL(                                                                 \
+                (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, D, G, V>), g, b, 0, \
+                stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,   \
+                GROUP_M);                                                                       \
         else                                                                                    \
             hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WM, WN, PADA, PADB, G, V>), g, b, 0, \
                                stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,       \
                                tiles_m, tiles_n, GROUP_M);                                      \
     } while (0)
     if (guard) {
-        if (vec) GEMM_MFMA_LAUNCH(true, true);
-        else GEMM_MFMA_LAUNCH(true, false);
+        if (vec) GEMM_MFMA_LAUNCH(false, true, true);
+        else GEMM_MFMA_LAUNCH(false, true, false);
     } else {
-        if (vec) GEMM_MFMA_LAUNCH(false, true);
-        else GEMM_MFMA_LAUNCH(false, false);
+        if (vec) GEMM_MFMA_LAUNCH(DIRECT, false, true);
+        else GEMM_MFMA_LAUNCH(false, false, false);
     }
 #undef GEMM_MFMA_LAUNCH
     return hipGetLastError();
@@ -498,6 +555,20 @@ const ConfigEntry kMfmaConfigs[] = {
     {"mfma2p_256x256x32_w4x4_swz_pb0", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2>, 256, 256, 32},
     {"mfma3_128x128x16_w2x2_swz_pb0", launch_mfma<128, 128, 16, 2, 2, -1, 0, 8, 3>, 128, 128, 16},
     {"mfma3_64x64x16_w2x2_swz_pb0", launch_mfma<64, 64, 16, 2, 2, -1, 0, 8, 3>, 64, 64, 16},
+    // two workgroups per CU (72 KiB of LDS each)
+    {"mfma3_256x128x16_w4x2_swz_pb0", launch_mfma<256, 128, 16, 4, 2, -1, 0, 8, 3>, 256, 128, 16},
+    {"mfma3_128x256x16_w2x4_swz_pb0", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3>, 128, 256, 16},
+    // direct global -> LDS loads
+    {"mfma3d_256x256x16_w4x4_swz", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3, true>, 256, 256, 16},
+    {"mfma3d_256x256x16_w2x4_swz", launch_mfma<256, 256, 16, 2, 4, -1, 0, 8, 3, true>, 256, 256, 16},
+    {"mfma3d_256x128x16_w4x2_swz", launch_mfma<256, 128, 16, 4, 2, -1, 0, 8, 3, true>, 256, 128, 16},
+    {"mfma3d_128x256x16_w2x4_swz", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3, true>, 128, 256, 16},
+    {"mfma2d_256x256x32_w4x4_swz", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2, true>, 256, 256, 32},
+    {"mfma2d_256x256x32_w4x4_swz_g4", launch_mfma<256, 256, 32, 4, 4, -1, 0, 4, 2, true>, 256, 256, 32},
+    {"mfma2d_256x256x32_w4x4_swz_g16", launch_mfma<256, 256, 32, 4, 4, -1, 0, 16, 2, true>, 256, 256, 32},
+    {"mfma2d_256x256x32_w2x4_swz", launch_mfma<256, 256, 32, 2, 4, -1, 0, 8, 2, true>, 256, 256, 32},
+    {"mfma3d_256x128x32_w4x2_swz", launch_mfma<256, 128, 32, 4, 2, -1, 0, 8, 3, true>, 256, 128, 32},
+    {"mfma3d_128x256x32_w2x4_swz", launch_mfma<128, 256, 32, 2, 4, -1, 0, 8, 3, true>, 128, 256, 32},
 };
 
 }  // namespace

@@ -9,6 +9,8 @@ sampled rows plus a Freivalds projection of the whole product.
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -22,8 +24,7 @@ from tests.gpu_util import (assert_close, assert_exact, freivalds, log, oracle_r
 pytestmark = pytest.mark.gpu
 
 ALL_CONFIGS = [(v, c, b.gemm_f32_config_name(v, c)) for v in range(4)
-               for c in range(b.gemm_f32_config_count(v))] if __import__("os").path.exists(
-    b.LIBRARY) else []
+               for c in range(b.gemm_f32_config_count(v))] if os.path.exists(b.LIBRARY) else []
 CONFIG_IDS = [name for _, _, name in ALL_CONFIGS]
 
 
@@ -105,6 +106,27 @@ def test_identity_and_permutation(v, c, name):
     Am = rng.standard_normal((40, n), dtype=np.float32)
     expect[:, perm] = Am
     assert_exact(run(Am, P, v, c), expect, name + " A.P")
+
+
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_full_tiles(v, c, name):
+    """Shapes that are whole tiles of every configuration: the unguarded
+    path, with direct global-to-LDS loads where a configuration has them."""
+    M, N, K = 512, 512, 96
+    log(f"full tiles {M}x{N}x{K} on {name}")
+    A, B = make_inputs(M, N, K, "int4", seed=13)
+    assert_exact(run(A, B, v, c), oracle.gemm(A, B), name + " int4")
+    A, B = make_inputs(M, N, K, "uniform", seed=14)
+    _, ref64 = oracle.gemm(A, B, return_f64=True)
+    assert_close(run(A, B, v, c), ref64, K, name + " uniform")
+    rng = np.random.default_rng(15)
+    X = rng.standard_normal((M, 512), dtype=np.float32)
+    assert_exact(run(X, np.eye(512, dtype=np.float32), v, c), X, name + " A.I")
+    perm = rng.permutation(512)
+    P = np.zeros((512, 512), dtype=np.float32)
+    P[np.arange(512), perm] = 1.0
+    Y = rng.standard_normal((512, N), dtype=np.float32)
+    assert_exact(run(P, Y, v, c), Y[perm], name + " P.B")
 
 
 # --------------------------------------------------------------------------
