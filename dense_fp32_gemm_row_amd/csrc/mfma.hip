@@ -436,17 +436,36 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
             else load_global((t + STAGES - 1) * BK);
         }
         // Branch-free so that the reads stay ahead of the MFMAs they feed
-        // (a branch here lets the compiler sink them back to their use).  With
-        // three buffers the last chunk reads ahead into step t + 1; in the
-        // last step that read is unused and stays inside buffer `nxt`, which
-        // nobody writes in that step.
+        // (a branch here lets the compiler sink them back to their use).
+        //
+        // Three buffers: the last chunk reads ahead into step t + 1 (tile t + 1
+        // was published by the previous barrier); the barrier ends the step.
+        //
+        // Two buffers: the barrier sits before the last chunk.  By then the
+        // last chunk's fragments are in registers (so every read of buffer
+        // `cur` is done: write after read) and tile t + 1 has landed in buffer
+        // `nxt` (read after write), so right after the barrier the first
+        // fragments of step t + 1 are read while the last chunk's MFMAs run.
+        //
+        // In the last step the look-ahead read of buffer `nxt` is unused; it
+        // stays inside the buffer, which nobody writes after the barrier.
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             const int set = kc & 1;
-            if (kc + 1 < KC)
-                read_frag(set ^ 1, cur, kc + 1);
-            else if constexpr (STAGES == 3)
-                read_frag(set ^ 1, nxt, 0);
+            if constexpr (STAGES == 2) {
+                if (kc == KC - 1) {
+                    if constexpr (!DIRECT) store_lds(nxt);  // stale but in-bounds in the last step
+                    // keep all of the previous chunk's MFMAs ahead of the
+                    // barrier: they cover the latency of the reads it waits for
+                    __builtin_amdgcn_sched_barrier(0);
+                    __syncthreads();
+                    read_frag(set ^ 1, nxt, 0);
+                } else {
+                    read_frag(set ^ 1, cur, kc + 1);
+                }
+            } else {
+                read_frag(set ^ 1, kc + 1 < KC ? cur : nxt, kc + 1 < KC ? kc + 1 : 0);
+            }
             mfma_chunk(set);
             // Issue order for the scheduler: the reads of the next chunk go
             // out one per MFMA at the start of this chunk, so their latency
@@ -462,11 +481,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
             if constexpr (kMfmaPerChunk > kPairs)
                 __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk - kPairs, 0);
         }
-        if constexpr (!DIRECT)
-            if (t + STAGES - 1 < nk) store_lds(ahead);
-        if (t + 1 < nk) __syncthreads();
-        // With two buffers the next step's first chunk is readable only now.
-        if constexpr (STAGES == 2) read_frag(0, nxt, 0);
+        if constexpr (STAGES == 3) {
+            if constexpr (!DIRECT)
+                if (t + 2 < nk) store_lds(ahead);
+            if (t + 1 < nk) __syncthreads();
+        }
         cur = nxt;
     }
 
