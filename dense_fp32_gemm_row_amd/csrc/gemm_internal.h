@@ -30,7 +30,6 @@ using LaunchFn = hipError_t (*)(const Problem &, hipStream_t);
 struct ConfigEntry {
     const char *name;  // stable, used by the tuning table and benchmarks
     LaunchFn launch;
-    int bm, bn, bk;    // output tile of one workgroup and K step
 };
 
 // Registries, one per variant (defined in the kernel sources).

@@ -75,10 +75,10 @@ hipError_t launch_lds(const Problem &p, hipStream_t stream) {
 }
 
 const ConfigEntry kLdsConfigs[] = {
-    {"lds_t16", launch_lds<16, 0>, 16, 16, 16},
-    {"lds_t32", launch_lds<32, 0>, 32, 32, 32},
-    {"lds_t16_pad1", launch_lds<16, 1>, 16, 16, 16},
-    {"lds_t32_pad1", launch_lds<32, 1>, 32, 32, 32},
+    {"lds_t16", launch_lds<16, 0>},
+    {"lds_t32", launch_lds<32, 0>},
+    {"lds_t16_pad1", launch_lds<16, 1>},
+    {"lds_t32_pad1", launch_lds<32, 1>},
 };
 
 }  // namespace

@@ -541,53 +541,38 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
 }
 
 const ConfigEntry kMfmaConfigs[] = {
-    // two LDS buffers, one barrier per K-step
-    {"mfma_128x128x16_w2x2_pa4_pb0", launch_mfma<128, 128, 16, 2, 2, 4, 0, 8, 0>, 128, 128, 16},
-    {"mfma_128x128x16_w2x2_pa0_pb0", launch_mfma<128, 128, 16, 2, 2, 0, 0, 8, 0>, 128, 128, 16},
-    {"mfma_128x128x16_w2x2_pa4_pb8", launch_mfma<128, 128, 16, 2, 2, 4, 8, 8, 0>, 128, 128, 16},
-    {"mfma_128x128x32_w2x2_pa4_pb0", launch_mfma<128, 128, 32, 2, 2, 4, 0, 8, 0>, 128, 128, 32},
-    {"mfma_256x128x16_w2x2_pa4_pb0", launch_mfma<256, 128, 16, 2, 2, 4, 0, 8, 0>, 256, 128, 16},
-    {"mfma_128x256x16_w2x2_pa4_pb0", launch_mfma<128, 256, 16, 2, 2, 4, 0, 8, 0>, 128, 256, 16},
-    {"mfma_256x256x16_w2x2_pa4_pb0", launch_mfma<256, 256, 16, 2, 2, 4, 0, 8, 0>, 256, 256, 16},
-    {"mfma_256x256x16_w2x4_pa4_pb0", launch_mfma<256, 256, 16, 2, 4, 4, 0, 8, 0>, 256, 256, 16},
-    {"mfma_256x256x32_w2x4_pa4_pb0", launch_mfma<256, 256, 32, 2, 4, 4, 0, 8, 0>, 256, 256, 32},
-    {"mfma_256x256x16_w4x4_pa4_pb0", launch_mfma<256, 256, 16, 4, 4, 4, 0, 8, 0>, 256, 256, 16},
-    {"mfma_256x256x32_w4x4_pa4_pb0", launch_mfma<256, 256, 32, 4, 4, 4, 0, 8, 0>, 256, 256, 32},
-    {"mfma_64x64x16_w2x2_pa4_pb0", launch_mfma<64, 64, 16, 2, 2, 4, 0, 8, 0>, 64, 64, 16},
-    {"mfma_64x64x32_w2x2_pa4_pb0", launch_mfma<64, 64, 32, 2, 2, 4, 0, 8, 0>, 64, 64, 32},
-    // three LDS buffers, fragments of the next step read before the barrier
-    {"mfma3_256x256x16_w2x4_pa4_pb0", launch_mfma<256, 256, 16, 2, 4, 4, 0, 8, 3>, 256, 256, 16},
-    {"mfma3_256x256x16_w4x4_pa4_pb0", launch_mfma<256, 256, 16, 4, 4, 4, 0, 8, 3>, 256, 256, 16},
-    {"mfma3_128x128x16_w2x2_pa4_pb0", launch_mfma<128, 128, 16, 2, 2, 4, 0, 8, 3>, 128, 128, 16},
-    {"mfma3_256x128x16_w2x2_pa4_pb0", launch_mfma<256, 128, 16, 2, 2, 4, 0, 8, 3>, 256, 128, 16},
-    {"mfma3_128x256x16_w2x2_pa4_pb0", launch_mfma<128, 256, 16, 2, 2, 4, 0, 8, 3>, 128, 256, 16},
-    {"mfma3_64x64x16_w2x2_pa4_pb0", launch_mfma<64, 64, 16, 2, 2, 4, 0, 8, 3>, 64, 64, 16},
-    // two LDS buffers, fragments pipelined within a step
-    {"mfma2p_256x256x32_w2x4_pa4_pb0", launch_mfma<256, 256, 32, 2, 4, 4, 0, 8, 2>, 256, 256, 32},
-    {"mfma2p_256x256x16_w2x4_pa4_pb0", launch_mfma<256, 256, 16, 2, 4, 4, 0, 8, 2>, 256, 256, 16},
-    {"mfma2p_128x128x32_w2x2_pa4_pb0", launch_mfma<128, 128, 32, 2, 2, 4, 0, 8, 2>, 128, 128, 32},
-    // pipelined, A tile XOR-swizzled instead of padded
-    {"mfma3_256x256x16_w4x4_swz_pb0", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3>, 256, 256, 16},
-    {"mfma3_256x256x16_w4x4_swz_pb8", launch_mfma<256, 256, 16, 4, 4, -1, 8, 8, 3>, 256, 256, 16},
-    {"mfma3_256x256x16_w2x4_swz_pb0", launch_mfma<256, 256, 16, 2, 4, -1, 0, 8, 3>, 256, 256, 16},
-    {"mfma3_128x256x32_w2x2_swz_pb0", launch_mfma<128, 256, 32, 2, 2, -1, 0, 8, 3>, 128, 256, 32},
-    {"mfma2p_256x256x32_w4x4_swz_pb0", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2>, 256, 256, 32},
-    {"mfma3_128x128x16_w2x2_swz_pb0", launch_mfma<128, 128, 16, 2, 2, -1, 0, 8, 3>, 128, 128, 16},
-    {"mfma3_64x64x16_w2x2_swz_pb0", launch_mfma<64, 64, 16, 2, 2, -1, 0, 8, 3>, 64, 64, 16},
-    // two workgroups per CU (72 KiB of LDS each)
-    {"mfma3_256x128x16_w4x2_swz_pb0", launch_mfma<256, 128, 16, 4, 2, -1, 0, 8, 3>, 256, 128, 16},
-    {"mfma3_128x256x16_w2x4_swz_pb0", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3>, 128, 256, 16},
-    // direct global -> LDS loads
-    {"mfma3d_256x256x16_w4x4_swz", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3, true>, 256, 256, 16},
-    {"mfma3d_256x256x16_w2x4_swz", launch_mfma<256, 256, 16, 2, 4, -1, 0, 8, 3, true>, 256, 256, 16},
-    {"mfma3d_256x128x16_w4x2_swz", launch_mfma<256, 128, 16, 4, 2, -1, 0, 8, 3, true>, 256, 128, 16},
-    {"mfma3d_128x256x16_w2x4_swz", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3, true>, 128, 256, 16},
-    {"mfma2d_256x256x32_w4x4_swz", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2, true>, 256, 256, 32},
-    {"mfma2d_256x256x32_w4x4_swz_g4", launch_mfma<256, 256, 32, 4, 4, -1, 0, 4, 2, true>, 256, 256, 32},
-    {"mfma2d_256x256x32_w4x4_swz_g16", launch_mfma<256, 256, 32, 4, 4, -1, 0, 16, 2, true>, 256, 256, 32},
-    {"mfma2d_256x256x32_w2x4_swz", launch_mfma<256, 256, 32, 2, 4, -1, 0, 8, 2, true>, 256, 256, 32},
-    {"mfma3d_256x128x32_w4x2_swz", launch_mfma<256, 128, 32, 4, 2, -1, 0, 8, 3, true>, 256, 128, 32},
-    {"mfma3d_128x256x32_w2x4_swz", launch_mfma<128, 256, 32, 2, 4, -1, 0, 8, 3, true>, 128, 256, 32},
+    // First kernel: two LDS buffers, one barrier per K-step, padded A rows
+    // (pa0 = unpadded, for the bank-conflict counters).
+    {"mfma_128x128x16_w2x2_pa4_pb0", launch_mfma<128, 128, 16, 2, 2, 4, 0, 8, 0>},
+    {"mfma_128x128x16_w2x2_pa0_pb0", launch_mfma<128, 128, 16, 2, 2, 0, 0, 8, 0>},
+    {"mfma_256x256x16_w2x4_pa4_pb0", launch_mfma<256, 256, 16, 2, 4, 4, 0, 8, 0>},
+    {"mfma_256x256x32_w2x4_pa4_pb0", launch_mfma<256, 256, 32, 2, 4, 4, 0, 8, 0>},
+    {"mfma_256x256x16_w4x4_pa4_pb0", launch_mfma<256, 256, 16, 4, 4, 4, 0, 8, 0>},
+    {"mfma_64x64x16_w2x2_pa4_pb0", launch_mfma<64, 64, 16, 2, 2, 4, 0, 8, 0>},
+    {"mfma_64x64x32_w2x2_pa4_pb0", launch_mfma<64, 64, 32, 2, 2, 4, 0, 8, 0>},
+    // Pipelined kernel, register staging: mfma3 = three LDS buffers, mfma2p =
+    // two buffers with the barrier before the last chunk; A rows padded (pa4)
+    // or XOR-swizzled (swz); pb8 pads B rows.
+    {"mfma3_256x256x16_w4x4_pa4_pb0", launch_mfma<256, 256, 16, 4, 4, 4, 0, 8, 3>},
+    {"mfma3_256x256x16_w4x4_swz_pb0", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3>},
+    {"mfma3_256x256x16_w4x4_swz_pb8", launch_mfma<256, 256, 16, 4, 4, -1, 8, 8, 3>},
+    {"mfma2p_256x256x32_w4x4_swz_pb0", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2>},
+    {"mfma3_128x128x16_w2x2_swz_pb0", launch_mfma<128, 128, 16, 2, 2, -1, 0, 8, 3>},
+    {"mfma3_64x64x16_w2x2_swz_pb0", launch_mfma<64, 64, 16, 2, 2, -1, 0, 8, 3>},
+    // Pipelined kernel, direct global -> LDS loads on full tiles (register
+    // staging on edge tiles): mfma3d = three buffers, mfma2d = two buffers;
+    // 256x128 / 128x256 tiles fit two workgroups per CU at BK = 16; g4 / g16
+    // change the column-strip height of the tile order.
+    {"mfma3d_256x256x16_w4x4_swz", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3, true>},
+    {"mfma3d_256x256x16_w2x4_swz", launch_mfma<256, 256, 16, 2, 4, -1, 0, 8, 3, true>},
+    {"mfma3d_256x128x16_w4x2_swz", launch_mfma<256, 128, 16, 4, 2, -1, 0, 8, 3, true>},
+    {"mfma3d_128x256x16_w2x4_swz", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3, true>},
+    {"mfma2d_256x256x32_w4x4_swz", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2, true>},
+    {"mfma2d_256x256x32_w4x4_swz_g4", launch_mfma<256, 256, 32, 4, 4, -1, 0, 4, 2, true>},
+    {"mfma2d_256x256x32_w4x4_swz_g16", launch_mfma<256, 256, 32, 4, 4, -1, 0, 16, 2, true>},
+    {"mfma2d_256x256x32_w2x4_swz", launch_mfma<256, 256, 32, 2, 4, -1, 0, 8, 2, true>},
+    {"mfma3d_256x128x32_w4x2_swz", launch_mfma<256, 128, 32, 4, 2, -1, 0, 8, 3, true>},
+    {"mfma3d_128x256x32_w2x4_swz", launch_mfma<128, 256, 32, 2, 4, -1, 0, 8, 3, true>},
 };
 
 }  // namespace

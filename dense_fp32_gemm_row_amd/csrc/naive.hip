@@ -58,9 +58,9 @@ hipError_t launch_naive(const Problem &p, hipStream_t stream) {
 }
 
 const ConfigEntry kNaiveConfigs[] = {
-    {"naive_64x4", launch_naive<64, 4>, 4, 64, 1},
-    {"naive_16x16", launch_naive<16, 16>, 16, 16, 1},
-    {"naive_64x1", launch_naive<64, 1>, 1, 64, 1},
+    {"naive_64x4", launch_naive<64, 4>},
+    {"naive_16x16", launch_naive<16, 16>},
+    {"naive_64x1", launch_naive<64, 1>},
 };
 
 }  // namespace

@@ -194,11 +194,11 @@ hipError_t launch_regblock(const Problem &p, hipStream_t stream) {
 }
 
 const ConfigEntry kRegblockConfigs[] = {
-    {"regblock_128x128x8_t8x8_pad4", launch_regblock<128, 128, 8, 8, 8, 4>, 128, 128, 8},
-    {"regblock_64x64x16_t4x4_pad4", launch_regblock<64, 64, 16, 4, 4, 4>, 64, 64, 16},
-    {"regblock_128x128x8_t8x8_pad0", launch_regblock<128, 128, 8, 8, 8, 0>, 128, 128, 8},
-    {"regblock_128x128x16_t8x8_pad4", launch_regblock<128, 128, 16, 8, 8, 4>, 128, 128, 16},
-    {"regblock_128x64x16_t8x4_pad4", launch_regblock<128, 64, 16, 8, 4, 4>, 128, 64, 16},
+    {"regblock_128x128x8_t8x8_pad4", launch_regblock<128, 128, 8, 8, 8, 4>},
+    {"regblock_64x64x16_t4x4_pad4", launch_regblock<64, 64, 16, 4, 4, 4>},
+    {"regblock_128x128x8_t8x8_pad0", launch_regblock<128, 128, 8, 8, 8, 0>},
+    {"regblock_128x128x16_t8x8_pad4", launch_regblock<128, 128, 16, 8, 8, 4>},
+    {"regblock_128x64x16_t8x4_pad4", launch_regblock<128, 64, 16, 8, 4, 4>},
 };
 
 }  // namespace

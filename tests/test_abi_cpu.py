@@ -131,3 +131,31 @@ def test_tensor_wrapper_rejects_cpu_tensors(lib):
     B = torch.zeros(4, 5)
     with pytest.raises(TypeError):
         b.gemm(A, B)
+
+
+def test_tuning_table_names_compiled_configs(lib):
+    import json
+
+    table = json.load(open(os.path.join(ROOT, "dense_fp32_gemm_row_amd", "tune", "table.json")))
+    names = {n for v in range(4) for n in b.config_names(v)}
+    for key in ("default_large", "default_medium", "default_small"):
+        assert table[key] in names, f"{key} names unknown configuration {table[key]}"
+    for e in table["entries"]:
+        assert e["config"] in names, f"table entry {e} names an unknown configuration"
+        v, c = b.gemm_f32_select(e["M"], e["N"], e["K"], e["K"], e["N"], e["N"])
+        assert b.gemm_f32_config_name(v, c) == e["config"]
+
+
+def test_generated_table_matches_json():
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location(
+        "gen_table", os.path.join(ROOT, "dense_fp32_gemm_row_amd", "tune", "gen_table.py"))
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    import json
+
+    with open(gen.TABLE) as f:
+        expect = gen.render(json.load(f))
+    with open(gen.OUT) as f:
+        assert f.read() == expect, "csrc/tune_table.inc is stale: rebuild"
