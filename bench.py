@@ -141,7 +141,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="square8192")
     ap.add_argument("--variant", default=None, help="naive|lds|regblock|mfma (default: library choice)")
     ap.add_argument("--config", default=None, help="configuration name of the variant")
@@ -180,15 +180,17 @@ def main() -> int:
     dev = torch.device("cuda:0")
     dA = torch.from_numpy(A).to(dev)
     dB = torch.from_numpy(B).to(dev)
-    dC = torch.empty((M, N), dtype=torch.float32, device=dev)
+    nb = w.batch
+    dC = torch.empty((nb, M, N) if nb > 1 else (M, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    flops = 2.0 * M * N * K
+    flops = 2.0 * nb * M * N * K
+    call = binding.gemm_batched if nb > 1 else binding.gemm
 
     if args.stages:
         return run_stages(args, w, A, B, dA, dB, dC, stream, flops)
 
     if args.variant is None:
-        v, c = binding.gemm_f32_select(M, N, K, K, N, N)
+        v, c = binding.gemm_f32_select(M, N, K, K, N, N) if nb == 1 else (None, None)
     else:
         v = binding.VARIANTS[args.variant]
         if args.config:
@@ -197,13 +199,13 @@ def main() -> int:
             c = binding.gemm_f32_select(M, N, K, K, N, N)[1]
         else:
             c = 0
-    cname = binding.gemm_f32_config_name(v, c)
+    cname = binding.gemm_f32_config_name(v, c) if v is not None else "library choice (batched)"
     log(f"kernel {cname}")
 
     if args.variant is None:
-        fn = lambda: binding.gemm(dA, dB, dC)  # noqa: E731  (gemm_f32)
+        fn = lambda: call(dA, dB, dC)  # noqa: E731  (gemm_f32 / gemm_f32_strided_batched)
     else:
-        fn = lambda: binding.gemm(dA, dB, dC, variant=v, config=c)  # noqa: E731
+        fn = lambda: call(dA, dB, dC, variant=v, config=c)  # noqa: E731
 
     total_ms, per = time_launches(fn, args.steps, args.warmup, stream)
     ms_step = total_ms / args.steps
@@ -227,8 +229,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_FP32_MATRIX_TFLOPS, 2),
-        "config": {"workload": w.name, "M": M, "N": N, "K": K, "dist": w.dist, "seed": w.seed,
-                   "layout": "row-major A, B, C", "kernel": cname, "parallelism": "none"},
+        "config": {"workload": w.name, "batch": nb, "M": M, "N": N, "K": K, "dist": w.dist,
+                   "seed": w.seed, "layout": "row-major A, B, C", "kernel": cname,
+                   "parallelism": "none"},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),
@@ -245,13 +248,20 @@ def main() -> int:
     rc = 0
     if not args.no_check:
         C = dC.cpu().numpy()
-        result["parity"] = parity_check(A, B, C)
+        if nb > 1:  # first and last product of the batch
+            checks = [parity_check(A[i], B[i], C[i]) for i in (0, nb - 1)]
+            result["parity"] = max(checks, key=lambda r: r["rel_fro"])
+            result["parity"]["ok"] = all(r["ok"] for r in checks)
+            result["parity"]["products_checked"] = [0, nb - 1]
+        else:
+            result["parity"] = parity_check(A, B, C)
         log(f"parity {result['parity']}")
         if not result["parity"]["ok"]:
             rc = 1
         del C
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(A[0] if nb > 1 else A, B[0] if nb > 1 else B,
+                                              args.cpu_seconds)
         log(f"cpu baseline {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
     return rc
@@ -267,7 +277,8 @@ def run_stages(args, w, A, B, dA, dB, dC, stream, flops) -> int:
         for c in range(binding.gemm_f32_config_count(v)):
             name = binding.gemm_f32_config_name(v, c)
             steps = args.steps if v >= 2 else max(2, min(args.steps, 3))
-            fn = lambda: binding.gemm(dA, dB, dC, variant=v, config=c)  # noqa: E731
+            call = binding.gemm_batched if w.batch > 1 else binding.gemm
+            fn = lambda: call(dA, dB, dC, variant=v, config=c)  # noqa: E731
             total, per = time_launches(fn, steps, 1, stream)
             avg = sum(per) / len(per)
             tf = flops / (avg / 1e3) / 1e12

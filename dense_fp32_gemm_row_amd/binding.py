@@ -64,6 +64,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gemm_f32_variant.restype = _int
     lib.gemm_f32_variant.argtypes = [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
                                      _i64, _vp]
+    lib.gemm_f32_strided_batched.restype = _int
+    lib.gemm_f32_strided_batched.argtypes = [_i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64,
+                                             _i64, _vp, _i64, _i64, _vp]
+    lib.gemm_f32_strided_batched_variant.restype = _int
+    lib.gemm_f32_strided_batched_variant.argtypes = [_int, _int, _i64, _i64, _i64, _i64, _vp, _i64,
+                                                     _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp]
     lib.gemm_f32_strerror.restype = ctypes.c_char_p
     lib.gemm_f32_strerror.argtypes = [_int]
     lib.gemm_f32_last_error.restype = ctypes.c_char_p
@@ -89,6 +95,18 @@ def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
 
 def gemm_f32_variant(variant, config_id, M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     return load().gemm_f32_variant(variant, config_id, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_strided_batched(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC,
+                             stream=None) -> int:
+    return load().gemm_f32_strided_batched(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC,
+                                           stream)
+
+
+def gemm_f32_strided_batched_variant(variant, config_id, batch, M, N, K, A, lda, sA, B, ldb, sB,
+                                     C, ldc, sC, stream=None) -> int:
+    return load().gemm_f32_strided_batched_variant(variant, config_id, batch, M, N, K, A, lda, sA,
+                                                   B, ldb, sB, C, ldc, sC, stream)
 
 
 def gemm_f32_strerror(code: int) -> str:
@@ -144,6 +162,53 @@ def _row_major_ld(t, name: str) -> int:
     if rows <= 1:
         return max(cols, 1)
     return t.stride(0)
+
+
+def _batch_layout(t, name: str) -> tuple[int, int]:
+    """(leading dimension, batch stride) of a 3-D float32 GPU tensor whose
+    matrices are row-major; a batch stride of 0 (expanded tensor) is allowed."""
+    import torch
+
+    if t.dtype != torch.float32 or t.dim() != 3 or not t.is_cuda:
+        raise TypeError(f"{name} must be a 3-D float32 GPU tensor")
+    _, rows, cols = t.shape
+    if cols > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    ld = t.stride(1) if rows > 1 else max(cols, 1)
+    return ld, t.stride(0)
+
+
+def gemm_batched(A, B, out=None, *, variant: int | str | None = None, config: int | str = -1,
+                 stream=None):
+    """``out[b] = A[b] @ B[b]`` for 3-D float32 GPU tensors through
+    gemm_f32_strided_batched (or its _variant form).  A or B may be an
+    expanded tensor (batch stride 0)."""
+    import torch
+
+    nb, M, K = A.shape
+    nb2, K2, N = B.shape
+    if nb != nb2 or K != K2:
+        raise ValueError(f"shape mismatch {tuple(A.shape)} x {tuple(B.shape)}")
+    lda, sa = _batch_layout(A, "A")
+    ldb, sb = _batch_layout(B, "B")
+    if out is None:
+        out = torch.empty((nb, M, N), dtype=torch.float32, device=A.device)
+    ldc, sc = _batch_layout(out, "out")
+    if tuple(out.shape) != (nb, M, N):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(nb, M, N)}")
+    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+    if variant is None:
+        rc = gemm_f32_strided_batched(nb, M, N, K, A.data_ptr(), lda, sa, B.data_ptr(), ldb, sb,
+                                      out.data_ptr(), ldc, sc, s.cuda_stream)
+    else:
+        v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+        c = config_id(v, config) if isinstance(config, str) else int(config)
+        rc = gemm_f32_strided_batched_variant(v, c, nb, M, N, K, A.data_ptr(), lda, sa,
+                                              B.data_ptr(), ldb, sb, out.data_ptr(), ldc, sc,
+                                              s.cuda_stream)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, gemm_f32_last_error())
+    return out
 
 
 def gemm(A, B, out=None, *, variant: int | str | None = None, config: int | str = -1,

@@ -31,12 +31,14 @@ int fail(int code, const char *fmt, ...) {
 }
 
 __global__ __launch_bounds__(256) void zero_fill_kernel(float *__restrict__ C, int M, int N,
-                                                        int64_t ldc) {
-    const int64_t total = static_cast<int64_t>(M) * N;
+                                                        int64_t ldc, int batch, int64_t sc) {
+    const int64_t per = static_cast<int64_t>(M) * N;
+    const int64_t total = per * batch;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
          e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int64_t i = e / N, j = e - i * N;
-        C[i * ldc + j] = 0.0f;
+        const int64_t b = e / per, r = e - b * per;
+        const int64_t i = r / N, j = r - i * N;
+        C[b * sc + i * ldc + j] = 0.0f;
     }
 }
 
@@ -69,6 +71,13 @@ Span span_of(const void *p, int64_t rows, int64_t cols, int64_t ld) {
                            static_cast<uint64_t>(cols);
     return {lo, lo + elems * sizeof(float)};
 }
+// ... and of `batch` such matrices `stride` floats apart.
+Span span_of_batch(const void *p, int64_t batch, int64_t stride, int64_t rows, int64_t cols,
+                   int64_t ld) {
+    Span s = span_of(p, rows, cols, ld);
+    if (s.lo != s.hi && batch > 1) s.hi += static_cast<uint64_t>(batch - 1) * stride * sizeof(float);
+    return s;
+}
 bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 
 int validate_sizes(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
@@ -88,11 +97,36 @@ int validate_sizes(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, in
     return GEMM_F32_OK;
 }
 
-int validate(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
-             int64_t ldb, const float *C, int64_t ldc) {
+// Largest element offset the batch strides may span (keeps every byte
+// offset well inside 64 bits).
+constexpr int64_t kSpanMax = int64_t{1} << 58;
+
+int validate_batch(int64_t batch, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t sa,
+                   int64_t ldb, int64_t sb, int64_t ldc, int64_t sc) {
+    if (batch < 0) return fail(GEMM_F32_EINVAL, "negative batch %lld", (long long)batch);
+    if (batch > 0x7fffffff) return fail(GEMM_F32_EINVAL, "batch above 2^31-1");
+    if (sa < 0 || sb < 0 || sc < 0) return fail(GEMM_F32_EINVAL, "negative batch stride");
+    if (batch > 1 && M > 0 && N > 0) {
+        const int64_t c_span = (M - 1) * ldc + N;
+        if (sc < c_span)
+            return fail(GEMM_F32_EINVAL, "strideC=%lld < %lld: the products' C regions overlap",
+                        (long long)sc, (long long)c_span);
+    }
+    const int64_t n = batch > 1 ? batch - 1 : 0;
+    if ((sa && n > kSpanMax / sa) || (sb && n > kSpanMax / sb) || (sc && n > kSpanMax / sc))
+        return fail(GEMM_F32_EINVAL, "batch x stride spans more than 2^58 floats");
+    (void)K, (void)lda, (void)ldb;
+    return GEMM_F32_OK;
+}
+
+int validate(int64_t batch, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+             int64_t sa, const float *B, int64_t ldb, int64_t sb, const float *C, int64_t ldc,
+             int64_t sc) {
     int rc = validate_sizes(M, N, K, lda, ldb, ldc);
     if (rc != GEMM_F32_OK) return rc;
-    if (M == 0 || N == 0) return GEMM_F32_OK;
+    rc = validate_batch(batch, M, N, K, lda, sa, ldb, sb, ldc, sc);
+    if (rc != GEMM_F32_OK) return rc;
+    if (M == 0 || N == 0 || batch == 0) return GEMM_F32_OK;
     const bool need_a = M > 0 && K > 0, need_b = K > 0 && N > 0;
     if (C == nullptr) return fail(GEMM_F32_EINVAL, "C is NULL with M*N > 0");
     if (need_a && A == nullptr) return fail(GEMM_F32_EINVAL, "A is NULL with M*K > 0");
@@ -100,31 +134,34 @@ int validate(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const
     if (reinterpret_cast<uintptr_t>(C) % 4 || (need_a && reinterpret_cast<uintptr_t>(A) % 4) ||
         (need_b && reinterpret_cast<uintptr_t>(B) % 4))
         return fail(GEMM_F32_EINVAL, "pointer not 4-byte aligned");
-    const Span sc = span_of(C, M, N, ldc);
-    if (need_a && overlaps(sc, span_of(A, M, K, lda)))
+    const Span scs = span_of_batch(C, batch, sc, M, N, ldc);
+    if (need_a && overlaps(scs, span_of_batch(A, batch, sa, M, K, lda)))
         return fail(GEMM_F32_EINVAL, "C overlaps A");
-    if (need_b && overlaps(sc, span_of(B, K, N, ldb)))
+    if (need_b && overlaps(scs, span_of_batch(B, batch, sb, K, N, ldb)))
         return fail(GEMM_F32_EINVAL, "C overlaps B");
     return GEMM_F32_OK;
 }
 
 // The tile configuration gemm_f32 uses for a shape: an exact entry of the
 // tuned table if there is one, else the rule-based choice below.
-void select_config(int64_t M, int64_t N, int64_t K, int *variant, int *config) {
-    for (const TuneEntry &e : kTuneTable) {
-        if (e.M == M && e.N == N && e.K == K) {
-            const int id = find_config(e.variant, e.config);
-            if (id >= 0) {
-                *variant = e.variant;
-                *config = id;
-                return;
+void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant, int *config) {
+    if (batch == 1) {
+        for (const TuneEntry &e : kTuneTable) {
+            if (e.M == M && e.N == N && e.K == K) {
+                const int id = find_config(e.variant, e.config);
+                if (id >= 0) {
+                    *variant = e.variant;
+                    *config = id;
+                    return;
+                }
             }
         }
     }
     // Rules: fewer, larger tiles once the grid fills the chip several times
-    // over; small tiles for small or ragged problems.
-    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    // over; small tiles for small or ragged problems.  A batch multiplies the
+    // number of tiles.
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256) * batch;
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128) * batch;
     const char *name = kDefaultSmall;
     if (t256 >= 512) name = kDefaultLarge;
     else if (t128 >= 256) name = kDefaultMedium;
@@ -133,30 +170,32 @@ void select_config(int64_t M, int64_t N, int64_t K, int *variant, int *config) {
     if (*config < 0) *config = 0;
 }
 
-int run(int variant, int config_id, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
-        const float *B, int64_t ldb, float *C, int64_t ldc, void *stream) {
+int run(int variant, int config_id, int64_t batch, int64_t M, int64_t N, int64_t K,
+        const float *A, int64_t lda, int64_t sa, const float *B, int64_t ldb, int64_t sb,
+        float *C, int64_t ldc, int64_t sc, void *stream) {
     clear_error();
     int count = 0;
     const ConfigEntry *cfgs = configs_of(variant, &count);
     if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant);
     if (config_id < -1 || config_id >= count)
         return fail(GEMM_F32_ENOKERNEL, "variant %d has no configuration %d", variant, config_id);
-    int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
+    int rc = validate(batch, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, sc);
     if (rc != GEMM_F32_OK) return rc;
-    if (M == 0 || N == 0) return GEMM_F32_OK;
+    if (M == 0 || N == 0 || batch == 0) return GEMM_F32_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     if (K == 0) {
-        err = launch_zero_fill(C, static_cast<int>(M), static_cast<int>(N), ldc, s);
+        err = launch_zero_fill(C, static_cast<int>(M), static_cast<int>(N), ldc,
+                               static_cast<int>(batch), sc, s);
     } else {
         if (config_id == -1) {
             int v = 0;
-            select_config(M, N, K, &v, &config_id);
+            select_config(batch, M, N, K, &v, &config_id);
             if (v != variant) config_id = 0;
         }
         const Problem p{static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), A, lda, B,
-                        ldb, C, ldc};
+                        ldb, C, ldc, static_cast<int>(batch), sa, sb, sc};
         err = cfgs[config_id].launch(p, s);
     }
     if (err != hipSuccess)
@@ -166,11 +205,12 @@ int run(int variant, int config_id, int64_t M, int64_t N, int64_t K, const float
 
 }  // namespace
 
-hipError_t launch_zero_fill(float *C, int M, int N, int64_t ldc, hipStream_t stream) {
-    const int64_t total = static_cast<int64_t>(M) * N;
+hipError_t launch_zero_fill(float *C, int M, int N, int64_t ldc, int batch, int64_t sc,
+                            hipStream_t stream) {
+    const int64_t total = static_cast<int64_t>(M) * N * batch;
     const int64_t blocks = (total + 255) / 256;
     const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
-    hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, stream, C, M, N, ldc);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, stream, C, M, N, ldc, batch, sc);
     return hipGetLastError();
 }
 
@@ -182,18 +222,37 @@ extern "C" {
 
 int gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
              int64_t ldb, float *C, int64_t ldc, void *stream) {
-    clear_error();
-    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
-    if (rc != GEMM_F32_OK) return rc;
-    int variant = GEMM_F32_VARIANT_MFMA, config = 0;
-    select_config(M, N, K, &variant, &config);
-    return run(variant, config, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return gemm_f32_strided_batched(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, stream);
 }
 
 int gemm_f32_variant(int variant, int config_id, int64_t M, int64_t N, int64_t K, const float *A,
                      int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
                      void *stream) {
-    return run(variant, config_id, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return run(variant, config_id, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, stream);
+}
+
+int gemm_f32_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const float *A,
+                             int64_t lda, int64_t strideA, const float *B, int64_t ldb,
+                             int64_t strideB, float *C, int64_t ldc, int64_t strideC,
+                             void *stream) {
+    clear_error();
+    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
+    if (rc != GEMM_F32_OK) return rc;
+    rc = validate_batch(batch, M, N, K, lda, strideA, ldb, strideB, ldc, strideC);
+    if (rc != GEMM_F32_OK) return rc;
+    int variant = GEMM_F32_VARIANT_MFMA, config = 0;
+    select_config(batch > 0 ? batch : 1, M, N, K, &variant, &config);
+    return run(variant, config, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+               stream);
+}
+
+int gemm_f32_strided_batched_variant(int variant, int config_id, int64_t batch, int64_t M,
+                                     int64_t N, int64_t K, const float *A, int64_t lda,
+                                     int64_t strideA, const float *B, int64_t ldb,
+                                     int64_t strideB, float *C, int64_t ldc, int64_t strideC,
+                                     void *stream) {
+    return run(variant, config_id, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc,
+               strideC, stream);
 }
 
 const char *gemm_f32_strerror(int code) {
@@ -227,7 +286,7 @@ int gemm_f32_select(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, i
     if (rc != GEMM_F32_OK) return rc;
     if (variant == nullptr || config_id == nullptr)
         return fail(GEMM_F32_EINVAL, "NULL output pointer");
-    select_config(M, N, K, variant, config_id);
+    select_config(1, M, N, K, variant, config_id);
     return GEMM_F32_OK;
 }
 

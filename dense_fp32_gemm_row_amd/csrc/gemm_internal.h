@@ -21,7 +21,18 @@ struct Problem {
     int64_t ldb;
     float *C;
     int64_t ldc;
+    // Independent products C_b = A_b x B_b, b < batch, with X_b = X + b * sX
+    // (one product: batch 1, strides 0).
+    int batch;
+    int64_t sa, sb, sc;
 };
+
+// Batch description passed to the kernels.
+struct BatchArgs {
+    int count;
+    int64_t sa, sb, sc;
+};
+inline BatchArgs batch_of(const Problem &p) { return {p.batch, p.sa, p.sb, p.sc}; }
 
 // Host-side launch of one tile configuration.  Returns hipSuccess or the
 // error of the launch.
@@ -41,14 +52,16 @@ const ConfigEntry *mfma_configs(int *count);
 // Sets the C region to zero (the K == 0 case).  A fill kernel rather than a
 // memset so that a captured graph replays it faithfully and ldc padding is
 // never touched.
-hipError_t launch_zero_fill(float *C, int M, int N, int64_t ldc, hipStream_t stream);
+hipError_t launch_zero_fill(float *C, int M, int N, int64_t ldc, int batch, int64_t sc,
+                            hipStream_t stream);
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// 16-byte alignment of a base pointer and a leading dimension: float4
-// loads along a row are then aligned for every row.
-inline bool rows_aligned16(const float *p, int64_t ld) {
-    return (reinterpret_cast<uintptr_t>(p) % 16u) == 0 && (ld % 4) == 0;
+// 16-byte alignment of a base pointer, a leading dimension and a batch
+// stride: float4 loads along a row are then aligned for every row of every
+// product.
+inline bool rows_aligned16(const float *p, int64_t ld, int64_t stride = 0) {
+    return (reinterpret_cast<uintptr_t>(p) % 16u) == 0 && (ld % 4) == 0 && (stride % 4) == 0;
 }
 
 }  // namespace gemm_f32_impl
@@ -67,6 +80,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
     const int q = n / kXcds, r = n % kXcds;
     const int xcd = bid % kXcds, local = bid / kXcds;
     return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+// Splits a linear workgroup id over `tiles` tiles per product into the
+// product index (applied to the three base pointers) and the tile index.
+template <class PA, class PB, class PC>
+__device__ __forceinline__ int batch_select(int lin, int tiles, const gemm_f32_impl::BatchArgs &bt,
+                                            PA &A, PB &B, PC &C) {
+    const int b = lin / tiles;
+    A += static_cast<int64_t>(b) * bt.sa;
+    B += static_cast<int64_t>(b) * bt.sb;
+    C += static_cast<int64_t>(b) * bt.sc;
+    return lin - b * tiles;
 }
 
 // Grouped ordering of output tiles: consecutive logical ids walk down a

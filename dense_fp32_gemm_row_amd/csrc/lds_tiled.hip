@@ -34,12 +34,12 @@ template <int T, int PAD>
 __global__ __launch_bounds__(T * T) void gemm_lds_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
-    int tiles_n) {
+    int tiles_m, int tiles_n, BatchArgs bt) {
     __shared__ float tileA[T][T + PAD];
     __shared__ float tileB[T][T + PAD];
 
     const int tx = threadIdx.x, ty = threadIdx.y;
-    const int tile = blockIdx.x;
+    const int tile = batch_select(blockIdx.x, tiles_m * tiles_n, bt, A, B, C);
     const int tile_row = tile / tiles_n;
     const int tile_col = tile - tile_row * tiles_n;
     const int row = tile_row * T + ty;
@@ -67,10 +67,11 @@ template <int T, int PAD>
 hipError_t launch_lds(const Problem &p, hipStream_t stream) {
     const int tiles_n = ceil_div(p.N, T);
     const int tiles_m = ceil_div(p.M, T);
-    const int64_t grid = static_cast<int64_t>(tiles_n) * tiles_m;
+    const int64_t grid = static_cast<int64_t>(tiles_n) * tiles_m * p.batch;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gemm_lds_kernel<T, PAD>), dim3(static_cast<unsigned>(grid)), dim3(T, T),
-                       0, stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_n);
+                       0, stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m,
+                       tiles_n, batch_of(p));
     return hipGetLastError();
 }
 

@@ -79,7 +79,7 @@ template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, bool GUARD
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
-    int tiles_m, int tiles_n, int group_m) {
+    int tiles_m, int tiles_n, int group_m, BatchArgs bt) {
     constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;  // wavefront sub-tile
     constexpr int FM = WTM / 32, FN = WTN / 32;  // 32 x 32 blocks per wavefront
@@ -101,7 +101,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
     const int wm = wave / WN, wn = wave % WN;
 
     int tm, tn;
-    grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
+    const int tile = batch_select(xcd_remap(blockIdx.x, tiles_m * tiles_n * bt.count),
+                                  tiles_m * tiles_n, bt, A, B, C);
+    grouped_tile(tile, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     // Per-thread global load slots (fixed across K-steps).
@@ -232,7 +234,7 @@ template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
-    int tiles_m, int tiles_n, int group_m) {
+    int tiles_m, int tiles_n, int group_m, BatchArgs bt) {
     constexpr int NT = 64 * WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -267,7 +269,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
     const int wm = wave / WN, wn = wave % WN;
 
     int tm, tn;
-    grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
+    const int tile = batch_select(xcd_remap(blockIdx.x, tiles_m * tiles_n * bt.count),
+                                  tiles_m * tiles_n, bt, A, B, C);
+    grouped_tile(tile, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     int a_m[LA], a_k[LA], b_k[LB], b_n[LB];
@@ -512,9 +516,9 @@ template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int GROUP_
 hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     constexpr int NT = 64 * WM * WN;
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
-    const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n;
+    const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * p.batch;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool vec = rows_aligned16(p.A, p.lda) && rows_aligned16(p.B, p.ldb);
+    const bool vec = rows_aligned16(p.A, p.lda, p.sa) && rows_aligned16(p.B, p.ldb, p.sb);
     const bool guard = (p.M % BM) || (p.N % BN) || (p.K % BK);
     const dim3 g(static_cast<unsigned>(grid)), b(NT);
 #define GEMM_MFMA_LAUNCH(D, G, V)                                                               \
@@ -523,11 +527,11 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
             hipLaunchKernelGGL(                                                                 \
                 (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, D, G, V>), g, b, 0, \
                 stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,   \
-                GROUP_M);                                                                       \
+                GROUP_M, batch_of(p));                                                          \
         else                                                                                    \
             hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WM, WN, PADA, PADB, G, V>), g, b, 0, \
                                stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,       \
-                               tiles_m, tiles_n, GROUP_M);                                      \
+                               tiles_m, tiles_n, GROUP_M, batch_of(p));                         \
     } while (0)
     if (guard) {
         if (vec) GEMM_MFMA_LAUNCH(false, true, true);

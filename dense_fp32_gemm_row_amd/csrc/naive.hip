@@ -27,8 +27,8 @@ template <int BX, int BY>
 __global__ __launch_bounds__(BX * BY) void gemm_naive_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
-    int tiles_n) {
-    const int tile = blockIdx.x;
+    int tiles_m, int tiles_n, BatchArgs bt) {
+    const int tile = batch_select(blockIdx.x, tiles_m * tiles_n, bt, A, B, C);
     const int tile_row = tile / tiles_n;
     const int tile_col = tile - tile_row * tiles_n;
     const int row = tile_row * BY + threadIdx.y;  // vertical parts only
@@ -49,11 +49,11 @@ template <int BX, int BY>
 hipError_t launch_naive(const Problem &p, hipStream_t stream) {
     const int tiles_n = ceil_div(p.N, BX);
     const int tiles_m = ceil_div(p.M, BY);
-    const int64_t grid = static_cast<int64_t>(tiles_n) * tiles_m;
+    const int64_t grid = static_cast<int64_t>(tiles_n) * tiles_m * p.batch;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gemm_naive_kernel<BX, BY>), dim3(static_cast<unsigned>(grid)),
                        dim3(BX, BY), 0, stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb,
-                       p.C, p.ldc, tiles_n);
+                       p.C, p.ldc, tiles_m, tiles_n, batch_of(p));
     return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ template <int BM, int BN, int BK, int TM, int TN, int PAD, bool VEC>
 __global__ __launch_bounds__((BM / TM) * (BN / TN)) void gemm_regblock_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
-    int tiles_m, int tiles_n, bool vec_store) {
+    int tiles_m, int tiles_n, BatchArgs bt, bool vec_store) {
     constexpr int TX = BN / TN;  // threads along columns
     constexpr int TY = BM / TM;  // threads along rows
     constexpr int NT = TX * TY;
@@ -56,7 +56,9 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void gemm_regblock_kernel(
     const int tid = threadIdx.x;
     const int tx = tid % TX, ty = tid / TX;
     int tm, tn;
-    grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, 8, tm, tn);
+    const int tile = batch_select(xcd_remap(blockIdx.x, tiles_m * tiles_n * bt.count),
+                                  tiles_m * tiles_n, bt, A, B, C);
+    grouped_tile(tile, tiles_m, tiles_n, 8, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     float acc[TM][TN];
@@ -178,18 +180,20 @@ template <int BM, int BN, int BK, int TM, int TN, int PAD>
 hipError_t launch_regblock(const Problem &p, hipStream_t stream) {
     constexpr int NT = (BM / TM) * (BN / TN);
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
-    const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n;
+    const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * p.batch;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool vec = rows_aligned16(p.A, p.lda) && rows_aligned16(p.B, p.ldb);
-    const bool vec_store = rows_aligned16(p.C, p.ldc);
+    const bool vec = rows_aligned16(p.A, p.lda, p.sa) && rows_aligned16(p.B, p.ldb, p.sb);
+    const bool vec_store = rows_aligned16(p.C, p.ldc, p.sc);
     if (vec)
         hipLaunchKernelGGL((gemm_regblock_kernel<BM, BN, BK, TM, TN, PAD, true>),
                            dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream, p.M, p.N,
-                           p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, vec_store);
+                           p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, batch_of(p),
+                           vec_store);
     else
         hipLaunchKernelGGL((gemm_regblock_kernel<BM, BN, BK, TM, TN, PAD, false>),
                            dim3(static_cast<unsigned>(grid)), dim3(NT), 0, stream, p.M, p.N,
-                           p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, vec_store);
+                           p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, batch_of(p),
+                           vec_store);
     return hipGetLastError();
 }
 

@@ -25,6 +25,8 @@ Workloads (sizes are M x N x K; A is M x K, B is K x N, all row-major):
                      dimension is a multiple of 32 or 64
   * ``ffn``          M = 8192 tokens, K = 4096, N = 14336, normal (an FFN
                      up-projection shape)
+  * ``batched64_1024`` 64 independent 1024 x 1024 x 1024 products, uniform
+                     (A is 64 x M x K, B is 64 x K x N, drawn in that order)
 """
 
 from __future__ import annotations
@@ -42,10 +44,11 @@ class Workload:
     K: int
     dist: str
     seed: int = 0
+    batch: int = 1
 
     @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        return 2 * self.batch * self.M * self.N * self.K
 
 
 WORKLOADS: dict[str, Workload] = {
@@ -58,13 +61,14 @@ WORKLOADS: dict[str, Workload] = {
         Workload("ragged", 1000, 1023, 777, "uniform"),
         Workload("ragged_int4", 1000, 1023, 777, "int4"),
         Workload("ffn", 8192, 14336, 4096, "normal"),
+        Workload("batched64_1024", 1024, 1024, 1024, "uniform", batch=64),
     )
 }
 
 HEADLINE = "square8192"
 
 
-def draw(rng: np.random.Generator, shape: tuple[int, int], dist: str,
+def draw(rng: np.random.Generator, shape: tuple[int, ...], dist: str,
          scale: float = 1.0) -> np.ndarray:
     """One float32 matrix of the given distribution."""
     if dist == "uniform":
@@ -81,14 +85,16 @@ def draw(rng: np.random.Generator, shape: tuple[int, int], dist: str,
 
 
 def make_inputs(M: int, N: int, K: int, dist: str = "uniform",
-                seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
-    """Returns (A, B): A is M x K and B is K x N, float32, C-contiguous."""
+                seed: int = 0, batch: int = 1) -> tuple[np.ndarray, np.ndarray]:
+    """Returns (A, B): A is M x K and B is K x N, float32, C-contiguous; with
+    batch > 1, A is batch x M x K and B is batch x K x N."""
     rng = np.random.default_rng(seed)
-    A = draw(rng, (M, K), dist)
-    B = draw(rng, (K, N), dist, scale=0.02 if dist == "normal" else 1.0)
+    lead = (batch,) if batch > 1 else ()
+    A = draw(rng, lead + (M, K), dist)
+    B = draw(rng, lead + (K, N), dist, scale=0.02 if dist == "normal" else 1.0)
     return A, B
 
 
 def workload_inputs(name: str, seed: int | None = None) -> tuple[np.ndarray, np.ndarray]:
     w = WORKLOADS[name]
-    return make_inputs(w.M, w.N, w.K, w.dist, w.seed if seed is None else seed)
+    return make_inputs(w.M, w.N, w.K, w.dist, w.seed if seed is None else seed, w.batch)

@@ -108,6 +108,42 @@ int gemm_f32_variant(int variant, int config_id,
                      float *C, int64_t ldc,
                      void *stream);
 
+/*
+ * gemm_f32_strided_batched -- `batch` independent products
+ *
+ *   C_b = A_b x B_b,  X_b = X + b * strideX (in floats),  0 <= b < batch,
+ *
+ * each with the semantics of gemm_f32 (same M, N, K and leading dimensions
+ * for every product).  The products are the independent output tiles of the
+ * pages' decomposition ("Tiled Matrix Multiplication in CUDA", section 1:
+ * every cell of C is independent) laid out over one more index; the pages
+ * motivate GEMM by attention and mixture-of-experts layers, which are
+ * batches of such products.
+ *
+ *   batch          0 <= batch <= 2^31 - 1; 0 enqueues nothing
+ *   strideA/B      >= 0; 0 reuses one A (or B) for every product
+ *   strideC        >= (M - 1) * ldc + N when batch > 1, so the products'
+ *                  C regions do not overlap; batch * stride must stay below
+ *                  2^58 floats
+ *
+ * No C region may overlap any A or B region (checked on the address ranges
+ * spanned by the whole batch).  The configuration is chosen from the shape
+ * of one product and the total number of tiles.  Returns as gemm_f32.
+ */
+int gemm_f32_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                             const float *A, int64_t lda, int64_t strideA,
+                             const float *B, int64_t ldb, int64_t strideB,
+                             float *C, int64_t ldc, int64_t strideC,
+                             void *stream);
+
+/* gemm_f32_strided_batched with an explicit kernel, as gemm_f32_variant. */
+int gemm_f32_strided_batched_variant(int variant, int config_id,
+                                     int64_t batch, int64_t M, int64_t N, int64_t K,
+                                     const float *A, int64_t lda, int64_t strideA,
+                                     const float *B, int64_t ldb, int64_t strideB,
+                                     float *C, int64_t ldc, int64_t strideC,
+                                     void *stream);
+
 /* Static description of a return code; never NULL. */
 const char *gemm_f32_strerror(int code);
 

@@ -159,3 +159,32 @@ def test_generated_table_matches_json():
         expect = gen.render(json.load(f))
     with open(gen.OUT) as f:
         assert f.read() == expect, "csrc/tune_table.inc is stale: rebuild"
+
+
+# (batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC) rejected before any HIP call
+BAD_BATCH = [
+    ("negative batch", (-1, 4, 4, 4, 0x1000, 4, 16, 0x2000, 4, 16, 0x3000, 4, 16), "negative batch"),
+    ("batch too large", (1 << 31, 4, 4, 4, 0x1000, 4, 16, 0x2000, 4, 16, 0x3000, 4, 16), "batch"),
+    ("negative stride", (2, 4, 4, 4, 0x1000, 4, -16, 0x2000, 4, 16, 0x30000, 4, 16), "negative batch stride"),
+    ("C products overlap", (2, 4, 4, 4, 0x1000, 4, 16, 0x2000, 4, 16, 0x30000, 4, 15), "strideC"),
+    ("C batch reaches A", (3, 4, 4, 4, 0x1000, 4, 16, 0x8000, 4, 16, 0x1000 - 64, 4, 16), "overlaps A"),
+    ("C batch reaches B", (3, 4, 4, 4, 0x1000, 4, 16, 0x8000, 4, 0, 0x8000 - 96, 4, 16), "overlaps B"),
+    ("span too large", (1 << 20, 4, 4, 4, 0x1000, 4, 1 << 40, 0x2000, 4, 16, 0x3000, 4, 16), "2^58"),
+    ("lda < K", (2, 4, 4, 5, 0x1000, 4, 32, 0x2000, 4, 32, 0x3000, 4, 32), "lda"),
+]
+
+
+@pytest.mark.parametrize("args,detail", [(a, d) for _, a, d in BAD_BATCH],
+                         ids=[n for n, _, _ in BAD_BATCH])
+def test_invalid_batched_arguments(lib, args, detail):
+    assert b.gemm_f32_strided_batched(*args, None) == b.GEMM_F32_EINVAL
+    assert detail in b.gemm_f32_last_error()
+    for v in range(4):
+        assert b.gemm_f32_strided_batched_variant(v, 0, *args, None) == b.GEMM_F32_EINVAL
+
+
+def test_empty_batches_enqueue_nothing(lib):
+    assert b.gemm_f32_strided_batched(0, 4, 4, 4, 0, 4, 16, 0, 4, 16, 0, 4, 16, None) == 0
+    assert b.gemm_f32_strided_batched(5, 0, 4, 4, 0, 4, 16, 0, 4, 16, 0, 4, 16, None) == 0
+    # a single product ignores strideC's lower bound
+    assert b.gemm_f32_strided_batched(0, 4, 4, 4, 0, 4, 0, 0, 4, 0, 0, 4, 0, None) == 0

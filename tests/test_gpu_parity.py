@@ -255,6 +255,97 @@ def test_degenerate_shapes(shape):
 
 
 # --------------------------------------------------------------------------
+# strided batches
+# --------------------------------------------------------------------------
+
+BATCH_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4"), (1, 1, "lds_t32"),
+                 (2, 0, "regblock_128x128x8_t8x8_pad4")] + [
+    (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in (
+        "mfma_64x64x32_w2x2_pa4_pb0", "mfma_256x256x16_w2x4_pa4_pb0", "mfma3_256x256x16_w4x4_swz_pb0",
+        "mfma2p_256x256x32_w4x4_swz_pb0", "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz_g4")]
+
+
+def _run_batched(A3, B3, M, N, K, nb, sa, sb, sc, lda, ldb, ldc, kernel):
+    """Runs one strided-batched call on flat device buffers laid out with the
+    given strides; returns the whole C buffer (NaN outside the products)."""
+    import torch
+
+    dA = to_dev(A3)
+    dB = to_dev(B3)
+    csize = (nb - 1) * sc + (M - 1) * ldc + N + 17
+    dC = torch.full((csize,), float("nan"), device="cuda:0")
+    v, c, name = kernel
+    if v is None:
+        rc = b.gemm_f32_strided_batched(nb, M, N, K, dA.data_ptr(), lda, sa, dB.data_ptr(), ldb,
+                                        sb, dC.data_ptr(), ldc, sc, None)
+    else:
+        rc = b.gemm_f32_strided_batched_variant(v, c, nb, M, N, K, dA.data_ptr(), lda, sa,
+                                                dB.data_ptr(), ldb, sb, dC.data_ptr(), ldc, sc,
+                                                None)
+    assert rc == 0, b.gemm_f32_last_error()
+    return to_host(dC)
+
+
+def _layout(rng, nb, rows, cols, ld, stride, dist):
+    """A flat buffer holding nb matrices rows x cols (leading dimension ld,
+    stride floats apart; stride 0 = one shared matrix), padding NaN-free."""
+    n = (max(nb - 1, 0) * stride + (rows - 1) * ld + cols) if rows and cols else 1
+    if dist == "int4":
+        flat = rng.integers(-4, 5, size=n).astype(np.float32)
+    else:
+        flat = (2 * rng.random(n, dtype=np.float32) - 1).astype(np.float32)
+    mats = [flat[i * stride: i * stride + (rows - 1) * ld + cols] for i in range(nb)]
+    mats = [np.lib.stride_tricks.as_strided(m, shape=(rows, cols), strides=(4 * ld, 4))
+            for m in mats]
+    return flat, [np.ascontiguousarray(m) for m in mats]
+
+
+@pytest.mark.parametrize("kernel", BATCH_KERNELS, ids=[k[2] for k in BATCH_KERNELS])
+@pytest.mark.parametrize("dist", ["int4", "uniform"])
+def test_strided_batched(kernel, dist):
+    log(f"batched {dist} on {kernel[2]}")
+    rng = np.random.default_rng(21)
+    nb, M, N, K = 3, 130, 70, 50
+    lda, ldb, ldc = K + 3, N + 1, N + 5
+    sa = M * lda + 37            # gaps between the A matrices
+    sb = 0                       # one B shared by every product
+    sc = M * ldc + 11
+    A_flat, As = _layout(rng, nb, M, K, lda, sa, dist)
+    B_flat, Bs = _layout(rng, 1, K, N, ldb, 0, dist)
+    Bs = Bs * nb
+    C_all = _run_batched(A_flat, B_flat, M, N, K, nb, sa, sb, sc, lda, ldb, ldc, kernel)
+    written = np.zeros(C_all.shape, dtype=bool)
+    for i in range(nb):
+        view = np.lib.stride_tricks.as_strided(C_all[i * sc:], shape=(M, N), strides=(4 * ldc, 4))
+        ref32, ref64 = oracle.gemm(As[i], Bs[i], return_f64=True)
+        if dist == "int4":
+            assert_exact(np.array(view), ref32, f"{kernel[2]} product {i}")
+        else:
+            assert_close(np.array(view), ref64, K, f"{kernel[2]} product {i}")
+        for r in range(M):
+            written[i * sc + r * ldc: i * sc + r * ldc + N] = True
+    assert np.isnan(C_all[~written]).all(), "a write landed outside the products' C regions"
+
+
+@pytest.mark.parametrize("kernel", BATCH_KERNELS, ids=[k[2] for k in BATCH_KERNELS])
+def test_strided_batched_full_tiles(kernel):
+    """Whole tiles in every product (the unguarded and direct-load paths)."""
+    import torch
+
+    log(f"batched full tiles on {kernel[2]}")
+    nb, M, N, K = 2, 512, 256, 64
+    A, B = make_inputs(nb * M, N, K, "int4", seed=22)
+    A3 = A.reshape(nb, M, K)
+    B3 = np.stack([B, (B[::-1] * -1).copy()])
+    out = torch.empty((nb, M, N), device="cuda:0")
+    v, c, _ = kernel
+    b.gemm_batched(to_dev(A3), to_dev(B3), out, variant=v, config=c)
+    got = to_host(out)
+    for i in range(nb):
+        assert_exact(got[i], oracle.gemm(A3[i], B3[i]), f"{kernel[2]} product {i}")
+
+
+# --------------------------------------------------------------------------
 # full-size workloads in the benchmark's launch configuration
 # --------------------------------------------------------------------------
 
@@ -278,3 +369,20 @@ def test_full_size_sampled(wname):
     log(f"{wname}: sampled max err {stats['max_err']:.3e} relF {stats['rel_fro']:.3e} "
         f"freivalds {fr:.3e}")
     assert fr <= 1e-5, f"Freivalds residual {fr:.3e}"
+
+
+def test_full_size_batched_sampled():
+    import torch
+
+    w = WORKLOADS["batched64_1024"]
+    log(f"full size {w.name}: {w.batch} x {w.M}x{w.N}x{w.K}")
+    A, B = workload_inputs(w.name)
+    dC = torch.empty((w.batch, w.M, w.N), device="cuda:0")
+    b.gemm_batched(to_dev(A), to_dev(B), dC)
+    C = to_host(dC)
+    assert not np.isnan(C).any()
+    for i in (0, 17, w.batch - 1):
+        rows = sample_rows(w.M, count=12, seed=i)
+        _, ref64 = oracle_rows(A[i], B[i], rows)
+        assert_close(C[i][rows], ref64, w.K, f"{w.name} product {i}")
+        assert freivalds(A[i], B[i], C[i], seed=i) <= 1e-5
