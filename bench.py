@@ -148,6 +148,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--ops", default="NN", choices=["NN", "NT", "TN", "TT"],
+                    help="store A and/or B transposed (the product is the same)")
     ap.add_argument("--stages", action="store_true")
     ap.add_argument("--stage-variants", default="naive,lds,regblock,mfma",
                     help="variants that --stages times")
@@ -167,6 +169,10 @@ def main() -> int:
     from dense_fp32_gemm_row_amd import binding
     from dense_fp32_gemm_row_amd.workloads import WORKLOADS, workload_inputs
 
+    if args.ops != "NN" and (args.stages or args.variant is not None):
+        print("--ops applies to the library's own choice only", file=sys.stderr)
+        return 2
+
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
@@ -178,8 +184,13 @@ def main() -> int:
     log(f"workload {w.name}: M={M} N={N} K={K} dist={w.dist}")
     A, B = workload_inputs(w.name)
     dev = torch.device("cuda:0")
-    dA = torch.from_numpy(A).to(dev)
-    dB = torch.from_numpy(B).to(dev)
+    def stored(X, op):  # op(X) = X, kept as stored (N) or as a view of X^T (T)
+        if op == "N":
+            return torch.from_numpy(X).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(np.swapaxes(X, -1, -2))).to(dev).transpose(-1, -2)
+
+    dA = stored(A, args.ops[0])
+    dB = stored(B, args.ops[1])
     nb = w.batch
     dC = torch.empty((nb, M, N) if nb > 1 else (M, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -190,7 +201,8 @@ def main() -> int:
         return run_stages(args, w, A, B, dA, dB, dC, stream, flops)
 
     if args.variant is None:
-        v, c = binding.gemm_f32_select(M, N, K, K, N, N) if nb == 1 else (None, None)
+        v, c = (binding.gemm_f32_select(M, N, K, K, N, N) if nb == 1 and args.ops == "NN"
+                else (None, None))
     else:
         v = binding.VARIANTS[args.variant]
         if args.config:
@@ -199,7 +211,8 @@ def main() -> int:
             c = binding.gemm_f32_select(M, N, K, K, N, N)[1]
         else:
             c = 0
-    cname = binding.gemm_f32_config_name(v, c) if v is not None else "library choice (batched)"
+    cname = (binding.gemm_f32_config_name(v, c) if v is not None
+             else f"library choice ({'batched ' if nb > 1 else ''}{args.ops})")
     log(f"kernel {cname}")
 
     if args.variant is None:
@@ -230,8 +243,9 @@ def main() -> int:
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_FP32_MATRIX_TFLOPS, 2),
         "config": {"workload": w.name, "batch": nb, "M": M, "N": N, "K": K, "dist": w.dist,
-                   "seed": w.seed, "layout": "row-major A, B, C", "kernel": cname,
-                   "parallelism": "none"},
+                   "seed": w.seed, "ops": args.ops,
+                   "layout": "row-major C; A, B row-major, stored transposed where ops says T",
+                   "kernel": cname, "parallelism": "none"},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),

@@ -23,6 +23,9 @@ GEMM_F32_EINVAL = -1
 GEMM_F32_EHIP = -2
 GEMM_F32_ENOKERNEL = -3
 
+OP_N = 0  # operand as stored
+OP_T = 1  # operand transposed
+
 VARIANT_NAIVE = 0
 VARIANT_LDS = 1
 VARIANT_REGBLOCK = 2
@@ -70,6 +73,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gemm_f32_strided_batched_variant.restype = _int
     lib.gemm_f32_strided_batched_variant.argtypes = [_int, _int, _i64, _i64, _i64, _i64, _vp, _i64,
                                                      _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp]
+    lib.gemm_f32_ex.restype = _int
+    lib.gemm_f32_ex.argtypes = [_int, _int, _int, _int, _i64, _i64, _i64, _i64, _vp, _i64, _i64,
+                                _vp, _i64, _i64, _vp, _i64, _i64, _vp]
     lib.gemm_f32_strerror.restype = ctypes.c_char_p
     lib.gemm_f32_strerror.argtypes = [_int]
     lib.gemm_f32_last_error.restype = ctypes.c_char_p
@@ -107,6 +113,12 @@ def gemm_f32_strided_batched_variant(variant, config_id, batch, M, N, K, A, lda,
                                      C, ldc, sC, stream=None) -> int:
     return load().gemm_f32_strided_batched_variant(variant, config_id, batch, M, N, K, A, lda, sA,
                                                    B, ldb, sB, C, ldc, sC, stream)
+
+
+def gemm_f32_ex(variant, config_id, opA, opB, batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc,
+                sC, stream=None) -> int:
+    return load().gemm_f32_ex(variant, config_id, opA, opB, batch, M, N, K, A, lda, sA, B, ldb,
+                              sB, C, ldc, sC, stream)
 
 
 def gemm_f32_strerror(code: int) -> str:
@@ -151,61 +163,62 @@ def config_id(variant: int, name: str) -> int:
 
 # ---- tensor-level convenience ----------------------------------------------
 
-def _row_major_ld(t, name: str) -> int:
+def _operand(t, name: str, dims: int) -> tuple[int, int, int]:
+    """(op, leading dimension, batch stride) of a float32 GPU tensor holding
+    one (dims = 2) or a batch (dims = 3) of matrices.  A row-major matrix is
+    OP_N with ld = stride of its rows; a transposed view of a row-major
+    matrix (unit stride down the columns, e.g. ``X.T``) is OP_T with ld = the
+    stored row stride.  A batch stride of 0 (expanded tensor) is allowed."""
     import torch
 
-    if t.dtype != torch.float32 or t.dim() != 2 or not t.is_cuda:
-        raise TypeError(f"{name} must be a 2-D float32 GPU tensor")
-    rows, cols = t.shape
-    if cols > 1 and t.stride(1) != 1:
-        raise ValueError(f"{name} must have unit column stride (row-major)")
-    if rows <= 1:
-        return max(cols, 1)
-    return t.stride(0)
+    if t.dtype != torch.float32 or t.dim() != dims or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dims}-D float32 GPU tensor")
+    rows, cols = t.shape[-2], t.shape[-1]
+    rs, cs = t.stride(-2), t.stride(-1)
+    bs = t.stride(0) if dims == 3 else 0
+    if cols <= 1 or cs == 1:
+        return OP_N, (rs if rows > 1 else max(cols, 1)), bs
+    if rows <= 1 or rs == 1:
+        return OP_T, (cs if cols > 1 else max(rows, 1)), bs
+    raise ValueError(f"{name} must be row-major or a transposed view of a row-major matrix")
 
 
-def _batch_layout(t, name: str) -> tuple[int, int]:
-    """(leading dimension, batch stride) of a 3-D float32 GPU tensor whose
-    matrices are row-major; a batch stride of 0 (expanded tensor) is allowed."""
+def _call(A, B, out, variant, config, stream, batched: bool):
     import torch
 
-    if t.dtype != torch.float32 or t.dim() != 3 or not t.is_cuda:
-        raise TypeError(f"{name} must be a 3-D float32 GPU tensor")
-    _, rows, cols = t.shape
-    if cols > 1 and t.stride(2) != 1:
-        raise ValueError(f"{name} must have unit column stride (row-major)")
-    ld = t.stride(1) if rows > 1 else max(cols, 1)
-    return ld, t.stride(0)
-
-
-def gemm_batched(A, B, out=None, *, variant: int | str | None = None, config: int | str = -1,
-                 stream=None):
-    """``out[b] = A[b] @ B[b]`` for 3-D float32 GPU tensors through
-    gemm_f32_strided_batched (or its _variant form).  A or B may be an
-    expanded tensor (batch stride 0)."""
-    import torch
-
-    nb, M, K = A.shape
-    nb2, K2, N = B.shape
-    if nb != nb2 or K != K2:
+    dims = 3 if batched else 2
+    nb = A.shape[0] if batched else 1
+    M, K = A.shape[-2], A.shape[-1]
+    K2, N = B.shape[-2], B.shape[-1]
+    if K != K2 or (batched and B.shape[0] != nb):
         raise ValueError(f"shape mismatch {tuple(A.shape)} x {tuple(B.shape)}")
-    lda, sa = _batch_layout(A, "A")
-    ldb, sb = _batch_layout(B, "B")
+    opa, lda, sa = _operand(A, "A", dims)
+    opb, ldb, sb = _operand(B, "B", dims)
+    shape = (nb, M, N) if batched else (M, N)
     if out is None:
-        out = torch.empty((nb, M, N), dtype=torch.float32, device=A.device)
-    ldc, sc = _batch_layout(out, "out")
-    if tuple(out.shape) != (nb, M, N):
-        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(nb, M, N)}")
-    s = stream if stream is not None else torch.cuda.current_stream(A.device)
+        out = torch.empty(shape, dtype=torch.float32, device=A.device)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+    opc, ldc, sc = _operand(out, "out", dims)
+    if opc != OP_N:
+        raise ValueError("out must be row-major")
+    sp = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
     if variant is None:
-        rc = gemm_f32_strided_batched(nb, M, N, K, A.data_ptr(), lda, sa, B.data_ptr(), ldb, sb,
-                                      out.data_ptr(), ldc, sc, s.cuda_stream)
+        v, c = -1, -1
     else:
         v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
         c = config_id(v, config) if isinstance(config, str) else int(config)
-        rc = gemm_f32_strided_batched_variant(v, c, nb, M, N, K, A.data_ptr(), lda, sa,
-                                              B.data_ptr(), ldb, sb, out.data_ptr(), ldc, sc,
-                                              s.cuda_stream)
+    a, b, cp = A.data_ptr(), B.data_ptr(), out.data_ptr()
+    if opa == OP_N and opb == OP_N and not batched:
+        rc = (gemm_f32(M, N, K, a, lda, b, ldb, cp, ldc, sp) if v == -1 else
+              gemm_f32_variant(v, c, M, N, K, a, lda, b, ldb, cp, ldc, sp))
+    elif opa == OP_N and opb == OP_N:
+        rc = (gemm_f32_strided_batched(nb, M, N, K, a, lda, sa, b, ldb, sb, cp, ldc, sc, sp)
+              if v == -1 else
+              gemm_f32_strided_batched_variant(v, c, nb, M, N, K, a, lda, sa, b, ldb, sb, cp,
+                                               ldc, sc, sp))
+    else:
+        rc = gemm_f32_ex(v, c, opa, opb, nb, M, N, K, a, lda, sa, b, ldb, sb, cp, ldc, sc, sp)
     if rc != GEMM_F32_OK:
         raise GemmError(rc, gemm_f32_last_error())
     return out
@@ -213,35 +226,20 @@ def gemm_batched(A, B, out=None, *, variant: int | str | None = None, config: in
 
 def gemm(A, B, out=None, *, variant: int | str | None = None, config: int | str = -1,
          stream=None):
-    """``out = A @ B`` for row-major float32 GPU tensors through the C ABI.
+    """``out = A @ B`` for 2-D float32 GPU tensors through the C ABI.
 
-    ``variant`` None lets the library choose (gemm_f32); otherwise a variant
-    id or name with an optional configuration id or name (gemm_f32_variant).
-    Enqueued on ``stream`` (a torch.cuda.Stream), default torch's current
-    stream; returns ``out`` without synchronising.
+    A and B may be row-major or transposed views of row-major matrices
+    (``X.T``); ``out`` is row-major.  ``variant`` None lets the library
+    choose; otherwise a variant id or name with an optional configuration
+    id or name.  Enqueued on ``stream`` (a torch.cuda.Stream), default
+    torch's current stream; returns ``out`` without synchronising.
     """
-    import torch
+    return _call(A, B, out, variant, config, stream, batched=False)
 
-    M, K = A.shape
-    K2, N = B.shape
-    if K != K2:
-        raise ValueError(f"shape mismatch {tuple(A.shape)} x {tuple(B.shape)}")
-    lda = _row_major_ld(A, "A")
-    ldb = _row_major_ld(B, "B")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    ldc = _row_major_ld(out, "out")
-    if tuple(out.shape) != (M, N):
-        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
-    s = stream if stream is not None else torch.cuda.current_stream(A.device)
-    sp = s.cuda_stream
-    if variant is None:
-        rc = gemm_f32(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, out.data_ptr(), ldc, sp)
-    else:
-        v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
-        c = config_id(v, config) if isinstance(config, str) else int(config)
-        rc = gemm_f32_variant(v, c, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
-                              out.data_ptr(), ldc, sp)
-    if rc != GEMM_F32_OK:
-        raise GemmError(rc, gemm_f32_last_error())
-    return out
+
+def gemm_batched(A, B, out=None, *, variant: int | str | None = None, config: int | str = -1,
+                 stream=None):
+    """``out[b] = A[b] @ B[b]`` for 3-D float32 GPU tensors (strided batch;
+    A or B may be an expanded tensor with batch stride 0, and either may be
+    a batch of transposed views)."""
+    return _call(A, B, out, variant, config, stream, batched=True)

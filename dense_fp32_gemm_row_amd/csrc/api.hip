@@ -80,15 +80,22 @@ Span span_of_batch(const void *p, int64_t batch, int64_t stride, int64_t rows, i
 }
 bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 
-int validate_sizes(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+int validate_sizes(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                   bool ta = false, bool tb = false) {
     constexpr int64_t kMax = 0x7fffffff;
     if (M < 0 || N < 0 || K < 0) return fail(GEMM_F32_EINVAL, "negative size M=%lld N=%lld K=%lld",
                                              (long long)M, (long long)N, (long long)K);
     if (M > kMax || N > kMax || K > kMax)
         return fail(GEMM_F32_EINVAL, "size above 2^31-1 (M=%lld N=%lld K=%lld)", (long long)M,
                     (long long)N, (long long)K);
-    if (lda < (K > 1 ? K : 1)) return fail(GEMM_F32_EINVAL, "lda=%lld < max(1, K=%lld)", (long long)lda, (long long)K);
-    if (ldb < (N > 1 ? N : 1)) return fail(GEMM_F32_EINVAL, "ldb=%lld < max(1, N=%lld)", (long long)ldb, (long long)N);
+    // a stored row of A holds K floats (M when transposed), of B N (K)
+    const int64_t a_row = ta ? M : K, b_row = tb ? K : N;
+    if (lda < (a_row > 1 ? a_row : 1))
+        return fail(GEMM_F32_EINVAL, "lda=%lld < max(1, %s=%lld)", (long long)lda, ta ? "M" : "K",
+                    (long long)a_row);
+    if (ldb < (b_row > 1 ? b_row : 1))
+        return fail(GEMM_F32_EINVAL, "ldb=%lld < max(1, %s=%lld)", (long long)ldb, tb ? "K" : "N",
+                    (long long)b_row);
     if (ldc < (N > 1 ? N : 1)) return fail(GEMM_F32_EINVAL, "ldc=%lld < max(1, N=%lld)", (long long)ldc, (long long)N);
     // Largest flat element index must stay addressable with 64-bit offsets.
     const int64_t kLdMax = (int64_t{1} << 62) / (kMax + 1);
@@ -119,10 +126,10 @@ int validate_batch(int64_t batch, int64_t M, int64_t N, int64_t K, int64_t lda, 
     return GEMM_F32_OK;
 }
 
-int validate(int64_t batch, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
-             int64_t sa, const float *B, int64_t ldb, int64_t sb, const float *C, int64_t ldc,
-             int64_t sc) {
-    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
+int validate(bool ta, bool tb, int64_t batch, int64_t M, int64_t N, int64_t K, const float *A,
+             int64_t lda, int64_t sa, const float *B, int64_t ldb, int64_t sb, const float *C,
+             int64_t ldc, int64_t sc) {
+    int rc = validate_sizes(M, N, K, lda, ldb, ldc, ta, tb);
     if (rc != GEMM_F32_OK) return rc;
     rc = validate_batch(batch, M, N, K, lda, sa, ldb, sb, ldc, sc);
     if (rc != GEMM_F32_OK) return rc;
@@ -135,17 +142,18 @@ int validate(int64_t batch, int64_t M, int64_t N, int64_t K, const float *A, int
         (need_b && reinterpret_cast<uintptr_t>(B) % 4))
         return fail(GEMM_F32_EINVAL, "pointer not 4-byte aligned");
     const Span scs = span_of_batch(C, batch, sc, M, N, ldc);
-    if (need_a && overlaps(scs, span_of_batch(A, batch, sa, M, K, lda)))
-        return fail(GEMM_F32_EINVAL, "C overlaps A");
-    if (need_b && overlaps(scs, span_of_batch(B, batch, sb, K, N, ldb)))
-        return fail(GEMM_F32_EINVAL, "C overlaps B");
+    const Span sas = ta ? span_of_batch(A, batch, sa, K, M, lda) : span_of_batch(A, batch, sa, M, K, lda);
+    const Span sbs = tb ? span_of_batch(B, batch, sb, N, K, ldb) : span_of_batch(B, batch, sb, K, N, ldb);
+    if (need_a && overlaps(scs, sas)) return fail(GEMM_F32_EINVAL, "C overlaps A");
+    if (need_b && overlaps(scs, sbs)) return fail(GEMM_F32_EINVAL, "C overlaps B");
     return GEMM_F32_OK;
 }
 
 // The tile configuration gemm_f32 uses for a shape: an exact entry of the
 // tuned table if there is one, else the rule-based choice below.
-void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant, int *config) {
-    if (batch == 1) {
+void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant, int *config,
+                   bool trans = false) {
+    if (batch == 1 && !trans) {
         for (const TuneEntry &e : kTuneTable) {
             if (e.M == M && e.N == N && e.K == K) {
                 const int id = find_config(e.variant, e.config);
@@ -162,24 +170,29 @@ void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant,
     // number of tiles.
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256) * batch;
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128) * batch;
-    const char *name = kDefaultSmall;
-    if (t256 >= 512) name = kDefaultLarge;
-    else if (t128 >= 256) name = kDefaultMedium;
+    const char *name = trans ? kTransposedSmall : kDefaultSmall;
+    if (t256 >= 512) name = trans ? kTransposedLarge : kDefaultLarge;
+    else if (t128 >= 256) name = trans ? kTransposedMedium : kDefaultMedium;
     *variant = GEMM_F32_VARIANT_MFMA;
     *config = find_config(GEMM_F32_VARIANT_MFMA, name);
     if (*config < 0) *config = 0;
 }
 
-int run(int variant, int config_id, int64_t batch, int64_t M, int64_t N, int64_t K,
-        const float *A, int64_t lda, int64_t sa, const float *B, int64_t ldb, int64_t sb,
-        float *C, int64_t ldc, int64_t sc, void *stream) {
+int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, int64_t N,
+        int64_t K, const float *A, int64_t lda, int64_t sa, const float *B, int64_t ldb,
+        int64_t sb, float *C, int64_t ldc, int64_t sc, void *stream) {
     clear_error();
     int count = 0;
+    if (variant == -1) {  // the library's choice
+        int rc = validate_sizes(M, N, K, lda, ldb, ldc, ta, tb);
+        if (rc != GEMM_F32_OK) return rc;
+        select_config(batch > 0 ? batch : 1, M, N, K, &variant, &config_id, ta || tb);
+    }
     const ConfigEntry *cfgs = configs_of(variant, &count);
     if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant);
     if (config_id < -1 || config_id >= count)
         return fail(GEMM_F32_ENOKERNEL, "variant %d has no configuration %d", variant, config_id);
-    int rc = validate(batch, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, sc);
+    int rc = validate(ta, tb, batch, M, N, K, A, lda, sa, B, ldb, sb, C, ldc, sc);
     if (rc != GEMM_F32_OK) return rc;
     if (M == 0 || N == 0 || batch == 0) return GEMM_F32_OK;
 
@@ -191,11 +204,19 @@ int run(int variant, int config_id, int64_t batch, int64_t M, int64_t N, int64_t
     } else {
         if (config_id == -1) {
             int v = 0;
-            select_config(batch, M, N, K, &v, &config_id);
-            if (v != variant) config_id = 0;
+            select_config(batch, M, N, K, &v, &config_id, ta || tb);
+            if (v != variant) {  // first configuration of the asked variant that fits
+                config_id = 0;
+                if (ta || tb)
+                    while (config_id + 1 < count && !(cfgs[config_id].caps & kCapTransposed))
+                        ++config_id;
+            }
         }
+        if ((ta || tb) && !(cfgs[config_id].caps & kCapTransposed))
+            return fail(GEMM_F32_ENOKERNEL, "configuration %s does not take transposed operands",
+                        cfgs[config_id].name);
         const Problem p{static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), A, lda, B,
-                        ldb, C, ldc, static_cast<int>(batch), sa, sb, sc};
+                        ldb, C, ldc, static_cast<int>(batch), sa, sb, sc, ta, tb};
         err = cfgs[config_id].launch(p, s);
     }
     if (err != hipSuccess)
@@ -222,13 +243,15 @@ extern "C" {
 
 int gemm_f32(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
              int64_t ldb, float *C, int64_t ldc, void *stream) {
-    return gemm_f32_strided_batched(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, stream);
+    return run(-1, -1, false, false, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, stream);
 }
 
 int gemm_f32_variant(int variant, int config_id, int64_t M, int64_t N, int64_t K, const float *A,
                      int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
                      void *stream) {
-    return run(variant, config_id, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, stream);
+    if (variant < 0) return (clear_error(), fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant));
+    return run(variant, config_id, false, false, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0,
+               stream);
 }
 
 int gemm_f32_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const float *A,
@@ -236,14 +259,10 @@ int gemm_f32_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K, con
                              int64_t strideB, float *C, int64_t ldc, int64_t strideC,
                              void *stream) {
     clear_error();
-    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
+    int rc = validate_batch(batch, M, N, K, lda, strideA, ldb, strideB, ldc, strideC);
     if (rc != GEMM_F32_OK) return rc;
-    rc = validate_batch(batch, M, N, K, lda, strideA, ldb, strideB, ldc, strideC);
-    if (rc != GEMM_F32_OK) return rc;
-    int variant = GEMM_F32_VARIANT_MFMA, config = 0;
-    select_config(batch > 0 ? batch : 1, M, N, K, &variant, &config);
-    return run(variant, config, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
-               stream);
+    return run(-1, -1, false, false, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc,
+               strideC, stream);
 }
 
 int gemm_f32_strided_batched_variant(int variant, int config_id, int64_t batch, int64_t M,
@@ -251,8 +270,25 @@ int gemm_f32_strided_batched_variant(int variant, int config_id, int64_t batch, 
                                      int64_t strideA, const float *B, int64_t ldb,
                                      int64_t strideB, float *C, int64_t ldc, int64_t strideC,
                                      void *stream) {
-    return run(variant, config_id, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc,
-               strideC, stream);
+    if (variant < 0) return (clear_error(), fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant));
+    return run(variant, config_id, false, false, batch, M, N, K, A, lda, strideA, B, ldb, strideB,
+               C, ldc, strideC, stream);
+}
+
+int gemm_f32_ex(int variant, int config_id, int opA, int opB, int64_t batch, int64_t M,
+                int64_t N, int64_t K, const float *A, int64_t lda, int64_t strideA,
+                const float *B, int64_t ldb, int64_t strideB, float *C, int64_t ldc,
+                int64_t strideC, void *stream) {
+    clear_error();
+    if ((opA != GEMM_F32_OP_N && opA != GEMM_F32_OP_T) ||
+        (opB != GEMM_F32_OP_N && opB != GEMM_F32_OP_T))
+        return fail(GEMM_F32_EINVAL, "opA/opB must be GEMM_F32_OP_N or GEMM_F32_OP_T");
+    if (variant < -1) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant);
+    const bool ta = opA == GEMM_F32_OP_T, tb = opB == GEMM_F32_OP_T;
+    int rc = validate_batch(batch, M, N, K, lda, strideA, ldb, strideB, ldc, strideC);
+    if (rc != GEMM_F32_OK) return rc;
+    return run(variant, variant == -1 ? -1 : config_id, ta, tb, batch, M, N, K, A, lda, strideA,
+               B, ldb, strideB, C, ldc, strideC, stream);
 }
 
 const char *gemm_f32_strerror(int code) {

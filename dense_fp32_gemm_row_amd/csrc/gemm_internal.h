@@ -25,6 +25,9 @@ struct Problem {
     // (one product: batch 1, strides 0).
     int batch;
     int64_t sa, sb, sc;
+    // Transposed operands: op(A) = A^T with A stored K x M (row-major, lda),
+    // op(B) = B^T with B stored N x K (ldb).
+    bool ta, tb;
 };
 
 // Batch description passed to the kernels.
@@ -38,9 +41,13 @@ inline BatchArgs batch_of(const Problem &p) { return {p.batch, p.sa, p.sb, p.sc}
 // error of the launch.
 using LaunchFn = hipError_t (*)(const Problem &, hipStream_t);
 
+// Capabilities of a configuration beyond plain row-major operands.
+constexpr unsigned kCapTransposed = 1u;  // accepts transposed A and/or B
+
 struct ConfigEntry {
     const char *name;  // stable, used by the tuning table and benchmarks
     LaunchFn launch;
+    unsigned caps;
 };
 
 // Registries, one per variant (defined in the kernel sources).

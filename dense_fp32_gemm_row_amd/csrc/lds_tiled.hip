@@ -65,6 +65,7 @@ __global__ __launch_bounds__(T * T) void gemm_lds_kernel(
 
 template <int T, int PAD>
 hipError_t launch_lds(const Problem &p, hipStream_t stream) {
+    if (p.ta || p.tb) return hipErrorNotSupported;
     const int tiles_n = ceil_div(p.N, T);
     const int tiles_m = ceil_div(p.M, T);
     const int64_t grid = static_cast<int64_t>(tiles_n) * tiles_m * p.batch;
@@ -76,10 +77,10 @@ hipError_t launch_lds(const Problem &p, hipStream_t stream) {
 }
 
 const ConfigEntry kLdsConfigs[] = {
-    {"lds_t16", launch_lds<16, 0>},
-    {"lds_t32", launch_lds<32, 0>},
-    {"lds_t16_pad1", launch_lds<16, 1>},
-    {"lds_t32_pad1", launch_lds<32, 1>},
+    {"lds_t16", launch_lds<16, 0>, 0},
+    {"lds_t32", launch_lds<32, 0>, 0},
+    {"lds_t16_pad1", launch_lds<16, 1>, 0},
+    {"lds_t32_pad1", launch_lds<32, 1>, 0},
 };
 
 }  // namespace

@@ -215,53 +215,191 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
     }
 }
 
-// Pipelined variant, with a ring of STAGES (2 or 3) LDS buffers.  Within a
+// One operand of the pipelined kernel: the R x BK slice (R = BM rows of op(A)
+// or BN columns of op(B)) that one K-step stages through LDS.
+//
+// Two storage flavours, chosen by how the operand lies in memory:
+//  * row flavour (KMAJOR = false): element (r, k) at X[r * ld + k], k
+//    contiguous -- A as stored, or B transposed.  LDS holds R rows of BK
+//    floats; a lane's 4 values of one chunk (k = 4 kk .. 4 kk + 3, see the
+//    operand layout above) are one 16-byte read.  The rows are padded by PAD
+//    floats when PAD > 0, otherwise their 16-byte slots are XOR-swizzled.
+//  * k-major flavour (KMAJOR = true): element (r, k) at X[k * ld + r], r
+//    contiguous -- B as stored, or A transposed.  LDS holds BK rows of R
+//    floats (+ PAD when PAD > 0); a lane reads its 4 values as 4 single
+//    floats, 32 consecutive r per half wavefront.
+// Register staging (with zero fill outside the matrix) and direct
+// global -> LDS loads are provided for both.
+template <int R, int BK, int PAD, bool KMAJOR, int NT, int NW, bool GUARD, bool VEC, bool DIRECT>
+struct OperandTile {
+    static constexpr bool SWZ = !KMAJOR && PAD <= 0;
+    static constexpr int LD = KMAJOR ? R + (PAD > 0 ? PAD : 0) : BK + (SWZ ? 0 : PAD);  // row length
+    static constexpr int SIZE = KMAJOR ? BK * LD : R * LD;               // floats per buffer
+    static constexpr int L = (R * BK) / (4 * NT);                        // float4 slots per thread
+    static constexpr int S = BK / 4;                                     // 16-byte slots per row
+    static constexpr int LOG2S = S == 2 ? 1 : S == 4 ? 2 : S == 8 ? 3 : 4;
+    static constexpr int CH = R * BK / 256;                              // 1 KiB chunks
+    static constexpr int J = DIRECT ? CH / NW : 1;
+    static_assert(L * 4 * NT == R * BK, "even tile split");
+    static_assert(LD % 4 == 0, "16-byte aligned LDS rows");
+    static_assert(!DIRECT || (PAD <= 0 && !GUARD && VEC), "direct loads: unpadded full tiles");
+    static_assert(!DIRECT || CH % NW == 0, "whole chunks per wavefront");
+
+    // XOR swizzle of the row flavour: slot q of row m is stored at slot
+    // q ^ g(m), g(m) = (r ^ (r >> log2 S)) mod S with r = m mod 32.  A
+    // wavefront's 16-byte reads (32 consecutive rows of one 32-row block, one
+    // slot) and its 16-byte stores (S lanes per row, 64 / S consecutive rows
+    // inside one 32-row block) then hit disjoint banks, whether the LDS
+    // serves 8 or 16 such accesses per cycle.  Depending on m mod 32 only,
+    // g is the same for every 32-row block a lane reads.
+    static __device__ __forceinline__ int swz(int m) {
+        return ((m & 31) ^ ((m & 31) >> LOG2S)) & (S - 1);
+    }
+
+    const float *X;
+    int64_t ld;
+    int r0, rlim;
+    int ro[L], co[L], st[L];  // tile coordinates and LDS offset of each slot
+    float4 reg[L];
+    const float *src[J];
+    int dst[J];
+
+    __device__ __forceinline__ void init(const float *X_, int64_t ld_, int r0_, int rlim_, int tid,
+                                         int wave, int lane) {
+        X = X_, ld = ld_, r0 = r0_, rlim = rlim_;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int e = tid + i * NT;
+            if constexpr (KMAJOR) {
+                ro[i] = e / (R / 4);        // k row
+                co[i] = (e % (R / 4)) * 4;  // r column
+                st[i] = ro[i] * LD + co[i];
+            } else {
+                ro[i] = e / S;              // r row
+                co[i] = (e % S) * 4;        // k column
+                st[i] = ro[i] * LD + (SWZ ? ((co[i] / 4) ^ swz(ro[i])) * 4 : co[i]);
+            }
+        }
+        if constexpr (DIRECT) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int c = wave + j * NW;
+                dst[j] = c * 256;
+                if constexpr (KMAJOR) {
+                    const int f = c * 256 + lane * 4;  // float offset in the k-major tile
+                    src[j] = X + static_cast<int64_t>(f / R) * ld + r0 + f % R;
+                } else {
+                    const int m = c * (64 / S) + lane / S;  // tile row of this lane's slot
+                    const int q = (lane % S) ^ swz(m);      // logical slot stored there
+                    src[j] = X + static_cast<int64_t>(r0 + m) * ld + 4 * q;
+                }
+            }
+        }
+    }
+
+    // Register staging of the tile of K-step starting at k0.
+    __device__ __forceinline__ void load(int k0, int K) {
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            if constexpr (KMAJOR) {
+                const int gk = k0 + ro[i];
+                const bool ok = !GUARD || gk < K;
+                const float *row = X + static_cast<int64_t>(ok ? gk : 0) * ld + r0;
+                reg[i] = load_row4<GUARD, VEC>(row, co[i], rlim - r0, ok);
+            } else {
+                const bool ok = !GUARD || r0 + ro[i] < rlim;
+                const float *row = X + static_cast<int64_t>(ok ? r0 + ro[i] : 0) * ld;
+                reg[i] = load_row4<GUARD, VEC>(row, k0 + co[i], K, ok);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(float *buf) const {
+#pragma unroll
+        for (int i = 0; i < L; ++i) *reinterpret_cast<float4 *>(&buf[st[i]]) = reg[i];
+    }
+
+    // Direct loads of the tile of K-step k0 into `buf`: one instruction moves
+    // 64 x 16 bytes into 1 KiB of contiguous LDS, lane L's 16 bytes at offset
+    // 16 L; each lane fetches the element that belongs at its slot (for the
+    // row flavour, the inverse of the swizzle).
+    __device__ __forceinline__ void load_direct(int k0, float *buf) const {
+        typedef const __attribute__((address_space(1))) void *gptr_t;
+        typedef __attribute__((address_space(3))) void *lptr_t;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const float *g = KMAJOR ? src[j] + static_cast<int64_t>(k0) * ld : src[j] + k0;
+            __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)(&buf[dst[j]]), 16, 0, 0);
+        }
+    }
+
+    // The 4 values (k = kc * 8 + 4 * half + s, s = 0..3) of F blocks of 32
+    // rows starting at row `rbase`, for lane l32 of half wavefront `half`.
+    template <int F>
+    __device__ __forceinline__ void read(const float *buf, int kc, int rbase, int half, int l32,
+                                         float (&v)[F][4]) const {
+        if constexpr (KMAJOR) {
+            const float *p = buf + (kc * 8 + 4 * half) * LD + rbase + l32;
+#pragma unroll
+            for (int f = 0; f < F; ++f)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) v[f][s] = p[s * LD + f * 32];
+        } else {
+            const int slot = SWZ ? (2 * kc + half) ^ swz(l32) : 2 * kc + half;
+            const float *p = buf + (rbase + l32) * LD + slot * 4;
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+                const float4 q = *reinterpret_cast<const float4 *>(p + f * 32 * LD);
+                v[f][0] = q.x, v[f][1] = q.y, v[f][2] = q.z, v[f][3] = q.w;
+            }
+        }
+    }
+
+    // LDS read instructions per chunk for F blocks (pairs of k-major blocks
+    // 32 floats apart merge into one two-address read).
+    template <int F>
+    static constexpr int reads() { return KMAJOR ? 4 * ((F + 1) / 2) : F; }
+};
+
+// Pipelined kernel, with a ring of STAGES (2 or 3) LDS buffers.  Within a
 // K-step the fragments of the next chunk of 8 k are read while the MFMAs of
-// the current chunk run (two register sets, alternating).  With a ring of
-// three LDS buffers, in addition, the tile of K-step
-// t + 1 is complete and published (by the barrier that ended step t - 1)
-// while step t still runs, so each wavefront reads its first operand
-// fragments of step t + 1 before the barrier that ends step t, and the
-// matrix cores restart right after the barrier instead of waiting on LDS.
+// the current chunk run (two register sets, alternating).  With three
+// buffers, in addition, the tile of K-step t + 1 is complete and published
+// (by the barrier that ended step t - 1) while step t still runs, so each
+// wavefront reads its first operand fragments of step t + 1 before the
+// barrier that ends step t, and the matrix cores restart right after the
+// barrier instead of waiting on LDS.
 //
 // Hazards, with three buffers and b(t) = t mod 3: step t writes tile t + 2 into
 // b(t + 2) = b(t - 1), last read in step t - 1, i.e. before the barrier that
 // ended step t - 1 (write after read); tile t + 2 is first read in step
-// t + 1, after the barrier that ends step t (read after write).  With two
-// buffers the scheme is the one of the first kernel.
+// t + 1, after the barrier that ends step t (read after write).  Two buffers:
+// see the barrier placement in the K loop.
+//
+// TA / TB: op(A) = A^T (A stored K x M) / op(B) = B^T (B stored N x K); a
+// transposed operand swaps storage flavour (see OperandTile), nothing else
+// changes.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
-          bool GUARD, bool VEC>
+          bool GUARD, bool VEC, bool TA, bool TB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n, int group_m, BatchArgs bt) {
-    constexpr int NT = 64 * WM * WN;
+    constexpr int NT = 64 * WM * WN, NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int LA = (BM * BK) / (4 * NT);
-    constexpr int LB = (BK * BN) / (4 * NT);
-    // PADA >= 0: A rows padded by PADA floats.  PADA < 0: unpadded A rows
-    // whose 16-byte slots are permuted by an XOR with a function of the row.
-    constexpr bool SWZ = PADA < 0;
-    constexpr int LDA_S = BK + (SWZ ? 0 : PADA), LDB_S = BN + PADB;
-    constexpr int S = BK / 4;                              // 16-byte slots per A row
-    constexpr int LOG2S = S == 2 ? 1 : S == 4 ? 2 : S == 8 ? 3 : 4;
     constexpr int KC = BK / 8;  // chunks of 8 k per K-step
-    // LDS read instructions per chunk: one 16-byte read per row block of A,
-    // and the 4 k values of each B column block (pairs of column blocks
-    // 32 floats apart merge into one two-address read).
-    constexpr int kReadsPerChunk = FM + 4 * ((FN + 1) / 2);
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32 x 32 blocks");
-    static_assert(BK % 16 == 0, "an even number of chunks per K-step");
+    using TileA = OperandTile<BM, BK, PADA, TA, NT, NW, GUARD, VEC, DIRECT>;
+    using TileB = OperandTile<BN, BK, PADB, !TB, NT, NW, GUARD, VEC, DIRECT>;
+    constexpr int kReadsPerChunk = TileA::template reads<FM>() + TileB::template reads<FN>();
     constexpr int kMfmaPerChunk = FM * FN * 4;
     constexpr int kPairs = kReadsPerChunk < kMfmaPerChunk ? kReadsPerChunk : kMfmaPerChunk;
-    static_assert(LA * 4 * NT == BM * BK && LB * 4 * NT == BK * BN, "even tile split");
-    static_assert(LDA_S % 4 == 0 && LDB_S % 4 == 0, "16-byte aligned LDS rows");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32 x 32 blocks");
+    static_assert(BK % 16 == 0, "an even number of chunks per K-step");
     static_assert(STAGES == 2 || STAGES == 3, "two or three LDS buffers");
-    static_assert(STAGES * (BM * LDA_S + BK * LDB_S) * 4 <= kLdsBytes, "LDS budget of a workgroup");
+    static_assert(STAGES * (TileA::SIZE + TileB::SIZE) * 4 <= kLdsBytes, "LDS budget of a workgroup");
 
-    __shared__ __align__(16) float sA[STAGES][BM * LDA_S];
-    __shared__ __align__(16) float sB[STAGES][BK * LDB_S];
+    __shared__ __align__(16) float sA[STAGES][TileA::SIZE];
+    __shared__ __align__(16) float sB[STAGES][TileB::SIZE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -274,125 +412,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
     grouped_tile(tile, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    int a_m[LA], a_k[LA], b_k[LB], b_n[LB];
-    const float *a_row[LA];
-    bool a_ok[LA];
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-        const int e = tid + i * NT;
-        a_m[i] = e / (BK / 4);
-        a_k[i] = (e % (BK / 4)) * 4;
-        const int gm = m0 + a_m[i];
-        a_ok[i] = gm < M;
-        a_row[i] = A + static_cast<int64_t>(a_ok[i] ? gm : 0) * lda;
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-        const int e = tid + i * NT;
-        b_k[i] = e / (BN / 4);
-        b_n[i] = (e % (BN / 4)) * 4;
-    }
-
-    float4 ra[LA], rb[LB];
-    auto load_global = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < LA; ++i)
-            ra[i] = load_row4<GUARD, VEC>(a_row[i], k0 + a_k[i], K, a_ok[i]);
-#pragma unroll
-        for (int i = 0; i < LB; ++i) {
-            const int gk = k0 + b_k[i];
-            const bool ok = !GUARD || gk < K;
-            const float *row = B + static_cast<int64_t>(ok ? gk : 0) * ldb + n0;
-            rb[i] = load_row4<GUARD, VEC>(row, b_n[i], N - n0, ok);
+    TileA ta;
+    TileB tb;
+    ta.init(A, lda, m0, M, tid, wave, lane);
+    tb.init(B, ldb, n0, N, tid, wave, lane);
+    auto load_step = [&](int k0, int buf) {
+        if constexpr (DIRECT) {
+            ta.load_direct(k0, sA[buf]);
+            tb.load_direct(k0, sB[buf]);
+        } else {
+            ta.load(k0, K);
+            tb.load(k0, K);
         }
     };
-    // XOR swizzle of the A tile: slot q of row m is stored at slot
-    // q ^ g(m), g(m) = (r ^ (r >> log2 S)) mod S with r = m mod 32.  A
-    // wavefront's 16-byte reads (32 consecutive rows of one 32-row block, one
-    // slot) and its 16-byte stores (S lanes per row, 64 / S consecutive rows
-    // inside one 32-row block) then hit disjoint banks, whether the LDS
-    // serves 8 or 16 such accesses per cycle.  Depending on m mod 32 only,
-    // g is the same for every 32-row block a lane reads.
-    auto swz = [](int m) { return ((m & 31) ^ ((m & 31) >> LOG2S)) & (S - 1); };
-    int a_st[LA];
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-        a_st[i] = a_m[i] * LDA_S + (SWZ ? ((a_k[i] / 4) ^ swz(a_m[i])) * 4 : a_k[i]);
-    auto store_lds = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < LA; ++i)
-            *reinterpret_cast<float4 *>(&sA[buf][a_st[i]]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < LB; ++i)
-            *reinterpret_cast<float4 *>(&sB[buf][b_k[i] * LDB_S + b_n[i]]) = rb[i];
-    };
-
-    // Direct global -> LDS loads (global_load_lds_dwordx4): one instruction
-    // moves 64 x 16 bytes into 1 KiB of contiguous LDS, lane L's 16 bytes at
-    // offset 16 L.  The tiles are cut into 1 KiB chunks, dealt round-robin to
-    // the wavefronts, and each lane fetches the global element that belongs
-    // at its LDS slot: for A the inverse of the XOR swizzle, for B the plain
-    // row-major position.  No registers hold the tile in flight and no LDS
-    // store instructions are issued; the barrier's wait on the memory
-    // counter completes the copy.  Only for full, 16-byte-aligned tiles.
-    constexpr int NW = WM * WN;
-    constexpr int CA = BM * BK / 256, CB = BK * BN / 256;  // 1 KiB chunks per tile
-    constexpr int JA = DIRECT ? CA / NW : 1, JB = DIRECT ? CB / NW : 1;
-    static_assert(!DIRECT || (SWZ && PADB == 0 && !GUARD && VEC), "direct loads: unpadded full tiles");
-    static_assert(!DIRECT || (CA % NW == 0 && CB % NW == 0), "whole chunks per wavefront");
-    const float *a_src[JA], *b_src[JB];
-    int a_dst[JA], b_dst[JB];
-    if constexpr (DIRECT) {
-#pragma unroll
-        for (int j = 0; j < JA; ++j) {
-            const int c = wave + j * NW;
-            const int m = c * (64 / S) + lane / S;          // tile row of this lane
-            const int q = (lane % S) ^ swz(m);             // logical slot stored here
-            a_src[j] = A + static_cast<int64_t>(m0 + m) * lda + 4 * q;
-            a_dst[j] = c * 256;
+    auto store_step = [&](int buf) {
+        if constexpr (!DIRECT) {
+            ta.store(sA[buf]);
+            tb.store(sB[buf]);
         }
-#pragma unroll
-        for (int j = 0; j < JB; ++j) {
-            const int c = wave + j * NW;
-            const int f = c * 256 + lane * 4;              // float offset in the B tile
-            b_src[j] = B + static_cast<int64_t>(f / BN) * ldb + n0 + f % BN;
-            b_dst[j] = c * 256;
-        }
-    }
-    // (address-space casts: global source, LDS destination)
-    typedef const __attribute__((address_space(1))) void *gptr_t;
-    typedef __attribute__((address_space(3))) void *lptr_t;
-    auto load_direct = [&](int k0, int buf) {
-#pragma unroll
-        for (int j = 0; j < JA; ++j)
-            __builtin_amdgcn_global_load_lds((gptr_t)(a_src[j] + k0), (lptr_t)(&sA[buf][a_dst[j]]),
-                                             16, 0, 0);
-#pragma unroll
-        for (int j = 0; j < JB; ++j)
-            __builtin_amdgcn_global_load_lds((gptr_t)(b_src[j] + static_cast<int64_t>(k0) * ldb),
-                                             (lptr_t)(&sB[buf][b_dst[j]]), 16, 0, 0);
     };
 
     const int half = lane >> 5;
     const int l32 = lane & 31;
-    // rows read by this lane are wm * WTM + i * 32 + l32, all congruent to
-    // l32 modulo 32: one swizzle term serves every row block
-    const int a_lds = (wm * WTM + l32) * LDA_S + (SWZ ? 0 : 4 * half);
-    const int g_lane = swz(l32);
-    const int b_lds = (4 * half) * LDB_S + wn * WTN + l32;
 
     // Two fragment register sets: operands of one chunk of 8 k.
-    float4 fa[2][FM];
+    float fa[2][FM][4];
     float fb[2][FN][4];
     auto read_frag = [&](int set, int buf, int kc) {
-        const float *pa = &sA[buf][a_lds + (SWZ ? ((2 * kc + half) ^ g_lane) * 4 : kc * 8)];
-        const float *pb = &sB[buf][b_lds + kc * 8 * LDB_S];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[set][i] = *reinterpret_cast<const float4 *>(pa + i * 32 * LDA_S);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) fb[set][j][s] = pb[s * LDB_S + j * 32];
+        ta.template read<FM>(sA[buf], kc, wm * WTM, half, l32, fa[set]);
+        tb.template read<FN>(sB[buf], kc, wn * WTN, half, l32, fb[set]);
     };
 
     floatx16 acc[FM][FN];
@@ -409,23 +457,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const float4 av = fa[set][i];
-                    const float a = s == 0 ? av.x : s == 1 ? av.y : s == 2 ? av.z : av.w;
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, fb[set][j][s], acc[i][j], 0, 0, 0);
-                }
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[set][i][s], fb[set][j][s],
+                                                                     acc[i][j], 0, 0, 0);
     };
 
     const int nk = (K + BK - 1) / BK;
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st) {
         if (st < nk) {
-            if constexpr (DIRECT) {
-                load_direct(st * BK, st);
-            } else {
-                load_global(st * BK);
-                store_lds(st);
-            }
+            load_step(st * BK, st);
+            store_step(st);
         }
     }
     __syncthreads();
@@ -435,10 +477,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
     for (int t = 0; t < nk; ++t) {
         const int nxt = cur == STAGES - 1 ? 0 : cur + 1;
         const int ahead = cur == 0 ? STAGES - 1 : cur - 1;  // (t + STAGES - 1) mod STAGES
-        if (t + STAGES - 1 < nk) {
-            if constexpr (DIRECT) load_direct((t + STAGES - 1) * BK, ahead);
-            else load_global((t + STAGES - 1) * BK);
-        }
+        if (t + STAGES - 1 < nk) load_step((t + STAGES - 1) * BK, ahead);
         // Branch-free so that the reads stay ahead of the MFMAs they feed
         // (a branch here lets the compiler sink them back to their use).
         //
@@ -458,7 +497,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
             const int set = kc & 1;
             if constexpr (STAGES == 2) {
                 if (kc == KC - 1) {
-                    if constexpr (!DIRECT) store_lds(nxt);  // stale but in-bounds in the last step
+                    store_step(nxt);  // register staging: stale but in-bounds in the last step
                     // keep all of the previous chunk's MFMAs ahead of the
                     // barrier: they cover the latency of the reads it waits for
                     __builtin_amdgcn_sched_barrier(0);
@@ -486,13 +525,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk - kPairs, 0);
         }
         if constexpr (STAGES == 3) {
-            if constexpr (!DIRECT)
-                if (t + 2 < nk) store_lds(ahead);
+            if (t + 2 < nk) store_step(ahead);
             if (t + 1 < nk) __syncthreads();
         }
         cur = nxt;
     }
 
+    // accumulator register r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4,
+    // column l % 32 of its block
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -511,23 +551,39 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
 // PIPE = 0: the first kernel; PIPE = 2 or 3: the pipelined kernel with that
 // many LDS buffers.  DIRECT: direct global -> LDS loads where the shape
 // allows (full tiles, 16-byte-aligned rows), register staging otherwise.
+// TRANS: also compiled for transposed operands (pipelined kernel only).
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int GROUP_M, int PIPE,
-          bool DIRECT = false>
+          bool DIRECT = false, bool TRANS = false>
 hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
+    static_assert(!TRANS || PIPE > 0, "transposed operands need the pipelined kernel");
     constexpr int NT = 64 * WM * WN;
+    if ((p.ta || p.tb) && !TRANS) return hipErrorNotSupported;
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
     const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * p.batch;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool vec = rows_aligned16(p.A, p.lda, p.sa) && rows_aligned16(p.B, p.ldb, p.sb);
     const bool guard = (p.M % BM) || (p.N % BN) || (p.K % BK);
     const dim3 g(static_cast<unsigned>(grid)), b(NT);
+#define GEMM_RING(D, G, V, TA, TB)                                                              \
+    hipLaunchKernelGGL(                                                                         \
+        (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, D, G, V, TA, TB>), g, b, 0, \
+        stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, GROUP_M,   \
+        batch_of(p))
+#define GEMM_RING_T(D, G, V)                                                                    \
+    do {                                                                                        \
+        if constexpr (TRANS) {                                                                  \
+            if (p.ta && p.tb) GEMM_RING(D, G, V, true, true);                                   \
+            else if (p.ta) GEMM_RING(D, G, V, true, false);                                     \
+            else if (p.tb) GEMM_RING(D, G, V, false, true);                                     \
+            else GEMM_RING(D, G, V, false, false);                                              \
+        } else {                                                                                \
+            GEMM_RING(D, G, V, false, false);                                                   \
+        }                                                                                       \
+    } while (0)
 #define GEMM_MFMA_LAUNCH(D, G, V)                                                               \
     do {                                                                                        \
         if constexpr (PIPE > 0)                                                                 \
-            hipLaunchKernelGGL(                                                                 \
-                (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, D, G, V>), g, b, 0, \
-                stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,   \
-                GROUP_M, batch_of(p));                                                          \
+            GEMM_RING_T(D, G, V);                                                               \
         else                                                                                    \
             hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WM, WN, PADA, PADB, G, V>), g, b, 0, \
                                stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,       \
@@ -541,42 +597,44 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
         else GEMM_MFMA_LAUNCH(false, false, false);
     }
 #undef GEMM_MFMA_LAUNCH
+#undef GEMM_RING_T
+#undef GEMM_RING
     return hipGetLastError();
 }
 
 const ConfigEntry kMfmaConfigs[] = {
     // First kernel: two LDS buffers, one barrier per K-step, padded A rows
     // (pa0 = unpadded, for the bank-conflict counters).
-    {"mfma_128x128x16_w2x2_pa4_pb0", launch_mfma<128, 128, 16, 2, 2, 4, 0, 8, 0>},
-    {"mfma_128x128x16_w2x2_pa0_pb0", launch_mfma<128, 128, 16, 2, 2, 0, 0, 8, 0>},
-    {"mfma_256x256x16_w2x4_pa4_pb0", launch_mfma<256, 256, 16, 2, 4, 4, 0, 8, 0>},
-    {"mfma_256x256x32_w2x4_pa4_pb0", launch_mfma<256, 256, 32, 2, 4, 4, 0, 8, 0>},
-    {"mfma_256x256x16_w4x4_pa4_pb0", launch_mfma<256, 256, 16, 4, 4, 4, 0, 8, 0>},
-    {"mfma_64x64x16_w2x2_pa4_pb0", launch_mfma<64, 64, 16, 2, 2, 4, 0, 8, 0>},
-    {"mfma_64x64x32_w2x2_pa4_pb0", launch_mfma<64, 64, 32, 2, 2, 4, 0, 8, 0>},
+    {"mfma_128x128x16_w2x2_pa4_pb0", launch_mfma<128, 128, 16, 2, 2, 4, 0, 8, 0>, 0},
+    {"mfma_128x128x16_w2x2_pa0_pb0", launch_mfma<128, 128, 16, 2, 2, 0, 0, 8, 0>, 0},
+    {"mfma_256x256x16_w2x4_pa4_pb0", launch_mfma<256, 256, 16, 2, 4, 4, 0, 8, 0>, 0},
+    {"mfma_256x256x32_w2x4_pa4_pb0", launch_mfma<256, 256, 32, 2, 4, 4, 0, 8, 0>, 0},
+    {"mfma_256x256x16_w4x4_pa4_pb0", launch_mfma<256, 256, 16, 4, 4, 4, 0, 8, 0>, 0},
+    {"mfma_64x64x16_w2x2_pa4_pb0", launch_mfma<64, 64, 16, 2, 2, 4, 0, 8, 0>, 0},
+    {"mfma_64x64x32_w2x2_pa4_pb0", launch_mfma<64, 64, 32, 2, 2, 4, 0, 8, 0>, 0},
     // Pipelined kernel, register staging: mfma3 = three LDS buffers, mfma2p =
     // two buffers with the barrier before the last chunk; A rows padded (pa4)
     // or XOR-swizzled (swz); pb8 pads B rows.
-    {"mfma3_256x256x16_w4x4_pa4_pb0", launch_mfma<256, 256, 16, 4, 4, 4, 0, 8, 3>},
-    {"mfma3_256x256x16_w4x4_swz_pb0", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3>},
-    {"mfma3_256x256x16_w4x4_swz_pb8", launch_mfma<256, 256, 16, 4, 4, -1, 8, 8, 3>},
-    {"mfma2p_256x256x32_w4x4_swz_pb0", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2>},
-    {"mfma3_128x128x16_w2x2_swz_pb0", launch_mfma<128, 128, 16, 2, 2, -1, 0, 8, 3>},
-    {"mfma3_64x64x16_w2x2_swz_pb0", launch_mfma<64, 64, 16, 2, 2, -1, 0, 8, 3>},
+    {"mfma3_256x256x16_w4x4_pa4_pb0", launch_mfma<256, 256, 16, 4, 4, 4, 0, 8, 3>, 0},
+    {"mfma3_256x256x16_w4x4_swz_pb0", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3>, 0},
+    {"mfma3_256x256x16_w4x4_swz_pb8", launch_mfma<256, 256, 16, 4, 4, -1, 8, 8, 3>, 0},
+    {"mfma2p_256x256x32_w4x4_swz_pb0", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2, false, true>, kCapTransposed},
+    {"mfma3_128x128x16_w2x2_swz_pb0", launch_mfma<128, 128, 16, 2, 2, -1, 0, 8, 3, false, true>, kCapTransposed},
+    {"mfma3_64x64x16_w2x2_swz_pb0", launch_mfma<64, 64, 16, 2, 2, -1, 0, 8, 3, false, true>, kCapTransposed},
     // Pipelined kernel, direct global -> LDS loads on full tiles (register
     // staging on edge tiles): mfma3d = three buffers, mfma2d = two buffers;
     // 256x128 / 128x256 tiles fit two workgroups per CU at BK = 16; g4 / g16
     // change the column-strip height of the tile order.
-    {"mfma3d_256x256x16_w4x4_swz", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3, true>},
-    {"mfma3d_256x256x16_w2x4_swz", launch_mfma<256, 256, 16, 2, 4, -1, 0, 8, 3, true>},
-    {"mfma3d_256x128x16_w4x2_swz", launch_mfma<256, 128, 16, 4, 2, -1, 0, 8, 3, true>},
-    {"mfma3d_128x256x16_w2x4_swz", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3, true>},
-    {"mfma2d_256x256x32_w4x4_swz", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2, true>},
-    {"mfma2d_256x256x32_w4x4_swz_g4", launch_mfma<256, 256, 32, 4, 4, -1, 0, 4, 2, true>},
-    {"mfma2d_256x256x32_w4x4_swz_g16", launch_mfma<256, 256, 32, 4, 4, -1, 0, 16, 2, true>},
-    {"mfma2d_256x256x32_w2x4_swz", launch_mfma<256, 256, 32, 2, 4, -1, 0, 8, 2, true>},
-    {"mfma3d_256x128x32_w4x2_swz", launch_mfma<256, 128, 32, 4, 2, -1, 0, 8, 3, true>},
-    {"mfma3d_128x256x32_w2x4_swz", launch_mfma<128, 256, 32, 2, 4, -1, 0, 8, 3, true>},
+    {"mfma3d_256x256x16_w4x4_swz", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3, true>, 0},
+    {"mfma3d_256x256x16_w2x4_swz", launch_mfma<256, 256, 16, 2, 4, -1, 0, 8, 3, true>, 0},
+    {"mfma3d_256x128x16_w4x2_swz", launch_mfma<256, 128, 16, 4, 2, -1, 0, 8, 3, true>, 0},
+    {"mfma3d_128x256x16_w2x4_swz", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3, true, true>, kCapTransposed},
+    {"mfma2d_256x256x32_w4x4_swz", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2, true, true>, kCapTransposed},
+    {"mfma2d_256x256x32_w4x4_swz_g4", launch_mfma<256, 256, 32, 4, 4, -1, 0, 4, 2, true>, 0},
+    {"mfma2d_256x256x32_w4x4_swz_g16", launch_mfma<256, 256, 32, 4, 4, -1, 0, 16, 2, true>, 0},
+    {"mfma2d_256x256x32_w2x4_swz", launch_mfma<256, 256, 32, 2, 4, -1, 0, 8, 2, true>, 0},
+    {"mfma3d_256x128x32_w4x2_swz", launch_mfma<256, 128, 32, 4, 2, -1, 0, 8, 3, true, true>, kCapTransposed},
+    {"mfma3d_128x256x32_w2x4_swz", launch_mfma<128, 256, 32, 2, 4, -1, 0, 8, 3, true>, 0},
 };
 
 }  // namespace

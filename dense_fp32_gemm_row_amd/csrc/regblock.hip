@@ -178,6 +178,7 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void gemm_regblock_kernel(
 
 template <int BM, int BN, int BK, int TM, int TN, int PAD>
 hipError_t launch_regblock(const Problem &p, hipStream_t stream) {
+    if (p.ta || p.tb) return hipErrorNotSupported;
     constexpr int NT = (BM / TM) * (BN / TN);
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
     const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * p.batch;
@@ -198,11 +199,11 @@ hipError_t launch_regblock(const Problem &p, hipStream_t stream) {
 }
 
 const ConfigEntry kRegblockConfigs[] = {
-    {"regblock_128x128x8_t8x8_pad4", launch_regblock<128, 128, 8, 8, 8, 4>},
-    {"regblock_64x64x16_t4x4_pad4", launch_regblock<64, 64, 16, 4, 4, 4>},
-    {"regblock_128x128x8_t8x8_pad0", launch_regblock<128, 128, 8, 8, 8, 0>},
-    {"regblock_128x128x16_t8x8_pad4", launch_regblock<128, 128, 16, 8, 8, 4>},
-    {"regblock_128x64x16_t8x4_pad4", launch_regblock<128, 64, 16, 8, 4, 4>},
+    {"regblock_128x128x8_t8x8_pad4", launch_regblock<128, 128, 8, 8, 8, 4>, 0},
+    {"regblock_64x64x16_t4x4_pad4", launch_regblock<64, 64, 16, 4, 4, 4>, 0},
+    {"regblock_128x128x8_t8x8_pad0", launch_regblock<128, 128, 8, 8, 8, 0>, 0},
+    {"regblock_128x128x16_t8x8_pad4", launch_regblock<128, 128, 16, 8, 8, 4>, 0},
+    {"regblock_128x64x16_t8x4_pad4", launch_regblock<128, 64, 16, 8, 4, 4>, 0},
 };
 
 }  // namespace

@@ -45,6 +45,10 @@ def render(table: dict) -> str:
         f'constexpr const char *kDefaultLarge = "{table["default_large"]}";',
         f'constexpr const char *kDefaultMedium = "{table["default_medium"]}";',
         f'constexpr const char *kDefaultSmall = "{table["default_small"]}";',
+        "// configurations for transposed operands (they must accept them)",
+        f'constexpr const char *kTransposedLarge = "{table["transposed_large"]}";',
+        f'constexpr const char *kTransposedMedium = "{table["transposed_medium"]}";',
+        f'constexpr const char *kTransposedSmall = "{table["transposed_small"]}";',
         "}  // namespace gemm_f32_impl",
         "",
     ]

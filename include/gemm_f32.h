@@ -53,6 +53,10 @@ extern "C" {
 #define GEMM_F32_EHIP (-2)      /* a HIP runtime call or launch failed */
 #define GEMM_F32_ENOKERNEL (-3) /* no such variant or tile configuration */
 
+/* Operand forms for gemm_f32_ex. */
+#define GEMM_F32_OP_N 0 /* as stored */
+#define GEMM_F32_OP_T 1 /* transposed */
+
 /* Kernel variants, in the order the pages build them up. */
 #define GEMM_F32_VARIANT_NAIVE 0    /* one thread per output cell */
 #define GEMM_F32_VARIANT_LDS 1      /* LDS (shared-memory) tiles, 2 barriers */
@@ -143,6 +147,44 @@ int gemm_f32_strided_batched_variant(int variant, int config_id,
                                      const float *B, int64_t ldb, int64_t strideB,
                                      float *C, int64_t ldc, int64_t strideC,
                                      void *stream);
+
+/*
+ * gemm_f32_ex -- the general form: transposed operands, a batch, and an
+ * optional explicit kernel.
+ *
+ *   C_b = op(A_b) x op(B_b),  0 <= b < batch,
+ *
+ *   op(A) = A (opA = GEMM_F32_OP_N; A stored M x K, lda >= max(1, K)) or A^T
+ *           (GEMM_F32_OP_T; A stored K x M row-major, lda >= max(1, M), so
+ *           op(A)[i][k] = A[k * lda + i]);
+ *   op(B) = B (opB = GEMM_F32_OP_N; B stored K x N, ldb >= max(1, N)) or B^T
+ *           (GEMM_F32_OP_T; B stored N x K, ldb >= max(1, K), so
+ *           op(B)[k][j] = B[j * ldb + k]).
+ *
+ * Row-major flat indexing is the pages' layout ("Tiled Matrix
+ * Multiplication in CUDA", section 2); the page names column-major storage
+ * as the other order, and a column-major M x K matrix with leading
+ * dimension ld is exactly the row-major K x M matrix that GEMM_F32_OP_T
+ * describes.  Column-major C = A x B can also be had without transposes as
+ * the row-major product C^T = B^T x A^T, i.e. gemm_f32 with the operands
+ * swapped.
+ *
+ *   variant, config_id   -1, -1 for the library's choice, else as in
+ *                        gemm_f32_variant.  Transposed operands are taken by
+ *                        the naive kernel and by the pipelined MFMA
+ *                        configurations that list them; others return
+ *                        GEMM_F32_ENOKERNEL.
+ *   batch, strides       as in gemm_f32_strided_batched (batch 1, strides 0
+ *                        for one product).
+ *
+ * Returns as gemm_f32; GEMM_F32_EINVAL for an unknown opA or opB.
+ */
+int gemm_f32_ex(int variant, int config_id, int opA, int opB,
+                int64_t batch, int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda, int64_t strideA,
+                const float *B, int64_t ldb, int64_t strideB,
+                float *C, int64_t ldc, int64_t strideC,
+                void *stream);
 
 /* Static description of a return code; never NULL. */
 const char *gemm_f32_strerror(int code);

@@ -188,3 +188,29 @@ def test_empty_batches_enqueue_nothing(lib):
     assert b.gemm_f32_strided_batched(5, 0, 4, 4, 0, 4, 16, 0, 4, 16, 0, 4, 16, None) == 0
     # a single product ignores strideC's lower bound
     assert b.gemm_f32_strided_batched(0, 4, 4, 4, 0, 4, 0, 0, 4, 0, 0, 4, 0, None) == 0
+
+
+def test_gemm_ex_validation(lib):
+    args = (1, 4, 6, 5, 0x1000, 5, 0, 0x2000, 6, 0, 0x3000, 6, 0, None)
+    # unknown operand forms
+    assert b.gemm_f32_ex(-1, -1, 2, 0, *args) == b.GEMM_F32_EINVAL
+    assert b.gemm_f32_ex(-1, -1, 0, -1, *args) == b.GEMM_F32_EINVAL
+    assert "opA/opB" in b.gemm_f32_last_error()
+    # unknown variant
+    assert b.gemm_f32_ex(-2, 0, 0, 0, *args) == b.GEMM_F32_ENOKERNEL
+    assert b.gemm_f32_ex(7, 0, 0, 0, *args) == b.GEMM_F32_ENOKERNEL
+    # transposed A is stored K x M: its rows hold M floats (M = 4 here)
+    bad = (1, 4, 6, 5, 0x1000, 3, 0, 0x2000, 6, 0, 0x3000, 6, 0, None)
+    assert b.gemm_f32_ex(-1, -1, b.OP_T, b.OP_N, *bad) == b.GEMM_F32_EINVAL
+    assert "lda=3 < max(1, M=4)" in b.gemm_f32_last_error()
+    # transposed B is stored N x K: its rows hold K floats (K = 5)
+    bad = (1, 4, 6, 5, 0x1000, 5, 0, 0x2000, 4, 0, 0x3000, 6, 0, None)
+    assert b.gemm_f32_ex(-1, -1, b.OP_N, b.OP_T, *bad) == b.GEMM_F32_EINVAL
+    assert "ldb=4 < max(1, K=5)" in b.gemm_f32_last_error()
+    # overlap is checked on the stored (transposed) extents: A^T stored 5 x 4
+    # at 0x1000 spans 80 bytes
+    ov = (1, 4, 6, 5, 0x1000, 4, 0, 0x2000, 6, 0, 0x1000 + 76, 6, 0, None)
+    assert b.gemm_f32_ex(-1, -1, b.OP_T, b.OP_N, *ov) == b.GEMM_F32_EINVAL
+    assert "overlaps A" in b.gemm_f32_last_error()
+    # empty products succeed without touching the device
+    assert b.gemm_f32_ex(-1, -1, b.OP_T, b.OP_T, 1, 0, 6, 5, 0, 1, 0, 0, 5, 0, 0, 6, 0, None) == 0

@@ -346,6 +346,74 @@ def test_strided_batched_full_tiles(kernel):
 
 
 # --------------------------------------------------------------------------
+# transposed operands
+# --------------------------------------------------------------------------
+
+TRANS_CAPABLE = ["mfma2d_256x256x32_w4x4_swz", "mfma3d_256x128x32_w4x2_swz",
+                 "mfma3d_128x256x16_w2x4_swz", "mfma3_64x64x16_w2x2_swz_pb0",
+                 "mfma3_128x128x16_w2x2_swz_pb0", "mfma2p_256x256x32_w4x4_swz_pb0"]
+TRANS_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4")] + [
+    (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in TRANS_CAPABLE]
+OPS = ["NN", "NT", "TN", "TT"]
+
+
+def _stored(X: np.ndarray, op: str):
+    """Device operand for op(X) = X: the tensor itself, or a transposed view
+    of its transpose stored row-major."""
+    if op == "N":
+        return to_dev(X)
+    return to_dev(np.ascontiguousarray(X.T)).T
+
+
+@pytest.mark.parametrize("kernel", TRANS_KERNELS, ids=[k[2] for k in TRANS_KERNELS])
+@pytest.mark.parametrize("ops", OPS)
+@pytest.mark.parametrize("shape", [(300, 277, 129), (512, 512, 96)], ids=["ragged", "full"])
+def test_transposed_operands(kernel, ops, shape):
+    import torch
+
+    M, N, K = shape
+    log(f"{ops} {shape} on {kernel[2]}")
+    v, c, name = kernel
+    A, B = make_inputs(M, N, K, "int4", seed=31)
+    out = torch.empty((M, N), device="cuda:0")
+    b.gemm(_stored(A, ops[0]), _stored(B, ops[1]), out, variant=v, config=c)
+    assert_exact(to_host(out), oracle.gemm(A, B), f"{name} {ops} int4")
+    A, B = make_inputs(M, N, K, "uniform", seed=32)
+    b.gemm(_stored(A, ops[0]), _stored(B, ops[1]), out, variant=v, config=c)
+    _, ref64 = oracle.gemm(A, B, return_f64=True)
+    assert_close(to_host(out), ref64, K, f"{name} {ops} uniform")
+
+
+@pytest.mark.parametrize("ops", ["NT", "TN", "TT"])
+def test_transposed_batched(ops):
+    import torch
+
+    log(f"batched {ops}")
+    nb, M, N, K = 3, 256, 192, 80
+    A, B = make_inputs(M * nb, N * nb, K, "int4", seed=33)
+    A3 = A.reshape(nb, M, K)
+    B3 = np.stack([B[:, i * N:(i + 1) * N] for i in range(nb)])
+    dA = to_dev(A3) if ops[0] == "N" else to_dev(np.ascontiguousarray(A3.transpose(0, 2, 1))).transpose(1, 2)
+    dB = to_dev(B3) if ops[1] == "N" else to_dev(np.ascontiguousarray(B3.transpose(0, 2, 1))).transpose(1, 2)
+    out = torch.empty((nb, M, N), device="cuda:0")
+    b.gemm_batched(dA, dB, out)
+    got = to_host(out)
+    for i in range(nb):
+        assert_exact(got[i], oracle.gemm(A3[i], B3[i]), f"batched {ops} product {i}")
+
+
+def test_transposed_rejected_where_unsupported():
+    import torch
+
+    A = torch.ones((64, 64), device="cuda:0")
+    for v, c, name in ALL_CONFIGS:
+        if v in (1, 2) or (v == 3 and name not in TRANS_CAPABLE):
+            with pytest.raises(b.GemmError) as e:
+                b.gemm(A.T, A, variant=v, config=c)
+            assert e.value.code == b.GEMM_F32_ENOKERNEL, name
+
+
+# --------------------------------------------------------------------------
 # full-size workloads in the benchmark's launch configuration
 # --------------------------------------------------------------------------
 
