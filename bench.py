@@ -150,6 +150,9 @@ def main() -> int:
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--ops", default="NN", choices=["NN", "NT", "TN", "TT"],
                     help="store A and/or B transposed (the product is the same)")
+    ap.add_argument("--splitk", type=int, default=None, metavar="S",
+                    help="time gemm_f32_splitk with S splits (partial products + reduction); "
+                         "0 = the library's choice of splits")
     ap.add_argument("--stages", action="store_true")
     ap.add_argument("--stage-variants", default="naive,lds,regblock,mfma",
                     help="variants that --stages times")
@@ -171,6 +174,9 @@ def main() -> int:
 
     if args.ops != "NN" and (args.stages or args.variant is not None):
         print("--ops applies to the library's own choice only", file=sys.stderr)
+        return 2
+    if args.splitk is not None and (args.ops != "NN" or args.stages):
+        print("--splitk takes row-major operands and no --stages", file=sys.stderr)
         return 2
 
     if not torch.cuda.is_available():
@@ -215,7 +221,18 @@ def main() -> int:
              else f"library choice ({'batched ' if nb > 1 else ''}{args.ops})")
     log(f"kernel {cname}")
 
-    if args.variant is None:
+    if args.splitk is not None:
+        if nb > 1:
+            print("--splitk takes a single product", file=sys.stderr)
+            return 2
+        need = binding.gemm_f32_splitk_workspace_size(M, N, K, args.splitk)
+        work = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+        sv, sc = (None, -1) if args.variant is None else (v, c)
+        fn = lambda: binding.gemm_splitk(dA, dB, args.splitk, dC, work,  # noqa: E731
+                                         variant=sv, config=sc)
+        splits = args.splitk or "library choice"
+        cname = f"{cname if args.variant is not None else 'library choice'} split-K {splits}"
+    elif args.variant is None:
         fn = lambda: call(dA, dB, dC)  # noqa: E731  (gemm_f32 / gemm_f32_strided_batched)
     else:
         fn = lambda: call(dA, dB, dC, variant=v, config=c)  # noqa: E731
@@ -243,7 +260,7 @@ def main() -> int:
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_FP32_MATRIX_TFLOPS, 2),
         "config": {"workload": w.name, "batch": nb, "M": M, "N": N, "K": K, "dist": w.dist,
-                   "seed": w.seed, "ops": args.ops,
+                   "seed": w.seed, "ops": args.ops, "splitk": args.splitk,
                    "layout": "row-major C; A, B row-major, stored transposed where ops says T",
                    "kernel": cname, "parallelism": "none"},
         "roofline": {

@@ -76,6 +76,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gemm_f32_ex.restype = _int
     lib.gemm_f32_ex.argtypes = [_int, _int, _int, _int, _i64, _i64, _i64, _i64, _vp, _i64, _i64,
                                 _vp, _i64, _i64, _vp, _i64, _i64, _vp]
+    lib.gemm_f32_splitk.restype = _int
+    lib.gemm_f32_splitk.argtypes = [_int, _int, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
+                                    _i64, _vp, _i64, _vp]
+    lib.gemm_f32_splitk_workspace_size.restype = _i64
+    lib.gemm_f32_splitk_workspace_size.argtypes = [_i64, _i64, _i64, _i64]
     lib.gemm_f32_strerror.restype = ctypes.c_char_p
     lib.gemm_f32_strerror.argtypes = [_int]
     lib.gemm_f32_last_error.restype = ctypes.c_char_p
@@ -119,6 +124,16 @@ def gemm_f32_ex(variant, config_id, opA, opB, batch, M, N, K, A, lda, sA, B, ldb
                 sC, stream=None) -> int:
     return load().gemm_f32_ex(variant, config_id, opA, opB, batch, M, N, K, A, lda, sA, B, ldb,
                               sB, C, ldc, sC, stream)
+
+
+def gemm_f32_splitk(variant, config_id, splits, M, N, K, A, lda, B, ldb, C, ldc, workspace,
+                    workspace_bytes, stream=None) -> int:
+    return load().gemm_f32_splitk(variant, config_id, splits, M, N, K, A, lda, B, ldb, C, ldc,
+                                  workspace, workspace_bytes, stream)
+
+
+def gemm_f32_splitk_workspace_size(M, N, K, splits) -> int:
+    return load().gemm_f32_splitk_workspace_size(M, N, K, splits)
 
 
 def gemm_f32_strerror(code: int) -> str:
@@ -235,6 +250,42 @@ def gemm(A, B, out=None, *, variant: int | str | None = None, config: int | str 
     torch's current stream; returns ``out`` without synchronising.
     """
     return _call(A, B, out, variant, config, stream, batched=False)
+
+
+def gemm_splitk(A, B, splits: int, out=None, workspace=None, *, variant: int | str | None = None,
+                config: int | str = -1, stream=None):
+    """``out = A @ B`` as `splits` partial products over K plus a fixed-order
+    reduction (gemm_f32_splitk).  ``workspace`` is a float32 GPU tensor of at
+    least gemm_f32_splitk_workspace_size bytes; allocated here when None."""
+    import torch
+
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"shape mismatch {tuple(A.shape)} x {tuple(B.shape)}")
+    opa, lda, _ = _operand(A, "A", 2)
+    opb, ldb, _ = _operand(B, "B", 2)
+    if opa != OP_N or opb != OP_N:
+        raise ValueError("gemm_splitk takes row-major operands")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    opc, ldc, _ = _operand(out, "out", 2)
+    need = gemm_f32_splitk_workspace_size(M, N, K, splits)
+    if workspace is None and need:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=A.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * 4 if workspace is not None else 0
+    sp = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
+    if variant is None:
+        v, c = -1, -1
+    else:
+        v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+        c = config_id(v, config) if isinstance(config, str) else int(config)
+    rc = gemm_f32_splitk(v, c, splits, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                         out.data_ptr(), ldc, wptr, wbytes, sp)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, gemm_f32_last_error())
+    return out
 
 
 def gemm_batched(A, B, out=None, *, variant: int | str | None = None, config: int | str = -1,

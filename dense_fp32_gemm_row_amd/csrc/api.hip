@@ -10,6 +10,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <algorithm>
+
 #include "../../include/gemm_f32.h"
 #include "gemm_internal.h"
 #include "tune_table.inc"
@@ -40,6 +42,57 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float *__restrict__ C, i
         const int64_t i = r / N, j = r - i * N;
         C[b * sc + i * ldc + j] = 0.0f;
     }
+}
+
+// Split-K reduction: C = W_0 + W_1 + ... + W_{S-1}, summed in that order for
+// every element, so the result does not depend on scheduling.  W_s is a
+// packed M x N slice (leading dimension N) `slice` floats after W_{s-1}.
+template <bool VEC4>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ W,
+                                                            int64_t slice, int S, int M, int N,
+                                                            float *__restrict__ C, int64_t ldc) {
+    constexpr int V = VEC4 ? 4 : 1;
+    const int64_t per_row = N / V;
+    const int64_t total = static_cast<int64_t>(M) * per_row;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t i = e / per_row, j = (e - i * per_row) * V;
+        const float *w = W + i * N + j;
+        if constexpr (VEC4) {
+            float4 acc = *reinterpret_cast<const float4 *>(w);
+            for (int s = 1; s < S; ++s) {
+                const float4 v = *reinterpret_cast<const float4 *>(w + s * slice);
+                acc.x += v.x, acc.y += v.y, acc.z += v.z, acc.w += v.w;
+            }
+            *reinterpret_cast<float4 *>(C + i * ldc + j) = acc;
+        } else {
+            float acc = w[0];
+            for (int s = 1; s < S; ++s) acc += w[s * slice];
+            C[i * ldc + j] = acc;
+        }
+    }
+}
+
+// Split geometry: `want` splits of K rounded to whole multiples of 32 (so
+// every kernel's K step divides a split); returns the split length and sets
+// the number of splits actually used.
+int split_len(int64_t K, int64_t want, int64_t *used) {
+    int64_t len = (K + want - 1) / want;
+    len = ((len + 31) / 32) * 32;
+    if (len < 32) len = 32;
+    *used = (K + len - 1) / len;
+    return static_cast<int>(len);
+}
+
+// Library choice of the number of K splits: enough 256 x 256 tiles to give
+// every CU one, with at least 1024 k per split.
+int64_t auto_splits(int64_t M, int64_t N, int64_t K) {
+    constexpr int64_t kCUs = 256;
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    int64_t s = (kCUs + tiles - 1) / tiles;
+    const int64_t by_k = K / 1024;
+    if (s > by_k) s = by_k;
+    return s < 1 ? 1 : s;
 }
 
 const ConfigEntry *configs_of(int variant, int *count) {
@@ -165,13 +218,13 @@ void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant,
             }
         }
     }
-    // Rules: fewer, larger tiles once the grid fills the chip several times
-    // over; small tiles for small or ragged problems.  A batch multiplies the
-    // number of tiles.
+    // Rules: 256 x 256 tiles once they give every CU of the chip one; 128-row
+    // tiles while 128 x 128 tiles still do; small tiles for small or ragged
+    // problems.  A batch multiplies the number of tiles.
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256) * batch;
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128) * batch;
     const char *name = trans ? kTransposedSmall : kDefaultSmall;
-    if (t256 >= 512) name = trans ? kTransposedLarge : kDefaultLarge;
+    if (t256 >= 256) name = trans ? kTransposedLarge : kDefaultLarge;
     else if (t128 >= 256) name = trans ? kTransposedMedium : kDefaultMedium;
     *variant = GEMM_F32_VARIANT_MFMA;
     *config = find_config(GEMM_F32_VARIANT_MFMA, name);
@@ -273,6 +326,85 @@ int gemm_f32_strided_batched_variant(int variant, int config_id, int64_t batch, 
     if (variant < 0) return (clear_error(), fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant));
     return run(variant, config_id, false, false, batch, M, N, K, A, lda, strideA, B, ldb, strideB,
                C, ldc, strideC, stream);
+}
+
+int64_t gemm_f32_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int64_t splits) {
+    if (M <= 0 || N <= 0 || K <= 0 || splits < 0 || M > 0x7fffffff || N > 0x7fffffff ||
+        K > 0x7fffffff || splits > 0xffff)
+        return 0;
+    if (splits == 0) splits = auto_splits(M, N, K);
+    if (splits <= 1) return 0;
+    int64_t used = 0;
+    split_len(K, splits, &used);
+    return used > 1 ? used * M * N * static_cast<int64_t>(sizeof(float)) : 0;
+}
+
+int gemm_f32_splitk(int variant, int config_id, int64_t splits, int64_t M, int64_t N, int64_t K,
+                    const float *A, int64_t lda, const float *B, int64_t ldb, float *C,
+                    int64_t ldc, void *workspace, int64_t workspace_bytes, void *stream) {
+    clear_error();
+    if (splits < 0 || splits > 0xffff)
+        return fail(GEMM_F32_EINVAL, "splits=%lld outside [0, 65535]", (long long)splits);
+    if (splits == 0 && M > 0 && N > 0 && K > 0 && M <= 0x7fffffff && N <= 0x7fffffff &&
+        K <= 0x7fffffff)
+        splits = auto_splits(M, N, K);
+    if (splits == 0) splits = 1;
+    if (variant < -1) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant);
+    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
+    if (rc != GEMM_F32_OK) return rc;
+    int64_t used = 1;
+    const int len = K > 0 ? split_len(K, splits, &used) : 0;
+    if (used <= 1 || M == 0 || N == 0)  // one split: the plain product, no workspace
+        return run(variant, variant == -1 ? -1 : config_id, false, false, 1, M, N, K, A, lda, 0, B,
+                   ldb, 0, C, ldc, 0, stream);
+    rc = validate(false, false, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0);
+    if (rc != GEMM_F32_OK) return rc;
+    const int64_t need = used * M * N * static_cast<int64_t>(sizeof(float));
+    float *W = static_cast<float *>(workspace);
+    if (W == nullptr || workspace_bytes < need)
+        return fail(GEMM_F32_EINVAL, "workspace of %lld bytes needed, %lld given", (long long)need,
+                    (long long)(W ? workspace_bytes : 0));
+    if (reinterpret_cast<uintptr_t>(W) % 4) return fail(GEMM_F32_EINVAL, "workspace not 4-byte aligned");
+    const Span sw = {reinterpret_cast<uintptr_t>(W), reinterpret_cast<uintptr_t>(W) + need};
+    if (overlaps(sw, span_of(A, M, K, lda)) || overlaps(sw, span_of(B, K, N, ldb)) ||
+        overlaps(sw, span_of(C, M, N, ldc)))
+        return fail(GEMM_F32_EINVAL, "workspace overlaps A, B or C");
+    // partial products: a strided batch over the K splits into the workspace
+    int v = variant, c = config_id;
+    if (v == -1) select_config(used, M, N, len, &v, &c);
+    int count = 0;
+    const ConfigEntry *cfgs = configs_of(v, &count);
+    if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", v);
+    if (c == -1) {
+        int vv = 0;
+        select_config(used, M, N, len, &vv, &c);
+        if (vv != v) c = 0;
+    }
+    if (c < 0 || c >= count)
+        return fail(GEMM_F32_ENOKERNEL, "variant %d has no configuration %d", v, c);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Problem p{static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), A, lda, B,
+                    ldb, W, N, static_cast<int>(used), len, static_cast<int64_t>(len) * ldb,
+                    M * N, false, false, len};
+    hipError_t err = cfgs[c].launch(p, st);
+    if (err == hipSuccess) {
+        const bool vec4 = (N % 4) == 0 && (ldc % 4) == 0 &&
+                          reinterpret_cast<uintptr_t>(C) % 16 == 0 &&
+                          reinterpret_cast<uintptr_t>(W) % 16 == 0;
+        const int64_t items = M * (vec4 ? N / 4 : N);
+        const unsigned grid = static_cast<unsigned>(std::min<int64_t>((items + 255) / 256, 8192));
+        if (vec4)
+            hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(grid), dim3(256), 0, st, W, M * N,
+                               static_cast<int>(used), static_cast<int>(M), static_cast<int>(N), C,
+                               ldc);
+        else
+            hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(grid), dim3(256), 0, st, W, M * N,
+                               static_cast<int>(used), static_cast<int>(M), static_cast<int>(N), C,
+                               ldc);
+        err = hipGetLastError();
+    }
+    if (err != hipSuccess) return fail(GEMM_F32_EHIP, "launch failed: %s", hipGetErrorString(err));
+    return GEMM_F32_OK;
 }
 
 int gemm_f32_ex(int variant, int config_id, int opA, int opB, int64_t batch, int64_t M,

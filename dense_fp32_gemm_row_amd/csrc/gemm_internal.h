@@ -28,14 +28,18 @@ struct Problem {
     // Transposed operands: op(A) = A^T with A stored K x M (row-major, lda),
     // op(B) = B^T with B stored N x K (ldb).
     bool ta, tb;
+    // Split-K partial products: product b covers k in [b * ksplit,
+    // min((b + 1) * ksplit, K)) (0: every product runs over all of K).
+    int ksplit;
 };
 
 // Batch description passed to the kernels.
 struct BatchArgs {
     int count;
     int64_t sa, sb, sc;
+    int ksplit;
 };
-inline BatchArgs batch_of(const Problem &p) { return {p.batch, p.sa, p.sb, p.sc}; }
+inline BatchArgs batch_of(const Problem &p) { return {p.batch, p.sa, p.sb, p.sc, p.ksplit}; }
 
 // Host-side launch of one tile configuration.  Returns hipSuccess or the
 // error of the launch.
@@ -90,14 +94,16 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 // Splits a linear workgroup id over `tiles` tiles per product into the
-// product index (applied to the three base pointers) and the tile index.
+// product index (applied to the three base pointers, and for split-K
+// partial products to the K extent) and the tile index.
 template <class PA, class PB, class PC>
 __device__ __forceinline__ int batch_select(int lin, int tiles, const gemm_f32_impl::BatchArgs &bt,
-                                            PA &A, PB &B, PC &C) {
+                                            PA &A, PB &B, PC &C, int &K) {
     const int b = lin / tiles;
     A += static_cast<int64_t>(b) * bt.sa;
     B += static_cast<int64_t>(b) * bt.sb;
     C += static_cast<int64_t>(b) * bt.sc;
+    if (bt.ksplit > 0) K = min(bt.ksplit, K - b * bt.ksplit);
     return lin - b * tiles;
 }
 

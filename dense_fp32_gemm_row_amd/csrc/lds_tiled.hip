@@ -39,7 +39,7 @@ __global__ __launch_bounds__(T * T) void gemm_lds_kernel(
     __shared__ float tileB[T][T + PAD];
 
     const int tx = threadIdx.x, ty = threadIdx.y;
-    const int tile = batch_select(blockIdx.x, tiles_m * tiles_n, bt, A, B, C);
+    const int tile = batch_select(blockIdx.x, tiles_m * tiles_n, bt, A, B, C, K);
     const int tile_row = tile / tiles_n;
     const int tile_col = tile - tile_row * tiles_n;
     const int row = tile_row * T + ty;

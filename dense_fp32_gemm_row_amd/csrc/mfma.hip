@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
 
     int tm, tn;
     const int tile = batch_select(xcd_remap(blockIdx.x, tiles_m * tiles_n * bt.count),
-                                  tiles_m * tiles_n, bt, A, B, C);
+                                  tiles_m * tiles_n, bt, A, B, C, K);
     grouped_tile(tile, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
 
     int tm, tn;
     const int tile = batch_select(xcd_remap(blockIdx.x, tiles_m * tiles_n * bt.count),
-                                  tiles_m * tiles_n, bt, A, B, C);
+                                  tiles_m * tiles_n, bt, A, B, C, K);
     grouped_tile(tile, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(BX * BY) void gemm_naive_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t a_ri, int64_t a_rk,
     const float *__restrict__ B, int64_t b_rk, int64_t b_rj, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n, BatchArgs bt) {
-    const int tile = batch_select(blockIdx.x, tiles_m * tiles_n, bt, A, B, C);
+    const int tile = batch_select(blockIdx.x, tiles_m * tiles_n, bt, A, B, C, K);
     const int tile_row = tile / tiles_n;
     const int tile_col = tile - tile_row * tiles_n;
     const int row = tile_row * BY + threadIdx.y;  // vertical parts only

@@ -57,7 +57,7 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void gemm_regblock_kernel(
     const int tx = tid % TX, ty = tid / TX;
     int tm, tn;
     const int tile = batch_select(xcd_remap(blockIdx.x, tiles_m * tiles_n * bt.count),
-                                  tiles_m * tiles_n, bt, A, B, C);
+                                  tiles_m * tiles_n, bt, A, B, C, K);
     grouped_tile(tile, tiles_m, tiles_n, 8, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 

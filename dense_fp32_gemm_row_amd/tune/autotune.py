@@ -34,6 +34,10 @@ DEFAULT_SHAPES = [
     ("ffn", 8192, 14336, 4096),
     # one eighth of the 8192 rows: a row shard of the headline product
     ("square8192_rowshard8", 1024, 8192, 8192),
+    # few output tiles, long K: the split-K shape
+    ("deepk", 1024, 1024, 65536),
+    # one tiny product: the floor of one timed launch
+    ("tiny", 1, 1, 1),
 ]
 
 
@@ -55,6 +59,33 @@ def time_config(binding, v, c, dA, dB, dC, reps, warmup):
     return times[len(times) // 2]
 
 
+def time_fn(fn, budget_ms: float) -> float:
+    """Median milliseconds of fn() over enough launches to fill ~budget_ms."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    probe = []
+    for _ in range(3):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        probe.append(s.elapsed_time(e))
+    reps = int(max(5, min(500, budget_ms / max(min(probe), 1e-3))))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    times = sorted(s.elapsed_time(e) for s, e in ev)
+    return times[len(times) // 2]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", required=True, help="where to write the tuned table (JSON)")
@@ -64,6 +95,9 @@ def main() -> int:
     ap.add_argument("--shapes", default=",".join(s[0] for s in DEFAULT_SHAPES))
     ap.add_argument("--budget-ms", type=float, default=400.0,
                     help="approximate timed milliseconds per configuration")
+    ap.add_argument("--splits", default="",
+                    help="comma-separated split counts: also time gemm_f32_splitk with each "
+                         "(reported, not written to the table)")
     args = ap.parse_args()
 
     import torch
@@ -94,6 +128,20 @@ def main() -> int:
                 print(json.dumps({"shape": name, "M": M, "N": N, "K": K, "config": cname,
                                   "median_ms": round(ms, 5),
                                   "tflops": round(flops / ms / 1e9, 3)}), flush=True)
+        for splits in [int(x) for x in args.splits.split(",") if x]:
+            need = binding.gemm_f32_splitk_workspace_size(M, N, K, splits)
+            work = torch.empty(max(need // 4, 1), device="cuda")
+            for v in variants:
+                for c in range(binding.gemm_f32_config_count(v)):
+                    cname = binding.gemm_f32_config_name(v, c)
+
+                    def split_call(v=v, c=c):
+                        binding.gemm_splitk(dA, dB, splits, dC, work, variant=v, config=c)
+
+                    ms = time_fn(split_call, args.budget_ms)
+                    print(json.dumps({"shape": name, "M": M, "N": N, "K": K, "config": cname,
+                                      "splitk": splits, "median_ms": round(ms, 5),
+                                      "tflops": round(flops / ms / 1e9, 3)}), flush=True)
         results.sort()
         best_ms, best = results[0]
         entries[(M, N, K)] = {"M": M, "N": N, "K": K, "config": best, "shape": name,

@@ -27,6 +27,8 @@ Workloads (sizes are M x N x K; A is M x K, B is K x N, all row-major):
                      up-projection shape)
   * ``batched64_1024`` 64 independent 1024 x 1024 x 1024 products, uniform
                      (A is 64 x M x K, B is 64 x K x N, drawn in that order)
+  * ``deepk``        1024 x 1024 x 65536, uniform: few output tiles and a long
+                     K, the shape that split-K serves
 """
 
 from __future__ import annotations
@@ -62,6 +64,7 @@ WORKLOADS: dict[str, Workload] = {
         Workload("ragged_int4", 1000, 1023, 777, "int4"),
         Workload("ffn", 8192, 14336, 4096, "normal"),
         Workload("batched64_1024", 1024, 1024, 1024, "uniform", batch=64),
+        Workload("deepk", 1024, 1024, 65536, "uniform"),
     )
 }
 

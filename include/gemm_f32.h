@@ -186,6 +186,48 @@ int gemm_f32_ex(int variant, int config_id, int opA, int opB,
                 float *C, int64_t ldc, int64_t strideC,
                 void *stream);
 
+/*
+ * gemm_f32_splitk -- C = A x B computed as `splits` partial products over
+ * slices of K, for shapes with too few output tiles to fill the GPU (small
+ * or ragged products; "Tiling and Blocking for Reuse", "choosing the tile
+ * size": tail effects and occupancy bound the tile choice).
+ *
+ *   C = sum over s of A[:, K_s] x B[K_s, :],  K_s = [s * L, min((s + 1) L, K))
+ *
+ * L is ceil(K / splits) rounded up to a multiple of 32; the number of
+ * slices actually used is ceil(K / L) <= splits.  Each partial product
+ * goes to its own M x N slice of `workspace` (packed rows), then one more
+ * kernel adds the slices into C in ascending s for every element, so the
+ * result is deterministic.
+ *
+ *   variant, config_id  kernel of the partial products, as in gemm_f32_ex
+ *                       (-1, -1: the library's choice)
+ *   splits              1 .. 65535, or 0 for the library's choice (enough
+ *                       256 x 256 tiles to give every CU of the GPU one, at
+ *                       least 1024 k per split); one slice is the plain
+ *                       product and needs no workspace
+ *   workspace           device memory of at least
+ *                       gemm_f32_splitk_workspace_size(M, N, K, splits)
+ *                       bytes, 4-byte aligned, owned by the caller, not
+ *                       overlapping A, B or C; its contents are overwritten
+ *   others              as in gemm_f32
+ *
+ * Returns as gemm_f32 (GEMM_F32_EINVAL also for a missing or short
+ * workspace).
+ */
+int gemm_f32_splitk(int variant, int config_id, int64_t splits,
+                    int64_t M, int64_t N, int64_t K,
+                    const float *A, int64_t lda,
+                    const float *B, int64_t ldb,
+                    float *C, int64_t ldc,
+                    void *workspace, int64_t workspace_bytes,
+                    void *stream);
+
+/* Bytes of workspace gemm_f32_splitk needs for these arguments, splits = 0
+   meaning the library's choice (0 when it needs none, or for invalid
+   sizes). */
+int64_t gemm_f32_splitk_workspace_size(int64_t M, int64_t N, int64_t K, int64_t splits);
+
 /* Static description of a return code; never NULL. */
 const char *gemm_f32_strerror(int code);
 

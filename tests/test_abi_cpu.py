@@ -214,3 +214,41 @@ def test_gemm_ex_validation(lib):
     assert "overlaps A" in b.gemm_f32_last_error()
     # empty products succeed without touching the device
     assert b.gemm_f32_ex(-1, -1, b.OP_T, b.OP_T, 1, 0, 6, 5, 0, 1, 0, 0, 5, 0, 0, 6, 0, None) == 0
+
+
+def test_splitk_workspace_size(lib):
+    f = b.gemm_f32_splitk_workspace_size
+    # K = 1000 in 4 splits: length ceil(250 / 32) * 32 = 256, 4 slices
+    assert f(100, 30, 1000, 4) == 4 * 100 * 30 * 4
+    # 7 splits of K = 100: length 32, only 4 slices are used
+    assert f(10, 10, 100, 7) == 4 * 10 * 10 * 4
+    # one slice: no workspace
+    assert f(10, 10, 32, 8) == 0
+    assert f(10, 10, 100, 1) == 0
+    assert f(0, 10, 100, 4) == 0 and f(-1, 10, 100, 4) == 0 and f(10, 10, 100, -1) == 0
+    # library choice (splits = 0): 16 tiles of 256 x 256 -> 16 splits when K allows
+    assert f(1024, 1024, 65536, 0) == 16 * 1024 * 1024 * 4
+    assert f(1024, 1024, 4096, 0) == 4 * 1024 * 1024 * 4   # at least 1024 k per split
+    assert f(1000, 1023, 777, 0) == 0                      # too little K: one slice
+
+
+def test_splitk_validation(lib):
+    base = dict(M=100, N=30, K=1000, A=0x100000, lda=1000, B=0x200000, ldb=30, C=0x300000, ldc=30)
+    need = b.gemm_f32_splitk_workspace_size(100, 30, 1000, 4)
+
+    def call(splits=4, ws=0x400000, wbytes=need, **kw):
+        a = dict(base, **kw)
+        return b.gemm_f32_splitk(-1, -1, splits, a["M"], a["N"], a["K"], a["A"], a["lda"], a["B"],
+                                 a["ldb"], a["C"], a["ldc"], ws, wbytes, None)
+
+    assert call(splits=-1) == b.GEMM_F32_EINVAL and "splits" in b.gemm_f32_last_error()
+    assert call(splits=70000) == b.GEMM_F32_EINVAL
+    assert call(ws=None) == b.GEMM_F32_EINVAL and "workspace" in b.gemm_f32_last_error()
+    assert call(wbytes=need - 4) == b.GEMM_F32_EINVAL and "needed" in b.gemm_f32_last_error()
+    assert call(ws=0x400002) == b.GEMM_F32_EINVAL
+    assert call(ws=0x300000 + 400) == b.GEMM_F32_EINVAL and "overlaps" in b.gemm_f32_last_error()
+    assert call(lda=999) == b.GEMM_F32_EINVAL and "lda" in b.gemm_f32_last_error()
+    assert b.gemm_f32_splitk(-2, 0, 4, 1, 1, 1, 0x1000, 1, 0x2000, 1, 0x3000, 1, 0x4000, 64,
+                             None) == b.GEMM_F32_ENOKERNEL
+    # empty products need nothing
+    assert call(M=0) == b.GEMM_F32_OK

@@ -414,6 +414,75 @@ def test_transposed_rejected_where_unsupported():
 
 
 # --------------------------------------------------------------------------
+# split-K
+# --------------------------------------------------------------------------
+
+SPLITK_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4"), (1, 1, "lds_t32"),
+                  (2, 0, "regblock_128x128x8_t8x8_pad4")] + [
+    (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in (
+        "mfma_64x64x32_w2x2_pa4_pb0", "mfma3_64x64x16_w2x2_swz_pb0", "mfma3_128x128x16_w2x2_swz_pb0",
+        "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz")]
+
+
+@pytest.mark.parametrize("kernel", SPLITK_KERNELS, ids=[k[2] for k in SPLITK_KERNELS])
+@pytest.mark.parametrize("splits", [2, 3, 7, 0])
+def test_splitk(kernel, splits):
+    import torch
+
+    M, N, K = 300, 277, 1029
+    v, c, name = kernel
+    log(f"split-K {splits} on {name}")
+    A, B = make_inputs(M, N, K, "int4", seed=41)
+    dA, dB = to_dev(A), to_dev(B)
+    buf = torch.full((M, N + 3), float("nan"), device="cuda:0")
+    b.gemm_splitk(dA, dB, splits, buf[:, :N], variant=v, config=c)
+    host = to_host(buf)
+    assert_exact(host[:, :N], oracle.gemm(A, B), f"{name} splits={splits} int4")
+    assert np.isnan(host[:, N:]).all()
+    A, B = make_inputs(M, N, K, "uniform", seed=42)
+    dA, dB = to_dev(A), to_dev(B)
+    out1 = b.gemm_splitk(dA, dB, splits, variant=v, config=c)
+    out2 = b.gemm_splitk(dA, dB, splits, variant=v, config=c)
+    _, ref64 = oracle.gemm(A, B, return_f64=True)
+    C1 = to_host(out1)
+    assert_close(C1, ref64, K, f"{name} splits={splits} uniform")
+    assert np.array_equal(C1.view(np.uint32), to_host(out2).view(np.uint32)), "not reproducible"
+
+
+@pytest.mark.parametrize("kernel", SPLITK_KERNELS, ids=[k[2] for k in SPLITK_KERNELS])
+def test_splitk_full_tiles(kernel):
+    """Whole tiles and whole splits: the unguarded and direct-load paths."""
+    v, c, name = kernel
+    log(f"split-K full tiles on {name}")
+    M, N, K = 512, 512, 1024
+    A, B = make_inputs(M, N, K, "int4", seed=43)
+    out = b.gemm_splitk(to_dev(A), to_dev(B), 4, variant=v, config=c)
+    assert_exact(to_host(out), oracle.gemm(A, B), f"{name} full tiles")
+
+
+def test_splitk_deep_k_sampled():
+    """The deep-K workload in the launch configuration the benchmark times
+    (library's choice of kernel and of splits)."""
+    w = WORKLOADS["deepk"]
+    log(f"split-K full size {w.name}")
+    A, B = workload_inputs(w.name)
+    C = to_host(b.gemm_splitk(to_dev(A), to_dev(B), 0))
+    assert not np.isnan(C).any()
+    rows = sample_rows(w.M, count=12)
+    _, ref64 = oracle_rows(A, B, rows)
+    assert_close(C[rows], ref64, w.K, "deepk")
+    assert freivalds(A, B, C) <= 1e-5
+
+
+def test_splitk_one_split_is_plain_product():
+    A, B = make_inputs(200, 100, 64, "uniform", seed=44)
+    dA, dB = to_dev(A), to_dev(B)
+    one = to_host(b.gemm_splitk(dA, dB, 1))
+    plain = to_host(b.gemm(dA, dB))
+    assert np.array_equal(one.view(np.uint32), plain.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
 # full-size workloads in the benchmark's launch configuration
 # --------------------------------------------------------------------------
 
