@@ -64,6 +64,101 @@ def read_traffic(workload: str, config_name: str) -> float | None:
     return float(val.group(1))
 
 
+def cpu_model() -> str | None:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def device_info(dev) -> dict:
+    """Compute units and maximum engine clock of the device, and the FP32
+    matrix peak they imply (CUs x 4 SIMDs x 64 FLOP per clock x clock).  The
+    clock comes from rocminfo, run as a child process; None when unavailable."""
+    import subprocess
+
+    import torch
+
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": p.gcnArchName, "cus": p.multi_processor_count,
+            "max_sclk_mhz": None, "peak_from_clock_tflops": None}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return info
+    arch = p.gcnArchName.split(":")[0]
+    for agent in out.split("Agent ")[1:]:
+        if re.search(rf"Name:\s+{re.escape(arch)}\b", agent) is None:
+            continue
+        clk = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        cus = re.search(r"Compute Unit:\s+(\d+)", agent)
+        if clk and cus:
+            info["max_sclk_mhz"] = int(clk.group(1))
+            info["peak_from_clock_tflops"] = round(
+                int(cus.group(1)) * 4 * 64 * int(clk.group(1)) * 1e6 / 1e12, 1)
+        break
+    return info
+
+
+class SclkSampler:
+    """Samples the device's current engine clock from the amdgpu driver's
+    pp_dpm_sclk file (the level marked '*') in a thread, while the timed
+    region runs.  Reports nothing where the file is absent or unreadable."""
+
+    def __init__(self, dev, period_s: float = 0.05, enabled: bool = True):
+        import threading
+
+        import torch
+
+        p = torch.cuda.get_device_properties(dev)
+        self.path = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
+                     f"{p.pci_device_id:02x}.0/pp_dpm_sclk")
+        self.period = period_s
+        self.enabled = enabled
+        self.samples: list[int] = []
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self) -> int | None:
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
+    def _run(self):
+        while not self.stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self.stop.wait(self.period)
+
+    def __enter__(self):
+        if self.enabled and os.access(self.path, os.R_OK):
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.thread.is_alive():
+            self.thread.join()
+
+    def summary(self) -> dict | None:
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"samples": len(v), "min_mhz": v[0], "median_mhz": v[len(v) // 2],
+                "max_mhz": v[-1], "source": "pp_dpm_sclk"}
+
+
 def time_launches(fn, steps: int, warmup: int, stream):
     """Runs fn() warmup times, then `steps` times with an event pair around
     each launch on `stream`.  Returns (total_ms, per-launch ms list)."""
@@ -110,6 +205,7 @@ def cpu_baseline(A, B, target_s: float) -> dict:
         "value": round(flops / t / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{len(rng_rows)} of {M} output rows (evenly spaced), each a full "
                   f"{K}x{N} sweep; {t:.1f} s wall, FP64 accumulation",
@@ -153,6 +249,8 @@ def main() -> int:
     ap.add_argument("--splitk", type=int, default=None, metavar="S",
                     help="time gemm_f32_splitk with S splits (partial products + reduction); "
                          "0 = the library's choice of splits")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="do not sample the engine clock during the timed region")
     ap.add_argument("--stages", action="store_true")
     ap.add_argument("--stage-variants", default="naive,lds,regblock,mfma",
                     help="variants that --stages times")
@@ -172,8 +270,8 @@ def main() -> int:
     from dense_fp32_gemm_row_amd import binding
     from dense_fp32_gemm_row_amd.workloads import WORKLOADS, workload_inputs
 
-    if args.ops != "NN" and (args.stages or args.variant is not None):
-        print("--ops applies to the library's own choice only", file=sys.stderr)
+    if args.ops != "NN" and args.stages:
+        print("--ops does not apply to --stages", file=sys.stderr)
         return 2
     if args.splitk is not None and (args.ops != "NN" or args.stages):
         print("--splitk takes row-major operands and no --stages", file=sys.stderr)
@@ -230,14 +328,17 @@ def main() -> int:
         sv, sc = (None, -1) if args.variant is None else (v, c)
         fn = lambda: binding.gemm_splitk(dA, dB, args.splitk, dC, work,  # noqa: E731
                                          variant=sv, config=sc)
-        splits = args.splitk or "library choice"
-        cname = f"{cname if args.variant is not None else 'library choice'} split-K {splits}"
+        splits = args.splitk or "library choice of"
+        cname = (f"{cname if args.variant is not None else 'library choice'}, "
+                 f"split-K ({splits} splits)")
     elif args.variant is None:
         fn = lambda: call(dA, dB, dC)  # noqa: E731  (gemm_f32 / gemm_f32_strided_batched)
     else:
         fn = lambda: call(dA, dB, dC, variant=v, config=c)  # noqa: E731
 
-    total_ms, per = time_launches(fn, args.steps, args.warmup, stream)
+    dinfo = device_info(dev)
+    with SclkSampler(dev, enabled=not args.no_sclk) as sclk:
+        total_ms, per = time_launches(fn, args.steps, args.warmup, stream)
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
     value = flops * args.steps / (total_ms / 1e3) / 1e12
@@ -272,8 +373,11 @@ def main() -> int:
             "traffic": read_traffic(w.name, cname),
             "kernel": cname,
             "avg_launch_ms": round(avg_launch_ms, 4),
+            "launch_ms": {"median": round(sorted(per)[len(per) // 2], 4),
+                          "min": round(min(per), 4), "max": round(max(per), 4)},
             "flops_per_launch": flops,
         },
+        "device": dict(dinfo, sclk_during_timing=sclk.summary()),
     }
 
     rc = 0

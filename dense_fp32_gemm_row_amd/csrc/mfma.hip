@@ -230,9 +230,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
 //    floats, 32 consecutive r per half wavefront.
 // Register staging (with zero fill outside the matrix) and direct
 // global -> LDS loads are provided for both.
-template <int R, int BK, int PAD, bool KMAJOR, int NT, int NW, bool GUARD, bool VEC, bool DIRECT>
+template <int R, int BK, int PAD, bool KMAJOR, int NT, int NW, bool GUARD, bool VEC, bool DIRECT,
+          int IL = 1>
 struct OperandTile {
     static constexpr bool SWZ = !KMAJOR && PAD <= 0;
+    static_assert(IL == 1 || (KMAJOR && (IL == 2 || IL == 4)), "interleave: k-major, 2 or 4 blocks");
     static constexpr int LD = KMAJOR ? R + (PAD > 0 ? PAD : 0) : BK + (SWZ ? 0 : PAD);  // row length
     static constexpr int SIZE = KMAJOR ? BK * LD : R * LD;               // floats per buffer
     static constexpr int L = (R * BK) / (4 * NT);                        // float4 slots per thread
@@ -332,20 +334,59 @@ struct OperandTile {
         }
     }
 
-    // The 4 values (k = kc * 8 + 4 * half + s, s = 0..3) of F blocks of 32
-    // rows starting at row `rbase`, for lane l32 of half wavefront `half`.
-    template <int F>
-    __device__ __forceinline__ void read(const float *buf, int kc, int rbase, int half, int l32,
-                                         float (&v)[F][4]) const {
+    // Per-lane part of the fragment reads of F blocks of 32 rows starting at
+    // row `rbase`, for lane l32 of half wavefront `half`: an LDS offset
+    // computed once, outside the K loop.  It is kept as one opaque value so
+    // that the read addresses stay a short chain of offsets from the LDS
+    // array (buffer, lane offset, chunk slot): the compiler's alias scopes
+    // for the LDS arrays only reach that far, and without them it cannot tell
+    // these reads from the direct loads of the other buffer and waits for
+    // those loads before every K-step.
+    int rd, rg, rh;
+    __device__ __forceinline__ void init_read(int rbase, int half, int l32) {
         if constexpr (KMAJOR) {
-            const float *p = buf + (kc * 8 + 4 * half) * LD + rbase + l32;
+            rd = 4 * half * LD + rbase + IL * l32;
+        } else {
+            rd = (rbase + l32) * LD;
+            rg = SWZ ? swz(l32) : 0;
+            rh = half;
+        }
+        asm("" : "+v"(rd));
+    }
+
+    // The 4 values (k = kc * 8 + 4 * half + s, s = 0..3) of F blocks of 32
+    // rows, for the lane set up by init_read.  IL = 1: block f holds rows
+    // 32 f + l32 of the wave's slice.  IL = F (k-major only): block f holds
+    // rows F l32 + f, so a lane's F values of one k are adjacent in LDS and
+    // come in one vector read.
+
+    template <int F>
+    __device__ __forceinline__ void read(const float *buf, int kc, float (&v)[F][4]) const {
+        if constexpr (KMAJOR && IL == 4) {
+            static_assert(F == 4, "interleave width = blocks per wave");
+            const float *p = buf + rd + kc * 8 * LD;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float4 q = *reinterpret_cast<const float4 *>(p + s * LD);
+                v[0][s] = q.x, v[1][s] = q.y, v[2][s] = q.z, v[3][s] = q.w;
+            }
+        } else if constexpr (KMAJOR && IL == 2) {
+            static_assert(F == 2, "interleave width = blocks per wave");
+            const float *p = buf + rd + kc * 8 * LD;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float2 q = *reinterpret_cast<const float2 *>(p + s * LD);
+                v[0][s] = q.x, v[1][s] = q.y;
+            }
+        } else if constexpr (KMAJOR) {
+            const float *p = buf + rd + kc * 8 * LD;
 #pragma unroll
             for (int f = 0; f < F; ++f)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) v[f][s] = p[s * LD + f * 32];
         } else {
-            const int slot = SWZ ? (2 * kc + half) ^ swz(l32) : 2 * kc + half;
-            const float *p = buf + (rbase + l32) * LD + slot * 4;
+            const int slot = SWZ ? (2 * kc + rh) ^ rg : 2 * kc + rh;
+            const float *p = buf + rd + slot * 4;
 #pragma unroll
             for (int f = 0; f < F; ++f) {
                 const float4 q = *reinterpret_cast<const float4 *>(p + f * 32 * LD);
@@ -355,9 +396,10 @@ struct OperandTile {
     }
 
     // LDS read instructions per chunk for F blocks (pairs of k-major blocks
-    // 32 floats apart merge into one two-address read).
+    // 32 floats apart merge into one two-address read; interleaved blocks
+    // are one vector read per k).
     template <int F>
-    static constexpr int reads() { return KMAJOR ? 4 * ((F + 1) / 2) : F; }
+    static constexpr int reads() { return KMAJOR ? (IL > 1 ? 4 : 4 * ((F + 1) / 2)) : F; }
 };
 
 // Pipelined kernel, with a ring of STAGES (2 or 3) LDS buffers.  Within a
@@ -378,8 +420,14 @@ struct OperandTile {
 // TA / TB: op(A) = A^T (A stored K x M) / op(B) = B^T (B stored N x K); a
 // transposed operand swaps storage flavour (see OperandTile), nothing else
 // changes.
+//
+// IL: when B's tile is k-major (B as stored), interleave the wave's column
+// blocks: lane l32 of block j owns column FN l32 + j of the wave's columns
+// instead of 32 j + l32.  A lane's B values of one k are then FN adjacent
+// floats, one LDS read instead of FN / 2 two-address reads, and its
+// outputs in one row are FN adjacent floats, one vector store.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
-          bool GUARD, bool VEC, bool TA, bool TB>
+          bool GUARD, bool VEC, bool TA, bool TB, bool IL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
@@ -389,7 +437,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int KC = BK / 8;  // chunks of 8 k per K-step
     using TileA = OperandTile<BM, BK, PADA, TA, NT, NW, GUARD, VEC, DIRECT>;
-    using TileB = OperandTile<BN, BK, PADB, !TB, NT, NW, GUARD, VEC, DIRECT>;
+    constexpr int ILB = (IL && !TB) ? FN : 1;  // interleave of B's column blocks
+    using TileB = OperandTile<BN, BK, PADB, !TB, NT, NW, GUARD, VEC, DIRECT, ILB>;
     constexpr int kReadsPerChunk = TileA::template reads<FM>() + TileB::template reads<FN>();
     constexpr int kMfmaPerChunk = FM * FN * 4;
     constexpr int kPairs = kReadsPerChunk < kMfmaPerChunk ? kReadsPerChunk : kMfmaPerChunk;
@@ -434,13 +483,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
 
     const int half = lane >> 5;
     const int l32 = lane & 31;
+    ta.init_read(wm * WTM, half, l32);
+    tb.init_read(wn * WTN, half, l32);
 
     // Two fragment register sets: operands of one chunk of 8 k.
     float fa[2][FM][4];
     float fb[2][FN][4];
     auto read_frag = [&](int set, int buf, int kc) {
-        ta.template read<FM>(sA[buf], kc, wm * WTM, half, l32, fa[set]);
-        tb.template read<FN>(sB[buf], kc, wn * WTN, half, l32, fb[set]);
+        ta.template read<FM>(sA[buf], kc, fa[set]);
+        tb.template read<FN>(sB[buf], kc, fb[set]);
     };
 
     floatx16 acc[FM][FN];
@@ -533,16 +584,48 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
 
     // accumulator register r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4,
     // column l % 32 of its block
+    if constexpr (ILB > 1) {
+        // column block j of lane l32 is column ILB * l32 + j of the wave
+        const int gn = n0 + wn * WTN + ILB * l32;
+        const int gm0 = m0 + wm * WTM + 4 * half;
+        const bool vec_c = !GUARD && ((reinterpret_cast<uintptr_t>(C) |
+                                       static_cast<uintptr_t>(ldc * 4)) & (4 * ILB - 1)) == 0;
+        if (vec_c) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int gn = n0 + wn * WTN + j * 32 + l32;
+                for (int r = 0; r < 16; ++r) {
+                    float *row = C + static_cast<int64_t>(gm0 + i * 32 + 8 * (r / 4) + r % 4) * ldc + gn;
+                    if constexpr (ILB == 4)
+                        *reinterpret_cast<float4 *>(row) =
+                            make_float4(acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]);
+                    else
+                        *reinterpret_cast<float2 *>(row) = make_float2(acc[i][0][r], acc[i][1][r]);
+                }
+        } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int gm = m0 + wm * WTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                if (!GUARD || (gm < M && gn < N))
-                    C[static_cast<int64_t>(gm) * ldc + gn] = acc[i][j][r];
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = gm0 + i * 32 + 8 * (r / 4) + r % 4;
+                    float *row = C + static_cast<int64_t>(gm) * ldc + gn;
+#pragma unroll
+                    for (int j = 0; j < ILB; ++j)
+                        if (!GUARD || (gm < M && gn + j < N)) row[j] = acc[i][j][r];
+                }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int gn = n0 + wn * WTN + j * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int gm = m0 + wm * WTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                    if (!GUARD || (gm < M && gn < N))
+                        C[static_cast<int64_t>(gm) * ldc + gn] = acc[i][j][r];
+                }
             }
         }
     }
@@ -552,10 +635,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
 // many LDS buffers.  DIRECT: direct global -> LDS loads where the shape
 // allows (full tiles, 16-byte-aligned rows), register staging otherwise.
 // TRANS: also compiled for transposed operands (pipelined kernel only).
+// IL: interleaved column blocks for B as stored (pipelined kernel only).
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int GROUP_M, int PIPE,
-          bool DIRECT = false, bool TRANS = false>
+          bool DIRECT = false, bool TRANS = false, bool IL = false>
 hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     static_assert(!TRANS || PIPE > 0, "transposed operands need the pipelined kernel");
+    static_assert(!IL || PIPE > 0, "interleaved blocks need the pipelined kernel");
     constexpr int NT = 64 * WM * WN;
     if ((p.ta || p.tb) && !TRANS) return hipErrorNotSupported;
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
@@ -566,7 +651,8 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     const dim3 g(static_cast<unsigned>(grid)), b(NT);
 #define GEMM_RING(D, G, V, TA, TB)                                                              \
     hipLaunchKernelGGL(                                                                         \
-        (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, D, G, V, TA, TB>), g, b, 0, \
+        (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, D, G, V, TA, TB, IL>), g, b, \
+        0,                                                                                      \
         stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, GROUP_M,   \
         batch_of(p))
 #define GEMM_RING_T(D, G, V)                                                                    \
@@ -635,6 +721,17 @@ const ConfigEntry kMfmaConfigs[] = {
     {"mfma2d_256x256x32_w2x4_swz", launch_mfma<256, 256, 32, 2, 4, -1, 0, 8, 2, true>, 0},
     {"mfma3d_256x128x32_w4x2_swz", launch_mfma<256, 128, 32, 4, 2, -1, 0, 8, 3, true, true>, kCapTransposed},
     {"mfma3d_128x256x32_w2x4_swz", launch_mfma<128, 256, 32, 2, 4, -1, 0, 8, 3, true>, 0},
+    // Interleaved column blocks of B as stored (il): one 8- or 16-byte LDS
+    // read per k for the wave's 2 or 4 column blocks, vector C stores.
+    {"mfma2d_256x256x32_w4x4_swz_g4_il", launch_mfma<256, 256, 32, 4, 4, -1, 0, 4, 2, true, true, true>, kCapTransposed},
+    {"mfma2d_256x256x32_w4x2_swz_g4_il", launch_mfma<256, 256, 32, 4, 2, -1, 0, 4, 2, true, true, true>, kCapTransposed},
+    {"mfma2d_256x256x32_w2x4_swz_g4_il", launch_mfma<256, 256, 32, 2, 4, -1, 0, 4, 2, true, true, true>, kCapTransposed},
+    {"mfma3d_256x128x32_w4x2_swz_il", launch_mfma<256, 128, 32, 4, 2, -1, 0, 8, 3, true, true, true>, kCapTransposed},
+    {"mfma3d_128x256x16_w2x4_swz_il", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3, true, true, true>, kCapTransposed},
+    {"mfma3_64x128x16_w2x2_swz_il", launch_mfma<64, 128, 16, 2, 2, -1, 0, 8, 3, false, true, true>, kCapTransposed},
+    {"mfma2d_256x256x32_w2x2_swz_g4_il", launch_mfma<256, 256, 32, 2, 2, -1, 0, 4, 2, true, true, true>, kCapTransposed},
+    {"mfma2d_256x256x32_w2x2_swz_g8_il", launch_mfma<256, 256, 32, 2, 2, -1, 0, 8, 2, true, true, true>, kCapTransposed},
+    {"mfma2d_256x256x32_w2x4_swz_g8_il", launch_mfma<256, 256, 32, 2, 4, -1, 0, 8, 2, true, true, true>, kCapTransposed},
 };
 
 }  // namespace

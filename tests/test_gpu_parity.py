@@ -50,6 +50,8 @@ def run(A: np.ndarray, B: np.ndarray, variant=None, config=-1, ldc_pad=0):
     else:
         dC = torch.empty((M, N), device="cuda:0")
     b.gemm(dA, dB, dC, variant=variant, config=config)
+    if ldc_pad:
+        assert bool(torch.isnan(buf[:, N:]).all()), "write outside C's columns"
     return to_host(dC)
 
 
@@ -127,6 +129,10 @@ def test_full_tiles(v, c, name):
     P[np.arange(512), perm] = 1.0
     Y = rng.standard_normal((512, N), dtype=np.float32)
     assert_exact(run(P, Y, v, c), Y[perm], name + " P.B")
+    # C rows at an odd stride inside a NaN guard band: whole tiles, but no
+    # vector stores of C
+    A, B = make_inputs(M, N, K, "int4", seed=16)
+    assert_exact(run(A, B, v, c, ldc_pad=1), oracle.gemm(A, B), name + " int4 odd ldc")
 
 
 # --------------------------------------------------------------------------
@@ -351,7 +357,12 @@ def test_strided_batched_full_tiles(kernel):
 
 TRANS_CAPABLE = ["mfma2d_256x256x32_w4x4_swz", "mfma3d_256x128x32_w4x2_swz",
                  "mfma3d_128x256x16_w2x4_swz", "mfma3_64x64x16_w2x2_swz_pb0",
-                 "mfma3_128x128x16_w2x2_swz_pb0", "mfma2p_256x256x32_w4x4_swz_pb0"]
+                 "mfma3_128x128x16_w2x2_swz_pb0", "mfma2p_256x256x32_w4x4_swz_pb0",
+                 "mfma2d_256x256x32_w4x4_swz_g4_il", "mfma2d_256x256x32_w4x2_swz_g4_il",
+                 "mfma2d_256x256x32_w2x4_swz_g4_il", "mfma3d_256x128x32_w4x2_swz_il",
+                 "mfma3d_128x256x16_w2x4_swz_il", "mfma3_64x128x16_w2x2_swz_il",
+                 "mfma2d_256x256x32_w2x2_swz_g4_il", "mfma2d_256x256x32_w2x2_swz_g8_il",
+                 "mfma2d_256x256x32_w2x4_swz_g8_il"]
 TRANS_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in TRANS_CAPABLE]
 OPS = ["NN", "NT", "TN", "TT"]
