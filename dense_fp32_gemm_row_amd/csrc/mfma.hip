@@ -244,7 +244,13 @@ struct OperandTile {
     static constexpr int J = DIRECT ? CH / NW : 1;
     static_assert(L * 4 * NT == R * BK, "even tile split");
     static_assert(LD % 4 == 0, "16-byte aligned LDS rows");
-    static_assert(!DIRECT || (PAD <= 0 && !GUARD && VEC), "direct loads: unpadded full tiles");
+    // Direct loads need unpadded LDS rows and 16-byte-aligned global rows.
+    // With GUARD they serve tiles that overhang the operand's R extent (M or
+    // N): the overhanging rows only feed outputs that are never stored, so
+    // instead of zero fill their loads are clamped onto the last valid row
+    // (row flavour) or 16-byte group (k-major flavour, which needs the R
+    // extent to be a multiple of 4).  K must be whole K-steps.
+    static_assert(!DIRECT || (PAD <= 0 && VEC), "direct loads: unpadded tiles, aligned rows");
     static_assert(!DIRECT || CH % NW == 0, "whole chunks per wavefront");
 
     // XOR swizzle of the row flavour: slot q of row m is stored at slot
@@ -289,11 +295,15 @@ struct OperandTile {
                 dst[j] = c * 256;
                 if constexpr (KMAJOR) {
                     const int f = c * 256 + lane * 4;  // float offset in the k-major tile
-                    src[j] = X + static_cast<int64_t>(f / R) * ld + r0 + f % R;
+                    int col = r0 + f % R;
+                    if (GUARD && col > rlim - 4) col = rlim - 4;
+                    src[j] = X + static_cast<int64_t>(f / R) * ld + col;
                 } else {
                     const int m = c * (64 / S) + lane / S;  // tile row of this lane's slot
                     const int q = (lane % S) ^ swz(m);      // logical slot stored there
-                    src[j] = X + static_cast<int64_t>(r0 + m) * ld + 4 * q;
+                    int row = r0 + m;
+                    if (GUARD && row > rlim - 1) row = rlim - 1;
+                    src[j] = X + static_cast<int64_t>(row) * ld + 4 * q;
                 }
             }
         }
@@ -426,209 +436,229 @@ struct OperandTile {
 // instead of 32 j + l32.  A lane's B values of one k are then FN adjacent
 // floats, one LDS read instead of FN / 2 two-address reads, and its
 // outputs in one row are FN adjacent floats, one vector store.
+// One output tile of the pipelined kernel: the K loop and the epilogue for
+// the tile at (m0, n0), with the LDS buffers of the workgroup.
+template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
+          bool GUARD, bool VEC, bool TA, bool TB, bool IL>
+struct RingTile {
+    static constexpr int NT = 64 * WM * WN, NW = WM * WN;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static constexpr int KC = BK / 8;  // chunks of 8 k per K-step
+    using TileA = OperandTile<BM, BK, PADA, TA, NT, NW, GUARD, VEC, DIRECT>;
+    static constexpr int ILB = (IL && !TB) ? FN : 1;  // interleave of B's column blocks
+    using TileB = OperandTile<BN, BK, PADB, !TB, NT, NW, GUARD, VEC, DIRECT, ILB>;
+    static constexpr int kReadsPerChunk = TileA::template reads<FM>() + TileB::template reads<FN>();
+    static constexpr int kMfmaPerChunk = FM * FN * 4;
+    static constexpr int kPairs = kReadsPerChunk < kMfmaPerChunk ? kReadsPerChunk : kMfmaPerChunk;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32 x 32 blocks");
+    static_assert(BK % 16 == 0, "an even number of chunks per K-step");
+    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS buffers");
+    static_assert(STAGES * (TileA::SIZE + TileB::SIZE) * 4 <= kLdsBytes, "LDS budget of a workgroup");
+
+
+    template <int SA, int SB>
+    static __device__ __forceinline__ void run(int M, int N, int K, const float *__restrict__ A,
+                                               int64_t lda, const float *__restrict__ B,
+                                               int64_t ldb, float *__restrict__ C, int64_t ldc,
+                                               int m0, int n0, float (&sA)[STAGES][SA],
+                                               float (&sB)[STAGES][SB]) {
+        static_assert(SA == TileA::SIZE && SB == TileB::SIZE, "LDS buffers of this tile shape");
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wave / WN, wn = wave % WN;
+
+        TileA ta;
+        TileB tb;
+        ta.init(A, lda, m0, M, tid, wave, lane);
+        tb.init(B, ldb, n0, N, tid, wave, lane);
+        auto load_step = [&](int k0, int buf) {
+            if constexpr (DIRECT) {
+                ta.load_direct(k0, sA[buf]);
+                tb.load_direct(k0, sB[buf]);
+            } else {
+                ta.load(k0, K);
+                tb.load(k0, K);
+            }
+        };
+        auto store_step = [&](int buf) {
+            if constexpr (!DIRECT) {
+                ta.store(sA[buf]);
+                tb.store(sB[buf]);
+            }
+        };
+
+        const int half = lane >> 5;
+        const int l32 = lane & 31;
+        ta.init_read(wm * WTM, half, l32);
+        tb.init_read(wn * WTN, half, l32);
+
+        // Two fragment register sets: operands of one chunk of 8 k.
+        float fa[2][FM][4];
+        float fb[2][FN][4];
+        auto read_frag = [&](int set, int buf, int kc) {
+            ta.template read<FM>(sA[buf], kc, fa[set]);
+            tb.template read<FN>(sB[buf], kc, fb[set]);
+        };
+
+        floatx16 acc[FM][FN];
+    #pragma unroll
+        for (int i = 0; i < FM; ++i)
+    #pragma unroll
+            for (int j = 0; j < FN; ++j)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        auto mfma_chunk = [&](int set) {
+    #pragma unroll
+            for (int s = 0; s < 4; ++s)
+    #pragma unroll
+                for (int i = 0; i < FM; ++i)
+    #pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[set][i][s], fb[set][j][s],
+                                                                         acc[i][j], 0, 0, 0);
+        };
+
+        const int nk = (K + BK - 1) / BK;
+    #pragma unroll
+        for (int st = 0; st < STAGES - 1; ++st) {
+            if (st < nk) {
+                load_step(st * BK, st);
+                store_step(st);
+            }
+        }
+        __syncthreads();
+        read_frag(0, 0, 0);
+
+        int cur = 0;  // t mod STAGES
+        for (int t = 0; t < nk; ++t) {
+            const int nxt = cur == STAGES - 1 ? 0 : cur + 1;
+            const int ahead = cur == 0 ? STAGES - 1 : cur - 1;  // (t + STAGES - 1) mod STAGES
+            if (t + STAGES - 1 < nk) load_step((t + STAGES - 1) * BK, ahead);
+            // Branch-free so that the reads stay ahead of the MFMAs they feed
+            // (a branch here lets the compiler sink them back to their use).
+            //
+            // Three buffers: the last chunk reads ahead into step t + 1 (tile t + 1
+            // was published by the previous barrier); the barrier ends the step.
+            //
+            // Two buffers: the barrier sits before the last chunk.  By then the
+            // last chunk's fragments are in registers (so every read of buffer
+            // `cur` is done: write after read) and tile t + 1 has landed in buffer
+            // `nxt` (read after write), so right after the barrier the first
+            // fragments of step t + 1 are read while the last chunk's MFMAs run.
+            //
+            // In the last step the look-ahead read of buffer `nxt` is unused; it
+            // stays inside the buffer, which nobody writes after the barrier.
+    #pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const int set = kc & 1;
+                if constexpr (STAGES == 2) {
+                    if (kc == KC - 1) {
+                        store_step(nxt);  // register staging: stale but in-bounds in the last step
+                        // keep all of the previous chunk's MFMAs ahead of the
+                        // barrier: they cover the latency of the reads it waits for
+                        __builtin_amdgcn_sched_barrier(0);
+                        __syncthreads();
+                        read_frag(set ^ 1, nxt, 0);
+                    } else {
+                        read_frag(set ^ 1, cur, kc + 1);
+                    }
+                } else {
+                    read_frag(set ^ 1, kc + 1 < KC ? cur : nxt, kc + 1 < KC ? kc + 1 : 0);
+                }
+                mfma_chunk(set);
+                // Issue order for the scheduler: the reads of the next chunk go
+                // out one per MFMA at the start of this chunk, so their latency
+                // hides behind the remaining MFMAs and the matrix pipe never
+                // waits for a burst of reads.
+    #pragma unroll
+                for (int r = 0; r < kPairs; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                }
+                if constexpr (kReadsPerChunk > kPairs)
+                    __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerChunk - kPairs, 0);
+                if constexpr (kMfmaPerChunk > kPairs)
+                    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk - kPairs, 0);
+            }
+            if constexpr (STAGES == 3) {
+                if (t + 2 < nk) store_step(ahead);
+                if (t + 1 < nk) __syncthreads();
+            }
+            cur = nxt;
+        }
+
+        // accumulator register r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4,
+        // column l % 32 of its block
+        if constexpr (ILB > 1) {
+            // column block j of lane l32 is column ILB * l32 + j of the wave
+            const int gn = n0 + wn * WTN + ILB * l32;
+            const int gm0 = m0 + wm * WTM + 4 * half;
+            const bool vec_c = !GUARD && ((reinterpret_cast<uintptr_t>(C) |
+                                           static_cast<uintptr_t>(ldc * 4)) & (4 * ILB - 1)) == 0;
+            if (vec_c) {
+    #pragma unroll
+                for (int i = 0; i < FM; ++i)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float *row = C + static_cast<int64_t>(gm0 + i * 32 + 8 * (r / 4) + r % 4) * ldc + gn;
+                        if constexpr (ILB == 4)
+                            *reinterpret_cast<float4 *>(row) =
+                                make_float4(acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]);
+                        else
+                            *reinterpret_cast<float2 *>(row) = make_float2(acc[i][0][r], acc[i][1][r]);
+                    }
+            } else {
+    #pragma unroll
+                for (int i = 0; i < FM; ++i)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int gm = gm0 + i * 32 + 8 * (r / 4) + r % 4;
+                        float *row = C + static_cast<int64_t>(gm) * ldc + gn;
+    #pragma unroll
+                        for (int j = 0; j < ILB; ++j)
+                            if (!GUARD || (gm < M && gn + j < N)) row[j] = acc[i][j][r];
+                    }
+            }
+        } else {
+    #pragma unroll
+            for (int i = 0; i < FM; ++i) {
+    #pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int gn = n0 + wn * WTN + j * 32 + l32;
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int gm = m0 + wm * WTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                        if (!GUARD || (gm < M && gn < N))
+                            C[static_cast<int64_t>(gm) * ldc + gn] = acc[i][j][r];
+                    }
+                }
+            }
+        }
+    }
+};
+
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
           bool GUARD, bool VEC, bool TA, bool TB, bool IL>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n, int group_m, BatchArgs bt) {
-    constexpr int NT = 64 * WM * WN, NW = WM * WN;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int KC = BK / 8;  // chunks of 8 k per K-step
-    using TileA = OperandTile<BM, BK, PADA, TA, NT, NW, GUARD, VEC, DIRECT>;
-    constexpr int ILB = (IL && !TB) ? FN : 1;  // interleave of B's column blocks
-    using TileB = OperandTile<BN, BK, PADB, !TB, NT, NW, GUARD, VEC, DIRECT, ILB>;
-    constexpr int kReadsPerChunk = TileA::template reads<FM>() + TileB::template reads<FN>();
-    constexpr int kMfmaPerChunk = FM * FN * 4;
-    constexpr int kPairs = kReadsPerChunk < kMfmaPerChunk ? kReadsPerChunk : kMfmaPerChunk;
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32 x 32 blocks");
-    static_assert(BK % 16 == 0, "an even number of chunks per K-step");
-    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS buffers");
-    static_assert(STAGES * (TileA::SIZE + TileB::SIZE) * 4 <= kLdsBytes, "LDS budget of a workgroup");
+    // DIRECT and GUARD together: direct loads clamped at the M and N edges
+    // (see OperandTile) and guarded stores; K is whole K-steps.
+    using Full = RingTile<BM, BN, BK, WM, WN, PADA, PADB, STAGES, DIRECT, GUARD, VEC, TA, TB, IL>;
 
-    __shared__ __align__(16) float sA[STAGES][TileA::SIZE];
-    __shared__ __align__(16) float sB[STAGES][TileB::SIZE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
+    __shared__ __align__(16) float sA[STAGES][Full::TileA::SIZE];
+    __shared__ __align__(16) float sB[STAGES][Full::TileB::SIZE];
 
     int tm, tn;
     const int tile = batch_select(xcd_remap(blockIdx.x, tiles_m * tiles_n * bt.count),
                                   tiles_m * tiles_n, bt, A, B, C, K);
     grouped_tile(tile, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-
-    TileA ta;
-    TileB tb;
-    ta.init(A, lda, m0, M, tid, wave, lane);
-    tb.init(B, ldb, n0, N, tid, wave, lane);
-    auto load_step = [&](int k0, int buf) {
-        if constexpr (DIRECT) {
-            ta.load_direct(k0, sA[buf]);
-            tb.load_direct(k0, sB[buf]);
-        } else {
-            ta.load(k0, K);
-            tb.load(k0, K);
-        }
-    };
-    auto store_step = [&](int buf) {
-        if constexpr (!DIRECT) {
-            ta.store(sA[buf]);
-            tb.store(sB[buf]);
-        }
-    };
-
-    const int half = lane >> 5;
-    const int l32 = lane & 31;
-    ta.init_read(wm * WTM, half, l32);
-    tb.init_read(wn * WTN, half, l32);
-
-    // Two fragment register sets: operands of one chunk of 8 k.
-    float fa[2][FM][4];
-    float fb[2][FN][4];
-    auto read_frag = [&](int set, int buf, int kc) {
-        ta.template read<FM>(sA[buf], kc, fa[set]);
-        tb.template read<FN>(sB[buf], kc, fb[set]);
-    };
-
-    floatx16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    auto mfma_chunk = [&](int set) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[set][i][s], fb[set][j][s],
-                                                                     acc[i][j], 0, 0, 0);
-    };
-
-    const int nk = (K + BK - 1) / BK;
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st) {
-        if (st < nk) {
-            load_step(st * BK, st);
-            store_step(st);
-        }
-    }
-    __syncthreads();
-    read_frag(0, 0, 0);
-
-    int cur = 0;  // t mod STAGES
-    for (int t = 0; t < nk; ++t) {
-        const int nxt = cur == STAGES - 1 ? 0 : cur + 1;
-        const int ahead = cur == 0 ? STAGES - 1 : cur - 1;  // (t + STAGES - 1) mod STAGES
-        if (t + STAGES - 1 < nk) load_step((t + STAGES - 1) * BK, ahead);
-        // Branch-free so that the reads stay ahead of the MFMAs they feed
-        // (a branch here lets the compiler sink them back to their use).
-        //
-        // Three buffers: the last chunk reads ahead into step t + 1 (tile t + 1
-        // was published by the previous barrier); the barrier ends the step.
-        //
-        // Two buffers: the barrier sits before the last chunk.  By then the
-        // last chunk's fragments are in registers (so every read of buffer
-        // `cur` is done: write after read) and tile t + 1 has landed in buffer
-        // `nxt` (read after write), so right after the barrier the first
-        // fragments of step t + 1 are read while the last chunk's MFMAs run.
-        //
-        // In the last step the look-ahead read of buffer `nxt` is unused; it
-        // stays inside the buffer, which nobody writes after the barrier.
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            const int set = kc & 1;
-            if constexpr (STAGES == 2) {
-                if (kc == KC - 1) {
-                    store_step(nxt);  // register staging: stale but in-bounds in the last step
-                    // keep all of the previous chunk's MFMAs ahead of the
-                    // barrier: they cover the latency of the reads it waits for
-                    __builtin_amdgcn_sched_barrier(0);
-                    __syncthreads();
-                    read_frag(set ^ 1, nxt, 0);
-                } else {
-                    read_frag(set ^ 1, cur, kc + 1);
-                }
-            } else {
-                read_frag(set ^ 1, kc + 1 < KC ? cur : nxt, kc + 1 < KC ? kc + 1 : 0);
-            }
-            mfma_chunk(set);
-            // Issue order for the scheduler: the reads of the next chunk go
-            // out one per MFMA at the start of this chunk, so their latency
-            // hides behind the remaining MFMAs and the matrix pipe never
-            // waits for a burst of reads.
-#pragma unroll
-            for (int r = 0; r < kPairs; ++r) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-            }
-            if constexpr (kReadsPerChunk > kPairs)
-                __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerChunk - kPairs, 0);
-            if constexpr (kMfmaPerChunk > kPairs)
-                __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk - kPairs, 0);
-        }
-        if constexpr (STAGES == 3) {
-            if (t + 2 < nk) store_step(ahead);
-            if (t + 1 < nk) __syncthreads();
-        }
-        cur = nxt;
-    }
-
-    // accumulator register r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4,
-    // column l % 32 of its block
-    if constexpr (ILB > 1) {
-        // column block j of lane l32 is column ILB * l32 + j of the wave
-        const int gn = n0 + wn * WTN + ILB * l32;
-        const int gm0 = m0 + wm * WTM + 4 * half;
-        const bool vec_c = !GUARD && ((reinterpret_cast<uintptr_t>(C) |
-                                       static_cast<uintptr_t>(ldc * 4)) & (4 * ILB - 1)) == 0;
-        if (vec_c) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float *row = C + static_cast<int64_t>(gm0 + i * 32 + 8 * (r / 4) + r % 4) * ldc + gn;
-                    if constexpr (ILB == 4)
-                        *reinterpret_cast<float4 *>(row) =
-                            make_float4(acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]);
-                    else
-                        *reinterpret_cast<float2 *>(row) = make_float2(acc[i][0][r], acc[i][1][r]);
-                }
-        } else {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int gm = gm0 + i * 32 + 8 * (r / 4) + r % 4;
-                    float *row = C + static_cast<int64_t>(gm) * ldc + gn;
-#pragma unroll
-                    for (int j = 0; j < ILB; ++j)
-                        if (!GUARD || (gm < M && gn + j < N)) row[j] = acc[i][j][r];
-                }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int gn = n0 + wn * WTN + j * 32 + l32;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int gm = m0 + wm * WTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-                    if (!GUARD || (gm < M && gn < N))
-                        C[static_cast<int64_t>(gm) * ldc + gn] = acc[i][j][r];
-                }
-            }
-        }
-    }
+    Full::run(M, N, K, A, lda, B, ldb, C, ldc, m0, n0, sA, sB);
 }
 
 // PIPE = 0: the first kernel; PIPE = 2 or 3: the pipelined kernel with that
@@ -647,7 +677,8 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * p.batch;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool vec = rows_aligned16(p.A, p.lda, p.sa) && rows_aligned16(p.B, p.ldb, p.sb);
-    const bool guard = (p.M % BM) || (p.N % BN) || (p.K % BK);
+    const bool edge_mn = (p.M % BM) || (p.N % BN);
+    const bool edge_k = (p.K % BK) != 0;
     const dim3 g(static_cast<unsigned>(grid)), b(NT);
 #define GEMM_RING(D, G, V, TA, TB)                                                              \
     hipLaunchKernelGGL(                                                                         \
@@ -675,7 +706,14 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
                                stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,       \
                                tiles_m, tiles_n, GROUP_M, batch_of(p));                         \
     } while (0)
-    if (guard) {
+    // Ragged M or N only, aligned rows, direct-load configuration: direct
+    // loads clamped at the edges (k-major operand tiles need their row
+    // length, M for A transposed and N for B as stored, a multiple of 4).
+    constexpr bool kMixed = DIRECT && PIPE > 0;
+    const bool clamp_ok = (!p.ta || p.M % 4 == 0) && (p.tb || p.N % 4 == 0);
+    if (edge_mn && !edge_k && vec && clamp_ok && kMixed) {
+        if constexpr (kMixed) GEMM_RING_T(true, true, true);
+    } else if (edge_mn || edge_k) {
         if (vec) GEMM_MFMA_LAUNCH(false, true, true);
         else GEMM_MFMA_LAUNCH(false, true, false);
     } else {
@@ -724,6 +762,7 @@ const ConfigEntry kMfmaConfigs[] = {
     // Interleaved column blocks of B as stored (il): one 8- or 16-byte LDS
     // read per k for the wave's 2 or 4 column blocks, vector C stores.
     {"mfma2d_256x256x32_w4x4_swz_g4_il", launch_mfma<256, 256, 32, 4, 4, -1, 0, 4, 2, true, true, true>, kCapTransposed},
+    {"mfma2d_256x256x32_w4x4_swz_g8_il", launch_mfma<256, 256, 32, 4, 4, -1, 0, 8, 2, true, true, true>, kCapTransposed},
     {"mfma2d_256x256x32_w4x2_swz_g4_il", launch_mfma<256, 256, 32, 4, 2, -1, 0, 4, 2, true, true, true>, kCapTransposed},
     {"mfma2d_256x256x32_w2x4_swz_g4_il", launch_mfma<256, 256, 32, 2, 4, -1, 0, 4, 2, true, true, true>, kCapTransposed},
     {"mfma3d_256x128x32_w4x2_swz_il", launch_mfma<256, 128, 32, 4, 2, -1, 0, 8, 3, true, true, true>, kCapTransposed},

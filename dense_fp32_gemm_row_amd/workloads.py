@@ -29,6 +29,10 @@ Workloads (sizes are M x N x K; A is M x K, B is K x N, all row-major):
                      (A is 64 x M x K, B is 64 x K x N, drawn in that order)
   * ``deepk``        1024 x 1024 x 65536, uniform: few output tiles and a long
                      K, the shape that split-K serves
+  * ``square8000``   8000 x 8000 x 8000, uniform: a large product whose M and N
+                     are not whole 256-row tiles (rows still 16-byte aligned)
+  * ``square8191``   8191 x 8191 x 8191, uniform: no dimension a multiple of 4,
+                     so no row is 16-byte aligned
 """
 
 from __future__ import annotations
@@ -65,6 +69,8 @@ WORKLOADS: dict[str, Workload] = {
         Workload("ffn", 8192, 14336, 4096, "normal"),
         Workload("batched64_1024", 1024, 1024, 1024, "uniform", batch=64),
         Workload("deepk", 1024, 1024, 65536, "uniform"),
+        Workload("square8000", 8000, 8000, 8000, "uniform"),
+        Workload("square8191", 8191, 8191, 8191, "uniform"),
     )
 }
 

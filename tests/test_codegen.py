@@ -39,30 +39,37 @@ def mfma_asm(tmp_path_factory):
     return out.read_text()
 
 
-def loop_blocks(body: str) -> str:
-    """The blocks of the (single, innermost) K loop of a kernel, in layout
-    order: the block the compiler marks as loop header and every block it
-    marks as inside that loop."""
-    blocks, cur = [], []
-    for line in body.splitlines():
-        if re.match(r"^(\.LBB\S+:|; %bb\.\d+:)", line) and cur:
-            blocks.append(cur)
-            cur = []
-        cur.append(line)
-    blocks.append(cur)
-    header = None
-    for blk in blocks:
-        m = re.match(r"^\.L(BB\S+):.*Loop Header", blk[0])
+def loops(body: str) -> list[str]:
+    """The K loops of a kernel (a tile kernel with edge handling has two: one
+    with direct loads, one with register staging), as layout ranges: every
+    backward branch (to a label earlier in the code) closes a loop that spans
+    from its target to itself, and overlapping spans are one loop.  The
+    compiler's own loop comments are not used: a rotated loop whose entry
+    block is also reached from before the loop is not marked as inside it."""
+    lines = body.splitlines()
+    label_at = {}
+    for i, line in enumerate(lines):
+        m = re.match(r"^(\.LBB\S+):", line)
         if m:
-            header = m.group(1)
-    assert header, "no loop header found"
-    keep = [blk for blk in blocks
-            if blk[0].startswith(f".L{header}:") or f"Header={header} " in blk[0]]
-    return "\n".join(line for blk in keep for line in blk)
+            label_at[m.group(1)] = i
+    spans = []
+    for i, line in enumerate(lines):
+        m = re.match(r"^\s*s_(?:c)?branch\S*\s+(\.LBB\S+)", line)
+        if m and label_at.get(m.group(1), i + 1) < i:
+            spans.append([label_at[m.group(1)], i])
+    spans.sort()
+    merged = []
+    for a, b in spans:
+        if merged and a <= merged[-1][1]:
+            merged[-1][1] = max(merged[-1][1], b)
+        else:
+            merged.append([a, b])
+    assert merged, "no loop found"
+    return ["\n".join(lines[a:b + 1]) for a, b in merged]
 
 
 def ring_kernels(asm: str):
-    """(template arguments, K-loop blocks) of every pipelined kernel."""
+    """(template arguments, K loops) of every pipelined kernel."""
     names, bodies = [], []
     for m in re.finditer(r"^(_Z\S*gemm_mfma_ring_kernel\S*):[^\n]*\n(.*?)^\.Lfunc_end", asm,
                          re.S | re.M):
@@ -74,18 +81,20 @@ def ring_kernels(asm: str):
                          text=True).stdout.splitlines()
     for d, body in zip(dem, bodies):
         args = [a.strip() for a in d[d.index("<") + 1:d.index(">")].split(",")]
-        yield args, loop_blocks(body)
+        yield args, loops(body)
 
 
 def test_direct_load_kernels_wait_only_at_the_barrier(mfma_asm):
     checked = 0
-    for args, loop in ring_kernels(mfma_asm):
+    for args, kloops in ring_kernels(mfma_asm):
         # <BM, BN, BK, WM, WN, PADA, PADB, STAGES, DIRECT, GUARD, VEC, TA, TB, IL>
         if args[8] != "true":
             continue
-        lines = [ln.strip() for ln in loop.splitlines()]
-        waits = [k for k, ln in enumerate(lines) if ln.startswith("s_waitcnt") and "vmcnt" in ln]
         where = ", ".join(args)
+        direct = [lp for lp in kloops if "global_load_lds_dwordx4" in lp]
+        assert len(direct) == 1, f"<{where}>: {len(direct)} K loops with direct loads"
+        lines = [ln.strip() for ln in direct[0].splitlines()]
+        waits = [k for k, ln in enumerate(lines) if ln.startswith("s_waitcnt") and "vmcnt" in ln]
         assert len(waits) == 1, f"<{where}>: {len(waits)} waits on global loads in the K loop"
         k = waits[0]
         assert any(ln.startswith("s_barrier") for ln in lines[k + 1:k + 3]), \

@@ -135,6 +135,33 @@ def test_full_tiles(v, c, name):
     assert_exact(run(A, B, v, c, ldc_pad=1), oracle.gemm(A, B), name + " int4 odd ldc")
 
 
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_edge_tiles_with_whole_k_steps(v, c, name):
+    """M and N not whole tiles, K whole K-steps and 16-byte-aligned rows: the
+    direct-load configurations load the edge tiles directly too, with the
+    overhanging rows and columns clamped into the operands, and guard the
+    stores.  N = 774 (B rows padded to 776 floats) is not a multiple of 4, so
+    there the edge tiles fall back to guarded register staging."""
+    import torch
+
+    for N, bpad in ((776, 0), (774, 2)):
+        M, K = 520, 96
+        log(f"edge tiles {M}x{N}x{K} (B padding {bpad}) on {name}")
+        A, B = make_inputs(M, N, K, "int4", seed=17)
+        dB = torch.full((K, N + bpad), float("nan"), device="cuda:0")
+        dB[:, :N] = to_dev(B)
+        buf = torch.full((M, N + 4), float("nan"), device="cuda:0")
+        b.gemm(to_dev(A), dB[:, :N], buf[:, :N], variant=v, config=c)
+        assert bool(torch.isnan(buf[:, N:]).all()), "write outside C's columns"
+        assert_exact(to_host(buf[:, :N]), oracle.gemm(A, B), f"{name} int4 N={N}")
+        A, B = make_inputs(M, N, K, "uniform", seed=18)
+        dB[:, :N] = to_dev(B)
+        _, ref64 = oracle.gemm(A, B, return_f64=True)
+        out = torch.empty((M, N), device="cuda:0")
+        b.gemm(to_dev(A), dB[:, :N], out, variant=v, config=c)
+        assert_close(to_host(out), ref64, K, f"{name} uniform N={N}")
+
+
 # --------------------------------------------------------------------------
 # the small workloads in full, library choice and every MFMA configuration
 # --------------------------------------------------------------------------
@@ -268,7 +295,8 @@ BATCH_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4"), (1, 1, "lds_t32"),
                  (2, 0, "regblock_128x128x8_t8x8_pad4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in (
         "mfma_64x64x32_w2x2_pa4_pb0", "mfma_256x256x16_w2x4_pa4_pb0", "mfma3_256x256x16_w4x4_swz_pb0",
-        "mfma2p_256x256x32_w4x4_swz_pb0", "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz_g4")]
+        "mfma2p_256x256x32_w4x4_swz_pb0", "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz_g4",
+        "mfma2d_256x256x32_w2x4_swz_g4_il", "mfma2d_256x256x32_w4x4_swz_g4_il")]
 
 
 def _run_batched(A3, B3, M, N, K, nb, sa, sb, sc, lda, ldb, ldc, kernel):
@@ -334,12 +362,15 @@ def test_strided_batched(kernel, dist):
 
 
 @pytest.mark.parametrize("kernel", BATCH_KERNELS, ids=[k[2] for k in BATCH_KERNELS])
-def test_strided_batched_full_tiles(kernel):
-    """Whole tiles in every product (the unguarded and direct-load paths)."""
+@pytest.mark.parametrize("shape", [(512, 256, 64), (520, 264, 64)], ids=["whole", "edge"])
+def test_strided_batched_full_tiles(kernel, shape):
+    """Whole tiles in every product (the unguarded and direct-load paths),
+    and ragged M and N with whole K-steps (direct interior, guarded edges)."""
     import torch
 
-    log(f"batched full tiles on {kernel[2]}")
-    nb, M, N, K = 2, 512, 256, 64
+    log(f"batched {shape} on {kernel[2]}")
+    nb = 2
+    M, N, K = shape
     A, B = make_inputs(nb * M, N, K, "int4", seed=22)
     A3 = A.reshape(nb, M, K)
     B3 = np.stack([B, (B[::-1] * -1).copy()])
@@ -362,7 +393,7 @@ TRANS_CAPABLE = ["mfma2d_256x256x32_w4x4_swz", "mfma3d_256x128x32_w4x2_swz",
                  "mfma2d_256x256x32_w2x4_swz_g4_il", "mfma3d_256x128x32_w4x2_swz_il",
                  "mfma3d_128x256x16_w2x4_swz_il", "mfma3_64x128x16_w2x2_swz_il",
                  "mfma2d_256x256x32_w2x2_swz_g4_il", "mfma2d_256x256x32_w2x2_swz_g8_il",
-                 "mfma2d_256x256x32_w2x4_swz_g8_il"]
+                 "mfma2d_256x256x32_w2x4_swz_g8_il", "mfma2d_256x256x32_w4x4_swz_g8_il"]
 TRANS_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in TRANS_CAPABLE]
 OPS = ["NN", "NT", "TN", "TT"]
@@ -378,7 +409,8 @@ def _stored(X: np.ndarray, op: str):
 
 @pytest.mark.parametrize("kernel", TRANS_KERNELS, ids=[k[2] for k in TRANS_KERNELS])
 @pytest.mark.parametrize("ops", OPS)
-@pytest.mark.parametrize("shape", [(300, 277, 129), (512, 512, 96)], ids=["ragged", "full"])
+@pytest.mark.parametrize("shape", [(300, 277, 129), (512, 512, 96), (520, 776, 96)],
+                         ids=["ragged", "full", "edge"])
 def test_transposed_operands(kernel, ops, shape):
     import torch
 
@@ -497,7 +529,7 @@ def test_splitk_one_split_is_plain_product():
 # full-size workloads in the benchmark's launch configuration
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("wname", ["square4096", "square8192", "ffn"])
+@pytest.mark.parametrize("wname", ["square4096", "square8192", "ffn", "square8000", "square8191"])
 def test_full_size_sampled(wname):
     import torch
 
