@@ -141,11 +141,11 @@ def test_edge_tiles_with_whole_k_steps(v, c, name):
     direct-load configurations load the edge tiles directly too, with the
     overhanging rows and columns clamped into the operands, and guard the
     stores.  N = 774 (B rows padded to 776 floats) is not a multiple of 4, so
-    there the edge tiles fall back to guarded register staging."""
+    there the edge tiles fall back to guarded register staging; 3 x 8 clamps
+    almost every row and column of a tile."""
     import torch
 
-    for N, bpad in ((776, 0), (774, 2)):
-        M, K = 520, 96
+    for M, N, K, bpad in ((520, 776, 96, 0), (520, 774, 96, 2), (3, 8, 64, 0)):
         log(f"edge tiles {M}x{N}x{K} (B padding {bpad}) on {name}")
         A, B = make_inputs(M, N, K, "int4", seed=17)
         dB = torch.full((K, N + bpad), float("nan"), device="cuda:0")
