@@ -41,11 +41,17 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_fingerprint(config_name: str) -> str:
+def kernel_fingerprint(config_name: str, root: str = ROOT) -> str:
+    """Hash of the configuration name and of the MFMA kernel sources with
+    comments and whitespace removed: it changes when the compiled code can,
+    not when a comment does."""
     h = hashlib.sha256(config_name.encode())
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(root, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

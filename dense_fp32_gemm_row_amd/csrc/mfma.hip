@@ -20,6 +20,17 @@
 //  * Edge tiles ("Tiled GEMM: Matrix Multiplication in CUDA", section 7.1):
 //    out-of-range elements of A and B are loaded as 0.0 and the stores are
 //    guarded; shapes that are tile multiples compile without the checks.
+//    The pipelined kernel needs zero fill only past K: when K is whole
+//    K-steps, loads past M or N are clamped into the operand instead (they
+//    only feed outputs that are never stored), which keeps direct
+//    global-to-LDS loads for the edge tiles.
+//
+// This file holds two kernels: the first MFMA kernel (gemm_mfma_kernel,
+// register staging, two LDS buffers) and the pipelined one
+// (gemm_mfma_ring_kernel: a ring of two or three LDS buffers, fragment
+// prefetch, optional direct global-to-LDS loads, XOR-swizzled A rows,
+// interleaved B column blocks, transposed operands).  The table at the end
+// lists every compiled tile configuration.
 //
 // Operand layout.  For the 32x32x2 instruction lane l supplies A[l % 32][kk]
 // and B[kk][l % 32] with kk = l / 32, and accumulator register r of lane l
@@ -27,8 +38,9 @@
 // chunk of 8 k values the kernel feeds instruction s (s = 0..3) with
 // k = 4 * kk + s, a fixed permutation of the chunk applied to A and B alike,
 // so lane l needs the 4 consecutive values A[m][4 * kk .. 4 * kk + 3]: one
-// 16-byte LDS read per accumulator row block serves 4 instructions.  B is
-// read as single floats, 32 consecutive columns per half wavefront.
+// 16-byte LDS read per accumulator row block serves 4 instructions.  B, k-major
+// in LDS, is read as single floats, 32 consecutive columns per half wavefront
+// (or, with interleaved column blocks, as one 8- or 16-byte read per k).
 //
 // LDS padding ("Tiled GEMM: Matrix Multiplication in CUDA", section 7.2):
 // rows of the A tile are BK floats; lanes 0..31 read 16 bytes each from 32
