@@ -321,19 +321,22 @@ struct OperandTile {
         }
     }
 
-    // Register staging of the tile of K-step starting at k0.
+    // Register staging of the tile of K-step starting at k0 (G: with zero
+    // fill outside the operand; the direct-load kernels use it for a
+    // partial last K-step).
+    template <bool G = GUARD>
     __device__ __forceinline__ void load(int k0, int K) {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             if constexpr (KMAJOR) {
                 const int gk = k0 + ro[i];
-                const bool ok = !GUARD || gk < K;
+                const bool ok = !G || gk < K;
                 const float *row = X + static_cast<int64_t>(ok ? gk : 0) * ld + r0;
-                reg[i] = load_row4<GUARD, VEC>(row, co[i], rlim - r0, ok);
+                reg[i] = load_row4<G, VEC>(row, co[i], rlim - r0, ok);
             } else {
-                const bool ok = !GUARD || r0 + ro[i] < rlim;
+                const bool ok = !G || r0 + ro[i] < rlim;
                 const float *row = X + static_cast<int64_t>(ok ? r0 + ro[i] : 0) * ld;
-                reg[i] = load_row4<GUARD, VEC>(row, k0 + co[i], K, ok);
+                reg[i] = load_row4<G, VEC>(row, k0 + co[i], K, ok);
             }
         }
     }
@@ -515,26 +518,31 @@ struct RingTile {
         };
 
         floatx16 acc[FM][FN];
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < FM; ++i)
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < FN; ++j)
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
         auto mfma_chunk = [&](int set) {
-    #pragma unroll
+#pragma unroll
             for (int s = 0; s < 4; ++s)
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < FM; ++i)
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < FN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[set][i][s], fb[set][j][s],
                                                                          acc[i][j], 0, 0, 0);
         };
 
-        const int nk = (K + BK - 1) / BK;
-    #pragma unroll
+        // Direct loads move whole K-steps only; a partial last K-step is
+        // the tail below.  (Spelled as the rounded-up count minus the tail:
+        // with K / BK as the trip count the compiler recomputed the global
+        // addresses with a 64-bit multiply every K-step instead of advancing
+        // them, and the 16-wave kernels lost 11%.)
+        const int nk = (K + BK - 1) / BK - (DIRECT && (K % BK) ? 1 : 0);
+#pragma unroll
         for (int st = 0; st < STAGES - 1; ++st) {
             if (st < nk) {
                 load_step(st * BK, st);
@@ -563,7 +571,7 @@ struct RingTile {
             //
             // In the last step the look-ahead read of buffer `nxt` is unused; it
             // stays inside the buffer, which nobody writes after the barrier.
-    #pragma unroll
+#pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const int set = kc & 1;
                 if constexpr (STAGES == 2) {
@@ -585,7 +593,7 @@ struct RingTile {
                 // out one per MFMA at the start of this chunk, so their latency
                 // hides behind the remaining MFMAs and the matrix pipe never
                 // waits for a burst of reads.
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < kPairs; ++r) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
@@ -602,6 +610,27 @@ struct RingTile {
             cur = nxt;
         }
 
+        // Tail of the direct-load kernels: the partial last K-step, staged
+        // through registers with zero fill past K (and past the M / N edges),
+        // once all waves are done with the loop's buffers.  One exposed
+        // global-load latency per tile; its registers are not live in the
+        // loop.
+        if constexpr (DIRECT) {
+            if (K % BK) {
+                ta.template load<true>(nk * BK, K);
+                tb.template load<true>(nk * BK, K);
+                __syncthreads();
+                ta.store(sA[0]);
+                tb.store(sB[0]);
+                __syncthreads();
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    read_frag(0, 0, kc);
+                    mfma_chunk(0);
+                }
+            }
+        }
+
         // accumulator register r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4,
         // column l % 32 of its block
         if constexpr (ILB > 1) {
@@ -611,9 +640,9 @@ struct RingTile {
             const bool vec_c = !GUARD && ((reinterpret_cast<uintptr_t>(C) |
                                            static_cast<uintptr_t>(ldc * 4)) & (4 * ILB - 1)) == 0;
             if (vec_c) {
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < FM; ++i)
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float *row = C + static_cast<int64_t>(gm0 + i * 32 + 8 * (r / 4) + r % 4) * ldc + gn;
                         if constexpr (ILB == 4)
@@ -623,24 +652,24 @@ struct RingTile {
                             *reinterpret_cast<float2 *>(row) = make_float2(acc[i][0][r], acc[i][1][r]);
                     }
             } else {
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < FM; ++i)
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int gm = gm0 + i * 32 + 8 * (r / 4) + r % 4;
                         float *row = C + static_cast<int64_t>(gm) * ldc + gn;
-    #pragma unroll
+#pragma unroll
                         for (int j = 0; j < ILB; ++j)
                             if (!GUARD || (gm < M && gn + j < N)) row[j] = acc[i][j][r];
                     }
             }
         } else {
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < FM; ++i) {
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     const int gn = n0 + wn * WTN + j * 32 + l32;
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int gm = m0 + wm * WTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
                         if (!GUARD || (gm < M && gn < N))
@@ -718,19 +747,24 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
                                stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,       \
                                tiles_m, tiles_n, GROUP_M, batch_of(p));                         \
     } while (0)
-    // Ragged M or N only, aligned rows, direct-load configuration: direct
-    // loads clamped at the edges (k-major operand tiles need their row
-    // length, M for A transposed and N for B as stored, a multiple of 4).
-    constexpr bool kMixed = DIRECT && PIPE > 0;
-    const bool clamp_ok = (!p.ta || p.M % 4 == 0) && (p.tb || p.N % 4 == 0);
-    if (edge_mn && !edge_k && vec && clamp_ok && kMixed) {
-        if constexpr (kMixed) GEMM_RING_T(true, true, true);
-    } else if (edge_mn || edge_k) {
-        if (vec) GEMM_MFMA_LAUNCH(false, true, true);
-        else GEMM_MFMA_LAUNCH(false, true, false);
-    } else {
+    // Direct-load configurations with aligned rows keep direct loads for
+    // any shape: loads past M or N are clamped into the operands (GUARD:
+    // guarded stores; k-major operand tiles need their row length, M for A
+    // transposed and N for B as stored, a multiple of 4), and a partial last
+    // K-step is staged at the end of the K loop.
+    constexpr bool kDirectAny = DIRECT && PIPE > 0;
+    const bool clamp_ok = !edge_mn || ((!p.ta || p.M % 4 == 0) && (p.tb || p.N % 4 == 0));
+    if (!edge_mn && !edge_k) {
         if (vec) GEMM_MFMA_LAUNCH(DIRECT, false, true);
         else GEMM_MFMA_LAUNCH(false, false, false);
+    } else if (kDirectAny && vec && clamp_ok) {
+        if constexpr (kDirectAny) {
+            if (edge_mn) GEMM_RING_T(true, true, true);
+            else GEMM_RING_T(true, false, true);
+        }
+    } else {
+        if (vec) GEMM_MFMA_LAUNCH(false, true, true);
+        else GEMM_MFMA_LAUNCH(false, true, false);
     }
 #undef GEMM_MFMA_LAUNCH
 #undef GEMM_RING_T
@@ -780,8 +814,6 @@ const ConfigEntry kMfmaConfigs[] = {
     {"mfma3d_256x128x32_w4x2_swz_il", launch_mfma<256, 128, 32, 4, 2, -1, 0, 8, 3, true, true, true>, kCapTransposed},
     {"mfma3d_128x256x16_w2x4_swz_il", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3, true, true, true>, kCapTransposed},
     {"mfma3_64x128x16_w2x2_swz_il", launch_mfma<64, 128, 16, 2, 2, -1, 0, 8, 3, false, true, true>, kCapTransposed},
-    {"mfma2d_256x256x32_w2x2_swz_g4_il", launch_mfma<256, 256, 32, 2, 2, -1, 0, 4, 2, true, true, true>, kCapTransposed},
-    {"mfma2d_256x256x32_w2x2_swz_g8_il", launch_mfma<256, 256, 32, 2, 2, -1, 0, 8, 2, true, true, true>, kCapTransposed},
     {"mfma2d_256x256x32_w2x4_swz_g8_il", launch_mfma<256, 256, 32, 2, 4, -1, 0, 8, 2, true, true, true>, kCapTransposed},
 };
 

@@ -33,6 +33,8 @@ Workloads (sizes are M x N x K; A is M x K, B is K x N, all row-major):
                      are not whole 256-row tiles (rows still 16-byte aligned)
   * ``square8191``   8191 x 8191 x 8191, uniform: no dimension a multiple of 4,
                      so no row is 16-byte aligned
+  * ``ktail8100``    8192 x 8192 x 8100, uniform: K is not a whole number of
+                     32-k steps, rows are 16-byte aligned
 """
 
 from __future__ import annotations
@@ -71,6 +73,7 @@ WORKLOADS: dict[str, Workload] = {
         Workload("deepk", 1024, 1024, 65536, "uniform"),
         Workload("square8000", 8000, 8000, 8000, "uniform"),
         Workload("square8191", 8191, 8191, 8191, "uniform"),
+        Workload("ktail8100", 8192, 8192, 8100, "uniform"),
     )
 }
 

@@ -1,6 +1,10 @@
 """Code-generation checks of the MFMA kernels (CPU only: hipcc cross-compiles
 gfx950 assembly without a GPU).
 
+Two properties of the direct-load K loops are checked, both found by
+measurement to matter: where the loop waits on global loads, and that it
+advances its global addresses instead of recomputing them.
+
 Direct global -> LDS loads of K-step t + 1 (or t + 2) land in a buffer that
 step t does not read.  The compiler only knows that through the alias scopes
 it gives each LDS array, and those scopes reach loads only a few address
@@ -99,5 +103,9 @@ def test_direct_load_kernels_wait_only_at_the_barrier(mfma_asm):
         k = waits[0]
         assert any(ln.startswith("s_barrier") for ln in lines[k + 1:k + 3]), \
             f"<{where}>: the wait on global loads is not right before the barrier"
+        # the per-step global addresses advance by increments; a multiply per
+        # K-step here cost the 16-wave kernels 11%
+        muls = [ln for ln in lines if ln.startswith(("s_mul_i32", "s_mul_hi_u32"))]
+        assert not muls, f"<{where}>: address multiplies in the K loop: {muls[:3]}"
         checked += 1
     assert checked >= 10, f"only {checked} direct-load kernels found"

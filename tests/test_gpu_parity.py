@@ -135,17 +135,26 @@ def test_full_tiles(v, c, name):
     assert_exact(run(A, B, v, c, ldc_pad=1), oracle.gemm(A, B), name + " int4 odd ldc")
 
 
+EDGE_CASES = [  # M, N, K, padding of B's rows
+    (520, 776, 96, 0),   # M and N edges, whole K-steps
+    (520, 774, 96, 2),   # N not a multiple of 4 (B rows padded to 16 bytes)
+    (3, 8, 64, 0),       # almost every row and column of a tile clamped
+    (512, 512, 72, 0),   # whole tiles, partial last K-step
+    (520, 776, 100, 0),  # edges and a partial last K-step
+    (256, 256, 20, 0),   # K shorter than one K-step
+]
+
+
 @pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
-def test_edge_tiles_with_whole_k_steps(v, c, name):
-    """M and N not whole tiles, K whole K-steps and 16-byte-aligned rows: the
-    direct-load configurations load the edge tiles directly too, with the
-    overhanging rows and columns clamped into the operands, and guard the
-    stores.  N = 774 (B rows padded to 776 floats) is not a multiple of 4, so
-    there the edge tiles fall back to guarded register staging; 3 x 8 clamps
-    almost every row and column of a tile."""
+def test_edge_tiles_and_k_tail(v, c, name):
+    """16-byte-aligned rows with M or N not whole tiles and/or K not whole
+    K-steps.  The direct-load configurations keep direct loads: loads past M
+    or N are clamped into the operands (the stores are guarded) and a partial
+    last K-step is staged through registers with zero fill.  N = 774 is not a
+    multiple of 4, so there the edge tiles fall back to register staging."""
     import torch
 
-    for M, N, K, bpad in ((520, 776, 96, 0), (520, 774, 96, 2), (3, 8, 64, 0)):
+    for M, N, K, bpad in EDGE_CASES:
         log(f"edge tiles {M}x{N}x{K} (B padding {bpad}) on {name}")
         A, B = make_inputs(M, N, K, "int4", seed=17)
         dB = torch.full((K, N + bpad), float("nan"), device="cuda:0")
@@ -153,13 +162,13 @@ def test_edge_tiles_with_whole_k_steps(v, c, name):
         buf = torch.full((M, N + 4), float("nan"), device="cuda:0")
         b.gemm(to_dev(A), dB[:, :N], buf[:, :N], variant=v, config=c)
         assert bool(torch.isnan(buf[:, N:]).all()), "write outside C's columns"
-        assert_exact(to_host(buf[:, :N]), oracle.gemm(A, B), f"{name} int4 N={N}")
+        assert_exact(to_host(buf[:, :N]), oracle.gemm(A, B), f"{name} int4 {M}x{N}x{K}")
         A, B = make_inputs(M, N, K, "uniform", seed=18)
         dB[:, :N] = to_dev(B)
         _, ref64 = oracle.gemm(A, B, return_f64=True)
         out = torch.empty((M, N), device="cuda:0")
         b.gemm(to_dev(A), dB[:, :N], out, variant=v, config=c)
-        assert_close(to_host(out), ref64, K, f"{name} uniform N={N}")
+        assert_close(to_host(out), ref64, K, f"{name} uniform {M}x{N}x{K}")
 
 
 # --------------------------------------------------------------------------
@@ -362,7 +371,8 @@ def test_strided_batched(kernel, dist):
 
 
 @pytest.mark.parametrize("kernel", BATCH_KERNELS, ids=[k[2] for k in BATCH_KERNELS])
-@pytest.mark.parametrize("shape", [(512, 256, 64), (520, 264, 64)], ids=["whole", "edge"])
+@pytest.mark.parametrize("shape", [(512, 256, 64), (520, 264, 64), (520, 264, 84)],
+                         ids=["whole", "edge", "edge_ktail"])
 def test_strided_batched_full_tiles(kernel, shape):
     """Whole tiles in every product (the unguarded and direct-load paths),
     and ragged M and N with whole K-steps (direct interior, guarded edges)."""
@@ -392,7 +402,6 @@ TRANS_CAPABLE = ["mfma2d_256x256x32_w4x4_swz", "mfma3d_256x128x32_w4x2_swz",
                  "mfma2d_256x256x32_w4x4_swz_g4_il", "mfma2d_256x256x32_w4x2_swz_g4_il",
                  "mfma2d_256x256x32_w2x4_swz_g4_il", "mfma3d_256x128x32_w4x2_swz_il",
                  "mfma3d_128x256x16_w2x4_swz_il", "mfma3_64x128x16_w2x2_swz_il",
-                 "mfma2d_256x256x32_w2x2_swz_g4_il", "mfma2d_256x256x32_w2x2_swz_g8_il",
                  "mfma2d_256x256x32_w2x4_swz_g8_il", "mfma2d_256x256x32_w4x4_swz_g8_il"]
 TRANS_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in TRANS_CAPABLE]
@@ -409,8 +418,9 @@ def _stored(X: np.ndarray, op: str):
 
 @pytest.mark.parametrize("kernel", TRANS_KERNELS, ids=[k[2] for k in TRANS_KERNELS])
 @pytest.mark.parametrize("ops", OPS)
-@pytest.mark.parametrize("shape", [(300, 277, 129), (512, 512, 96), (520, 776, 96)],
-                         ids=["ragged", "full", "edge"])
+@pytest.mark.parametrize("shape", [(300, 277, 129), (512, 512, 96), (520, 776, 96),
+                                   (520, 776, 100)],
+                         ids=["ragged", "full", "edge", "edge_ktail"])
 def test_transposed_operands(kernel, ops, shape):
     import torch
 
@@ -529,7 +539,8 @@ def test_splitk_one_split_is_plain_product():
 # full-size workloads in the benchmark's launch configuration
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("wname", ["square4096", "square8192", "ffn", "square8000", "square8191"])
+@pytest.mark.parametrize("wname", ["square4096", "square8192", "ffn", "square8000", "square8191",
+                                   "ktail8100"])
 def test_full_size_sampled(wname):
     import torch
 
