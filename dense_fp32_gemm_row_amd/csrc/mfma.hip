@@ -20,10 +20,11 @@
 //  * Edge tiles ("Tiled GEMM: Matrix Multiplication in CUDA", section 7.1):
 //    out-of-range elements of A and B are loaded as 0.0 and the stores are
 //    guarded; shapes that are tile multiples compile without the checks.
-//    The pipelined kernel needs zero fill only past K: when K is whole
-//    K-steps, loads past M or N are clamped into the operand instead (they
-//    only feed outputs that are never stored), which keeps direct
-//    global-to-LDS loads for the edge tiles.
+//    The pipelined kernel keeps direct global-to-LDS loads for them: with
+//    16-byte-aligned rows, loads past M or N are clamped into the operand
+//    (they only feed outputs that are never stored) and a partial last
+//    K-step is staged through registers; without aligned rows, 4-byte
+//    buffer loads return zero for every element outside the operand.
 //
 // This file holds two kernels: the first MFMA kernel (gemm_mfma_kernel,
 // register staging, two LDS buffers) and the pipelined one
@@ -242,6 +243,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
 //    floats, 32 consecutive r per half wavefront.
 // Register staging (with zero fill outside the matrix) and direct
 // global -> LDS loads are provided for both.
+// Whether an R x BK operand tile loaded by NW wavefronts can use 4-byte
+// direct loads (see OperandTile): whole 256-byte chunks per wavefront, and a
+// chunk stride that keeps the row flavour's swizzle (whole 32-row blocks) or
+// the k-major flavour's columns (whole rows) fixed.
+constexpr bool dw_tile_ok(int R, int BK, int NW, bool kmajor) {
+    return (R * BK / 64) % NW == 0 &&
+           (kmajor ? (64 * NW) % R == 0 : (64 * NW) % BK == 0 && ((64 * NW) / BK) % 32 == 0);
+}
+
 template <int R, int BK, int PAD, bool KMAJOR, int NT, int NW, bool GUARD, bool VEC, bool DIRECT,
           int IL = 1>
 struct OperandTile {
@@ -253,7 +263,21 @@ struct OperandTile {
     static constexpr int S = BK / 4;                                     // 16-byte slots per row
     static constexpr int LOG2S = S == 2 ? 1 : S == 4 ? 2 : S == 8 ? 3 : 4;
     static constexpr int CH = R * BK / 256;                              // 1 KiB chunks
-    static constexpr int J = DIRECT ? CH / NW : 1;
+    // Direct loads come in two kinds.  With 16-byte-aligned rows (VEC) one
+    // global_load_lds_dwordx4 moves 1 KiB.  Without (DW) one 4-byte buffer
+    // load into LDS moves 256 bytes, a float per lane, and a lane whose
+    // element lies outside the operand (past K or past the R extent) gets an
+    // offset outside the buffer's range, which the hardware's range check
+    // turns into zero: zero fill with no registers, for edge tiles and a
+    // partial last K-step alike.  A wavefront's successive 256-byte chunks
+    // are NW chunks apart, which must keep the row flavour's swizzle (whole
+    // 32-row blocks) and the k-major flavour's columns (whole rows) fixed.
+    static constexpr bool DW = DIRECT && !VEC;
+    static constexpr int CHW = R * BK / 64;                              // 256-byte chunks
+    static constexpr int DW_STEP = KMAJOR ? 64 * NW / R : 64 * NW / BK;  // rows between them
+    static constexpr bool DW_OK = dw_tile_ok(R, BK, NW, KMAJOR);
+    static constexpr int J = DIRECT && !DW ? CH / NW : 1;
+    static constexpr int JW = DW ? CHW / NW : 1;
     static_assert(L * 4 * NT == R * BK, "even tile split");
     static_assert(LD % 4 == 0, "16-byte aligned LDS rows");
     // Direct loads need unpadded LDS rows and 16-byte-aligned global rows.
@@ -262,8 +286,9 @@ struct OperandTile {
     // instead of zero fill their loads are clamped onto the last valid row
     // (row flavour) or 16-byte group (k-major flavour, which needs the R
     // extent to be a multiple of 4).  K must be whole K-steps.
-    static_assert(!DIRECT || (PAD <= 0 && VEC), "direct loads: unpadded tiles, aligned rows");
-    static_assert(!DIRECT || CH % NW == 0, "whole chunks per wavefront");
+    static_assert(!DIRECT || PAD <= 0, "direct loads: unpadded tiles");
+    static_assert(!DIRECT || DW || CH % NW == 0, "whole chunks per wavefront");
+    static_assert(!DW || DW_OK, "4-byte direct loads: chunk stride keeps swizzle and columns");
 
     // XOR swizzle of the row flavour: slot q of row m is stored at slot
     // q ^ g(m), g(m) = (r ^ (r >> log2 S)) mod S with r = m mod 32.  A
@@ -283,6 +308,9 @@ struct OperandTile {
     float4 reg[L];
     const float *src[J];
     int dst[J];
+    __amdgpu_buffer_rsrc_t rsrc;  // DW: the operand as a buffer
+    int dw_off, dw_lim, dw_row;   // DW: lane's element offset, k row (k-major) or k column
+                                  // (row flavour), and row of the first chunk (row flavour)
 
     __device__ __forceinline__ void init(const float *X_, int64_t ld_, int r0_, int rlim_, int tid,
                                          int wave, int lane) {
@@ -300,7 +328,25 @@ struct OperandTile {
                 st[i] = ro[i] * LD + (SWZ ? ((co[i] / 4) ^ swz(ro[i])) * 4 : co[i]);
             }
         }
-        if constexpr (DIRECT) {
+        if constexpr (DW) {
+            // range up to 2^31 - 1 bytes: every valid offset is below it (the
+            // launcher checks the operand's span), 0x80000000 is outside
+            rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(X_), 0, 0x7fffffff,
+                                                     0x00020000);
+            const int f = wave * 64 + lane;  // float offset of the lane in its first chunk
+            if constexpr (KMAJOR) {
+                const int kr = f / R, col = f % R;
+                dw_off = kr * static_cast<int>(ld_) + r0_ + col;
+                dw_lim = r0_ + col < rlim_ ? kr : 0x40000000;  // k row; out-of-range column: never valid
+            } else {
+                const int m = f / BK;
+                const int kc = 4 * (((f % BK) / 4) ^ swz(m)) + f % 4;
+                dw_off = (r0_ + m) * static_cast<int>(ld_) + kc;
+                dw_lim = kc;
+                dw_row = r0_ + m;
+            }
+        }
+        if constexpr (DIRECT && !DW) {
 #pragma unroll
             for (int j = 0; j < J; ++j) {
                 const int c = wave + j * NW;
@@ -349,13 +395,32 @@ struct OperandTile {
     // 64 x 16 bytes into 1 KiB of contiguous LDS, lane L's 16 bytes at offset
     // 16 L; each lane fetches the element that belongs at its slot (for the
     // row flavour, the inverse of the swizzle).
-    __device__ __forceinline__ void load_direct(int k0, float *buf) const {
+    __device__ __forceinline__ void load_direct(int k0, int K, float *buf) const {
         typedef const __attribute__((address_space(1))) void *gptr_t;
         typedef __attribute__((address_space(3))) void *lptr_t;
+        if constexpr (DW) {
+            const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const float *g = KMAJOR ? src[j] + static_cast<int64_t>(k0) * ld : src[j] + k0;
-            __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)(&buf[dst[j]]), 16, 0, 0);
+            for (int j = 0; j < JW; ++j) {
+                int off;
+                bool ok;
+                if constexpr (KMAJOR) {  // chunk j holds k rows DW_STEP * j further on
+                    off = dw_off + (k0 + j * DW_STEP) * static_cast<int>(ld);
+                    ok = dw_lim + j * DW_STEP + k0 < K;
+                } else {                 // ... rows DW_STEP * j further down
+                    off = dw_off + j * DW_STEP * static_cast<int>(ld) + k0;
+                    ok = dw_row + j * DW_STEP < rlim && dw_lim + k0 < K;
+                }
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (lptr_t)(&buf[(wave + j * NW) * 64]), 4,
+                    ok ? off * 4 : static_cast<int>(0x80000000u), 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const float *g = KMAJOR ? src[j] + static_cast<int64_t>(k0) * ld : src[j] + k0;
+                __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)(&buf[dst[j]]), 16, 0, 0);
+            }
         }
     }
 
@@ -490,8 +555,8 @@ struct RingTile {
         tb.init(B, ldb, n0, N, tid, wave, lane);
         auto load_step = [&](int k0, int buf) {
             if constexpr (DIRECT) {
-                ta.load_direct(k0, sA[buf]);
-                tb.load_direct(k0, sB[buf]);
+                ta.load_direct(k0, K, sA[buf]);
+                tb.load_direct(k0, K, sB[buf]);
             } else {
                 ta.load(k0, K);
                 tb.load(k0, K);
@@ -541,7 +606,7 @@ struct RingTile {
         // with K / BK as the trip count the compiler recomputed the global
         // addresses with a 64-bit multiply every K-step instead of advancing
         // them, and the 16-wave kernels lost 11%.)
-        const int nk = (K + BK - 1) / BK - (DIRECT && (K % BK) ? 1 : 0);
+        const int nk = (K + BK - 1) / BK - (DIRECT && VEC && (K % BK) ? 1 : 0);
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st) {
             if (st < nk) {
@@ -615,7 +680,7 @@ struct RingTile {
         // once all waves are done with the loop's buffers.  One exposed
         // global-load latency per tile; its registers are not live in the
         // loop.
-        if constexpr (DIRECT) {
+        if constexpr (DIRECT && VEC) {
             if (K % BK) {
                 ta.template load<true>(nk * BK, K);
                 tb.template load<true>(nk * BK, K);
@@ -747,6 +812,32 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
                                stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,       \
                                tiles_m, tiles_n, GROUP_M, batch_of(p));                         \
     } while (0)
+    // Rows not 16-byte aligned: 4-byte direct loads with range-checked zero
+    // fill, where the tile shape allows it and every element offset (with a
+    // tile's overhang) stays below 2^29 floats, the buffers' 32-bit range.
+    if constexpr (DIRECT && PIPE > 0) {
+        constexpr int NW = WM * WN;
+        const int64_t a_rows = p.ta ? p.K : p.M, a_cols = p.ta ? p.M : p.K;
+        const int64_t b_rows = p.tb ? p.N : p.K, b_cols = p.tb ? p.K : p.N;
+        constexpr int64_t kSpan = int64_t{1} << 29;
+        const bool spans_ok = (a_rows + 256) * p.lda + a_cols + 256 < kSpan &&
+                              (b_rows + 256) * p.ldb + b_cols + 256 < kSpan;
+        if (!vec && spans_ok) {
+#define GEMM_DW(TA_, TB_)                                                                       \
+    if constexpr ((TRANS || (!TA_ && !TB_)) && dw_tile_ok(BM, BK, NW, TA_) &&                   \
+                  dw_tile_ok(BN, BK, NW, !TB_)) {                                               \
+        if (p.ta == TA_ && p.tb == TB_) {                                                       \
+            GEMM_RING(true, true, false, TA_, TB_);                                             \
+            return hipGetLastError();                                                           \
+        }                                                                                       \
+    }
+            GEMM_DW(false, false)
+            GEMM_DW(false, true)
+            GEMM_DW(true, false)
+            GEMM_DW(true, true)
+#undef GEMM_DW
+        }
+    }
     // Direct-load configurations with aligned rows keep direct loads for
     // any shape: loads past M or N are clamped into the operands (GUARD:
     // guarded stores; k-major operand tiles need their row length, M for A

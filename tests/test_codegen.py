@@ -95,7 +95,8 @@ def test_direct_load_kernels_wait_only_at_the_barrier(mfma_asm):
         if args[8] != "true":
             continue
         where = ", ".join(args)
-        direct = [lp for lp in kloops if "global_load_lds_dwordx4" in lp]
+        direct = [lp for lp in kloops
+                  if "global_load_lds_dwordx4" in lp or re.search(r"buffer_load_dword .* lds", lp)]
         assert len(direct) == 1, f"<{where}>: {len(direct)} K loops with direct loads"
         lines = [ln.strip() for ln in direct[0].splitlines()]
         waits = [k for k, ln in enumerate(lines) if ln.startswith("s_waitcnt") and "vmcnt" in ln]
