@@ -203,9 +203,16 @@ int validate(bool ta, bool tb, int64_t batch, int64_t M, int64_t N, int64_t K, c
 }
 
 // The tile configuration gemm_f32 uses for a shape: an exact entry of the
-// tuned table if there is one, else the rule-based choice below.
+// tuned table if there is one, else the cost model's choice.  The model
+// ("Tiling and Blocking for Reuse", choosing the tile size: reuse against
+// occupancy and tails, settled by measurement): a CU receives
+// n = ceil(tiles / CUs) tiles of a candidate and runs up to nrates of them
+// at once at the measured per-CU rate for that many, so the predicted time
+// is n * 2 * bm * bn * K / rate; rows that are not 16-byte aligned scale
+// the rate by the candidate's measured factor.  A batch multiplies the
+// tiles.  Transposed operands consider only configurations that take them.
 void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant, int *config,
-                   bool trans = false) {
+                   bool trans = false, bool aligned = true) {
     if (batch == 1 && !trans) {
         for (const TuneEntry &e : kTuneTable) {
             if (e.M == M && e.N == N && e.K == K) {
@@ -218,17 +225,30 @@ void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant,
             }
         }
     }
-    // Rules: 256 x 256 tiles once they give every CU of the chip one; 128-row
-    // tiles while 128 x 128 tiles still do; small tiles for small or ragged
-    // problems.  A batch multiplies the number of tiles.
-    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256) * batch;
-    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128) * batch;
-    const char *name = trans ? kTransposedSmall : kDefaultSmall;
-    if (t256 >= 256) name = trans ? kTransposedLarge : kDefaultLarge;
-    else if (t128 >= 256) name = trans ? kTransposedMedium : kDefaultMedium;
+    int count = 0;
+    const ConfigEntry *cfgs = configs_of(GEMM_F32_VARIANT_MFMA, &count);
+    int best = -1;
+    double best_t = 0.0;
+    for (const ModelCandidate &m : kModel) {
+        const int id = find_config(GEMM_F32_VARIANT_MFMA, m.config);
+        if (id < 0 || (trans && !(cfgs[id].caps & kCapTransposed))) continue;
+        const int64_t tiles = ((M + m.bm - 1) / m.bm) * ((N + m.bn - 1) / m.bn) * batch;
+        const int64_t n = (tiles + kModelCUs - 1) / kModelCUs;
+        const int conc = static_cast<int>(n < m.nrates ? n : m.nrates);
+        const double rate = m.gflops_per_cu[conc > 0 ? conc - 1 : 0] * (aligned ? 1.0 : m.unaligned);
+        const double t = static_cast<double>(n) * m.bm * m.bn * static_cast<double>(K) / rate;
+        if (best < 0 || t < best_t) best = id, best_t = t;
+    }
     *variant = GEMM_F32_VARIANT_MFMA;
-    *config = find_config(GEMM_F32_VARIANT_MFMA, name);
-    if (*config < 0) *config = 0;
+    *config = best >= 0 ? best : 0;
+}
+
+// Rows of A and B 16-byte aligned in every product (the direct-load kernels'
+// fast path).
+bool operands_aligned(const float *A, int64_t lda, int64_t sa, const float *B, int64_t ldb,
+                      int64_t sb) {
+    return reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(B) % 16 == 0 &&
+           lda % 4 == 0 && ldb % 4 == 0 && sa % 4 == 0 && sb % 4 == 0;
 }
 
 int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, int64_t N,
@@ -239,7 +259,8 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
     if (variant == -1) {  // the library's choice
         int rc = validate_sizes(M, N, K, lda, ldb, ldc, ta, tb);
         if (rc != GEMM_F32_OK) return rc;
-        select_config(batch > 0 ? batch : 1, M, N, K, &variant, &config_id, ta || tb);
+        select_config(batch > 0 ? batch : 1, M, N, K, &variant, &config_id, ta || tb,
+                      operands_aligned(A, lda, sa, B, ldb, sb));
     }
     const ConfigEntry *cfgs = configs_of(variant, &count);
     if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant);
@@ -257,7 +278,8 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
     } else {
         if (config_id == -1) {
             int v = 0;
-            select_config(batch, M, N, K, &v, &config_id, ta || tb);
+            select_config(batch, M, N, K, &v, &config_id, ta || tb,
+                          operands_aligned(A, lda, sa, B, ldb, sb));
             if (v != variant) {  // first configuration of the asked variant that fits
                 config_id = 0;
                 if (ta || tb)
@@ -371,13 +393,14 @@ int gemm_f32_splitk(int variant, int config_id, int64_t splits, int64_t M, int64
         return fail(GEMM_F32_EINVAL, "workspace overlaps A, B or C");
     // partial products: a strided batch over the K splits into the workspace
     int v = variant, c = config_id;
-    if (v == -1) select_config(used, M, N, len, &v, &c);
+    const bool aligned = operands_aligned(A, lda, len, B, ldb, static_cast<int64_t>(len) * ldb);
+    if (v == -1) select_config(used, M, N, len, &v, &c, false, aligned);
     int count = 0;
     const ConfigEntry *cfgs = configs_of(v, &count);
     if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", v);
     if (c == -1) {
         int vv = 0;
-        select_config(used, M, N, len, &vv, &c);
+        select_config(used, M, N, len, &vv, &c, false, aligned);
         if (vv != v) c = 0;
     }
     if (c < 0 || c >= count)
@@ -454,7 +477,7 @@ int gemm_f32_select(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, i
     if (rc != GEMM_F32_OK) return rc;
     if (variant == nullptr || config_id == nullptr)
         return fail(GEMM_F32_EINVAL, "NULL output pointer");
-    select_config(1, M, N, K, variant, config_id);
+    select_config(1, M, N, K, variant, config_id, false, lda % 4 == 0 && ldb % 4 == 0);
     return GEMM_F32_OK;
 }
 

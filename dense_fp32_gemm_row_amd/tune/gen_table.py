@@ -42,13 +42,26 @@ def render(table: dict) -> str:
     lines += [
         '    {-1, -1, -1, 3, ""},',
         "};",
-        f'constexpr const char *kDefaultLarge = "{table["default_large"]}";',
-        f'constexpr const char *kDefaultMedium = "{table["default_medium"]}";',
-        f'constexpr const char *kDefaultSmall = "{table["default_small"]}";',
-        "// configurations for transposed operands (they must accept them)",
-        f'constexpr const char *kTransposedLarge = "{table["transposed_large"]}";',
-        f'constexpr const char *kTransposedMedium = "{table["transposed_medium"]}";',
-        f'constexpr const char *kTransposedSmall = "{table["transposed_small"]}";',
+        "// Cost model for shapes not listed (see tune/table.json): per-CU",
+        "// throughput of each candidate with 1, 2, ... of its tiles on a CU.",
+        "struct ModelCandidate {",
+        "    const char *config;",
+        "    int bm, bn, nrates;",
+        "    float gflops_per_cu[4];",
+        "    float unaligned;",
+        "};",
+        f'constexpr int kModelCUs = {int(table["model"]["cus"])};',
+        "constexpr ModelCandidate kModel[] = {",
+    ]
+    for c in table["model"]["candidates"]:
+        rates = [float(x) for x in c["gflops_per_cu"]]
+        if not 1 <= len(rates) <= 4:
+            raise ValueError(f"{c['config']}: 1 to 4 rates")
+        padded = ", ".join(f"{x:.1f}f" for x in rates + [rates[-1]] * (4 - len(rates)))
+        lines.append(f'    {{"{c["config"]}", {int(c["bm"])}, {int(c["bn"])}, {len(rates)}, '
+                     f'{{{padded}}}, {float(c["unaligned"]):.3f}f}},')
+    lines += [
+        "};",
         "}  // namespace gemm_f32_impl",
         "",
     ]

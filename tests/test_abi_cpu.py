@@ -138,12 +138,32 @@ def test_tuning_table_names_compiled_configs(lib):
 
     table = json.load(open(os.path.join(ROOT, "dense_fp32_gemm_row_amd", "tune", "table.json")))
     names = {n for v in range(4) for n in b.config_names(v)}
-    for key in ("default_large", "default_medium", "default_small"):
-        assert table[key] in names, f"{key} names unknown configuration {table[key]}"
+    for c in table["model"]["candidates"]:
+        assert c["config"] in names, f"model candidate names unknown configuration {c['config']}"
+        assert c["config"].startswith("mfma")
+        assert 1 <= len(c["gflops_per_cu"]) <= 4 and 0 < c["unaligned"] <= 1
     for e in table["entries"]:
         assert e["config"] in names, f"table entry {e} names an unknown configuration"
         v, c = b.gemm_f32_select(e["M"], e["N"], e["K"], e["K"], e["N"], e["N"])
         assert b.gemm_f32_config_name(v, c) == e["config"]
+
+
+def test_cost_model_choices(lib):
+    """The cost model's choice on shapes not in the table: small products
+    get small tiles, a product that fills the chip many times over the
+    largest tile, and wave quantisation is accounted for (3072^3: 144 tiles
+    of 256^2 would leave 112 CUs idle)."""
+    def pick(M, N, K, lda=None, ldb=None):
+        v, c = b.gemm_f32_select(M, N, K, lda or K, ldb or N, N)
+        return b.gemm_f32_config_name(v, c)
+
+    assert pick(512, 512, 512).startswith("mfma_64x64")
+    assert pick(8192, 8192, 8192 + 64) == "mfma2d_256x256x32_w4x4_swz_g4_il"
+    assert "64x64" in pick(3072, 3072, 3072)
+    assert pick(8192, 1024, 4096).startswith("mfma3d_256x128")
+    # the same shape with rows that are not 16-byte aligned may choose differently,
+    # but always a compiled configuration
+    assert pick(4096, 4096, 4095, 4095, 4096) in {n for n in b.config_names(3)}
 
 
 def test_generated_table_matches_json():
