@@ -66,8 +66,10 @@ extern "C" {
 
 /*
  * gemm_f32 -- C = A x B with the kernel and tile configuration the library
- * selects for the shape (a built-in table tuned by measurement on MI355X,
- * "Tiling and Blocking for Reuse", "choosing the tile size").
+ * selects for the shape ("Tiling and Blocking for Reuse", "choosing the tile
+ * size"): a built-in table of shapes tuned by measurement on MI355X, and for
+ * other shapes a cost model whose per-CU rates were measured there (it
+ * accounts for how many tiles each CU receives and runs at once).
  *
  *   M, N, K    sizes, 0 <= M, N, K <= 2^31 - 1
  *   A, lda     M x K operand, lda >= max(1, K)
