@@ -171,6 +171,40 @@ def test_edge_tiles_and_k_tail(v, c, name):
         assert_close(to_host(out), ref64, K, f"{name} uniform {M}x{N}x{K}")
 
 
+@pytest.fixture(scope="module")
+def huge_strided():
+    """Operands whose rows lie more than 2^31 floats apart from the start:
+    A has 3 rows lda = 2^30 + 64 floats apart, B 64 rows ldb = 2^25 + 4
+    floats apart (about 21 GB of device memory, only the used rows written)."""
+    import torch
+
+    M, N, K = 3, 8, 64
+    lda, ldb = (1 << 30) + 64, (1 << 25) + 4
+    A, B = make_inputs(M, N, K, "int4", seed=41)
+    bufA = torch.empty((M - 1) * lda + K, dtype=torch.float32, device="cuda:0")
+    bufB = torch.empty((K - 1) * ldb + N, dtype=torch.float32, device="cuda:0")
+    dA = bufA.as_strided((M, K), (lda, 1))
+    dB = bufB.as_strided((K, N), (ldb, 1))
+    dA.copy_(to_dev(A))
+    dB.copy_(to_dev(B))
+    yield A, B, dA, dB
+    del dA, dB, bufA, bufB
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_offsets_beyond_2_31(v, c, name, huge_strided):
+    """Element offsets above 2^31 in A and in B: 64-bit row offsets in every
+    kernel."""
+    import torch
+
+    A, B, dA, dB = huge_strided
+    log(f"offsets beyond 2^31 on {name}")
+    out = torch.full((A.shape[0], B.shape[1]), float("nan"), device="cuda:0")
+    b.gemm(dA, dB, out, variant=v, config=c)
+    assert_exact(to_host(out), oracle.gemm(A, B), name)
+
+
 # --------------------------------------------------------------------------
 # the small workloads in full, library choice and every MFMA configuration
 # --------------------------------------------------------------------------
