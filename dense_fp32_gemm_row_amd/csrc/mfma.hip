@@ -515,7 +515,9 @@ struct OperandTile {
 // blocks: lane l32 of block j owns column FN l32 + j of the wave's columns
 // instead of 32 j + l32.  A lane's B values of one k are then FN adjacent
 // floats, one LDS read instead of FN / 2 two-address reads, and its
-// outputs in one row are FN adjacent floats, one vector store.
+// outputs in one row are FN adjacent floats, one vector store.  Likewise
+// for A's row blocks when A's tile is k-major (A transposed) and B's is
+// too: row block i of lane l32 is row FM l32 + i.
 // One output tile of the pipelined kernel: the K loop and the epilogue for
 // the tile at (m0, n0), with the LDS buffers of the workgroup.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
@@ -525,7 +527,13 @@ struct RingTile {
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int KC = BK / 8;  // chunks of 8 k per K-step
-    using TileA = OperandTile<BM, BK, PADA, TA, NT, NW, GUARD, VEC, DIRECT>;
+    // Interleave of A's row blocks: only when B's tile is k-major as well.
+    // With A transposed and B transposed (TT) it issued a third fewer LDS
+    // reads for the same LDS busy cycles, the waves waited longer to issue
+    // them, and MFMA busy fell from 93.3% to 91.2% (TT 146.8 -> 142.8
+    // TFLOP/s, same box); with B as stored (TN) it gains 1.3%.
+    static constexpr int ILA = (IL && TA && !TB) ? FM : 1;
+    using TileA = OperandTile<BM, BK, PADA, TA, NT, NW, GUARD, VEC, DIRECT, ILA>;
     static constexpr int ILB = (IL && !TB) ? FN : 1;  // interleave of B's column blocks
     using TileB = OperandTile<BN, BK, PADB, !TB, NT, NW, GUARD, VEC, DIRECT, ILB>;
     static constexpr int kReadsPerChunk = TileA::template reads<FM>() + TileB::template reads<FN>();
@@ -697,19 +705,25 @@ struct RingTile {
         }
 
         // accumulator register r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4,
-        // column l % 32 of its block
+        // column l % 32 of its block; with interleaved row blocks (ILA) row
+        // rho of block i is row ILA * rho + i of the wave, else 32 i + rho
+        const int wrow0 = m0 + wm * WTM;
+        auto row_of = [&](int i, int r) {
+            const int rho = 8 * (r / 4) + 4 * half + r % 4;
+            return wrow0 + (ILA > 1 ? ILA * rho + i : 32 * i + rho);
+        };
         if constexpr (ILB > 1) {
             // column block j of lane l32 is column ILB * l32 + j of the wave
             const int gn = n0 + wn * WTN + ILB * l32;
-            const int gm0 = m0 + wm * WTM + 4 * half;
-            const bool vec_c = !GUARD && ((reinterpret_cast<uintptr_t>(C) |
-                                           static_cast<uintptr_t>(ldc * 4)) & (4 * ILB - 1)) == 0;
+            const bool vec_c = (!GUARD || (m0 + BM <= M && n0 + BN <= N)) &&
+                               ((reinterpret_cast<uintptr_t>(C) | static_cast<uintptr_t>(ldc * 4)) &
+                                (4 * ILB - 1)) == 0;
             if (vec_c) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        float *row = C + static_cast<int64_t>(gm0 + i * 32 + 8 * (r / 4) + r % 4) * ldc + gn;
+                        float *row = C + static_cast<int64_t>(row_of(i, r)) * ldc + gn;
                         if constexpr (ILB == 4)
                             *reinterpret_cast<float4 *>(row) =
                                 make_float4(acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]);
@@ -721,7 +735,7 @@ struct RingTile {
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int gm = gm0 + i * 32 + 8 * (r / 4) + r % 4;
+                        const int gm = row_of(i, r);
                         float *row = C + static_cast<int64_t>(gm) * ldc + gn;
 #pragma unroll
                         for (int j = 0; j < ILB; ++j)
@@ -736,7 +750,7 @@ struct RingTile {
                     const int gn = n0 + wn * WTN + j * 32 + l32;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int gm = m0 + wm * WTM + i * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+                        const int gm = row_of(i, r);
                         if (!GUARD || (gm < M && gn < N))
                             C[static_cast<int64_t>(gm) * ldc + gn] = acc[i][j][r];
                     }
