@@ -9,6 +9,17 @@ The build turns that table into the dispatch table of gemm_f32.
 
     python -m dense_fp32_gemm_row_amd.tune.autotune --out tuned.json
 
+With --calibrate it also measures the cost model that gemm_f32 uses for
+shapes not in the table: every candidate of the table's "model" section runs
+on the calibration shapes below, and for each shape a CU's share is
+n = ceil(tiles / cus) tiles, run min(n, len(gflops_per_cu)) at a time; the
+per-CU rate 2 * bm * bn * K * n / (time - launch floor) is collected by that
+concurrency, and each entry of gflops_per_cu becomes the median of its
+group.  `unaligned` is the median ratio of the rate on shapes whose rows are
+not 16-byte aligned to the aligned rate at the same concurrency.
+
+    python -m dense_fp32_gemm_row_amd.tune.autotune --out tuned.json --calibrate
+
 Correctness of every configuration is established separately by the parity
 tests; this script only measures.
 """
@@ -39,6 +50,68 @@ DEFAULT_SHAPES = [
     # one tiny product: the floor of one timed launch
     ("tiny", 1, 1, 1),
 ]
+
+
+# calibration shapes of the cost model: every one runs long enough (K up to
+# 8192 for the small tile counts) that the host-side launch floor, 7 to 20 us
+# depending on the host, stays a small correction; squares over the sizes
+# where the candidates trade places, a few rectangular products, and shapes
+# whose rows are not 16-byte aligned (K or N not a multiple of 4)
+CAL_SHAPES = ([(n, n, 8192) for n in (512, 768, 1024, 1280, 1536, 1792)] +
+              [(n, n, n) for n in (2048, 2560, 3072, 3584, 4096, 5120, 6144, 8192)] +
+              [(1024, 8192, 8192), (8192, 1024, 4096), (2048, 2048, 8192), (4096, 2048, 1024),
+               (3000, 3000, 3000)])
+CAL_UNALIGNED = [(1000, 1023, 7777), (2049, 2049, 2049), (3001, 3001, 3001)]
+
+
+def calibrate_model(binding, model: dict, budget_ms: float) -> dict:
+    """Measured per-CU rates of the model's candidates (see the module doc)."""
+    import math
+    import statistics
+
+    import torch
+
+    cus = int(model["cus"])
+    times: dict[tuple, float] = {}
+    for M, N, K in CAL_SHAPES + CAL_UNALIGNED + [(1, 1, 1)]:
+        g = torch.Generator(device="cuda").manual_seed(0)
+        dA = torch.rand((M, K), device="cuda", generator=g)
+        dB = torch.rand((K, N), device="cuda", generator=g)
+        dC = torch.empty((M, N), device="cuda")
+        for cand in model["candidates"]:
+            cfg = cand["config"]
+
+            def call(cfg=cfg):
+                binding.gemm(dA, dB, dC, variant="mfma", config=cfg)
+
+            times[(cfg, M, N, K)] = time_fn(call, budget_ms)
+            print(json.dumps({"calibrate": cfg, "M": M, "N": N, "K": K,
+                              "median_ms": round(times[(cfg, M, N, K)], 5)}), flush=True)
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+    out = {"cus": cus, "candidates": []}
+    for cand in model["candidates"]:
+        cfg, bm, bn = cand["config"], int(cand["bm"]), int(cand["bn"])
+        occ = len(cand["gflops_per_cu"])
+        floor = times[(cfg, 1, 1, 1)]
+
+        def rate(M, N, K):
+            tiles = math.ceil(M / bm) * math.ceil(N / bn)
+            n = math.ceil(tiles / cus)
+            ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
+            return min(n, occ), 2.0 * bm * bn * K * n / (ms * 1e-3) / 1e9
+
+        groups: dict[int, list[float]] = {}
+        for shape in CAL_SHAPES:
+            conc, r = rate(*shape)
+            groups.setdefault(conc, []).append(r)
+        rates = []
+        for conc in range(1, occ + 1):  # a level with no shape inherits the one below
+            rates.append(round(statistics.median(groups[conc]), 1) if conc in groups else rates[-1])
+        ratios = [r / rates[conc - 1] for conc, r in (rate(*s) for s in CAL_UNALIGNED)]
+        out["candidates"].append({**cand, "gflops_per_cu": rates,
+                                  "unaligned": round(min(1.0, statistics.median(ratios)), 3)})
+    return out
 
 
 def time_config(binding, v, c, dA, dB, dC, reps, warmup):
@@ -95,6 +168,8 @@ def main() -> int:
     ap.add_argument("--shapes", default=",".join(s[0] for s in DEFAULT_SHAPES))
     ap.add_argument("--budget-ms", type=float, default=400.0,
                     help="approximate timed milliseconds per configuration")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also re-measure the cost model's per-CU rates (written to --out)")
     ap.add_argument("--splits", default="",
                     help="comma-separated split counts: also time gemm_f32_splitk with each "
                          "(reported, not written to the table)")
@@ -151,6 +226,8 @@ def main() -> int:
         del dA, dB, dC
         torch.cuda.empty_cache()
     table["entries"] = sorted(entries.values(), key=lambda e: (e["M"], e["N"], e["K"]))
+    if args.calibrate:
+        table["model"] = calibrate_model(binding, table["model"], min(args.budget_ms, 200.0))
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     with open(args.out, "w") as f:
         json.dump(table, f, indent=2)
