@@ -30,8 +30,9 @@
 // register staging, two LDS buffers) and the pipelined one
 // (gemm_mfma_ring_kernel: a ring of two or three LDS buffers, fragment
 // prefetch, optional direct global-to-LDS loads, XOR-swizzled A rows,
-// interleaved B column blocks, transposed operands).  The table at the end
-// lists every compiled tile configuration.
+// interleaved B column blocks, transposed operands, and k-groups that share
+// each K-step between groups of wavefronts).  The table at the end lists
+// every compiled tile configuration.
 //
 // Operand layout.  For the 32x32x2 instruction lane l supplies A[l % 32][kk]
 // and B[kk][l % 32] with kk = l / 32, and accumulator register r of lane l
@@ -245,12 +246,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
 // global -> LDS loads are provided for both.
 // Whether an R x BK operand tile loaded by NW wavefronts can use 4-byte
 // direct loads (see OperandTile): whole 256-byte chunks per wavefront, and a
-// chunk stride that keeps the row flavour's swizzle (whole 32-row blocks) or
-// the k-major flavour's columns (whole rows) fixed.
+// chunk stride of whole rows, which keeps a lane's column fixed (the k-major
+// flavour) or cycles it through a few swizzled positions (the row flavour).
 constexpr bool dw_tile_ok(int R, int BK, int NW, bool kmajor) {
-    return (R * BK / 64) % NW == 0 &&
-           (kmajor ? (64 * NW) % R == 0 : (64 * NW) % BK == 0 && ((64 * NW) / BK) % 32 == 0);
+    return (R * BK / 64) % NW == 0 && (kmajor ? (64 * NW) % R == 0 : (64 * NW) % BK == 0);
 }
+constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
 
 template <int R, int BK, int PAD, bool KMAJOR, int NT, int NW, bool GUARD, bool VEC, bool DIRECT,
           int IL = 1>
@@ -270,14 +271,17 @@ struct OperandTile {
     // offset outside the buffer's range, which the hardware's range check
     // turns into zero: zero fill with no registers, for edge tiles and a
     // partial last K-step alike.  A wavefront's successive 256-byte chunks
-    // are NW chunks apart, which must keep the row flavour's swizzle (whole
-    // 32-row blocks) and the k-major flavour's columns (whole rows) fixed.
+    // are NW chunks apart, DW_STEP whole rows: a lane keeps its column in the
+    // k-major flavour, and in the row flavour its element's k column follows
+    // the row's swizzle, which repeats every 32 rows (DW_P chunks).
     static constexpr bool DW = DIRECT && !VEC;
     static constexpr int CHW = R * BK / 64;                              // 256-byte chunks
     static constexpr int DW_STEP = KMAJOR ? 64 * NW / R : 64 * NW / BK;  // rows between them
     static constexpr bool DW_OK = dw_tile_ok(R, BK, NW, KMAJOR);
     static constexpr int J = DIRECT && !DW ? CH / NW : 1;
     static constexpr int JW = DW ? CHW / NW : 1;
+    static constexpr int DW_P = KMAJOR || !DW_OK ? 1 : 32 / gcd(DW_STEP, 32);
+    static constexpr int DW_NC = DW_P < JW ? DW_P : JW;  // distinct k columns of a lane
     static_assert(L * 4 * NT == R * BK, "even tile split");
     static_assert(LD % 4 == 0, "16-byte aligned LDS rows");
     // Direct loads need unpadded LDS rows and 16-byte-aligned global rows.
@@ -309,8 +313,9 @@ struct OperandTile {
     const float *src[J];
     int dst[J];
     __amdgpu_buffer_rsrc_t rsrc;  // DW: the operand as a buffer
-    int dw_off, dw_lim, dw_row;   // DW: lane's element offset, k row (k-major) or k column
-                                  // (row flavour), and row of the first chunk (row flavour)
+    int dw_off, dw_lim, dw_row;   // DW: lane's element offset (row flavour: of its row), k row
+                                  // (k-major) and row of the first chunk (row flavour)
+    int dw_kc[DW_NC];             // DW, row flavour: k column in chunks j = p mod DW_P
 
     __device__ __forceinline__ void init(const float *X_, int64_t ld_, int r0_, int rlim_, int tid,
                                          int wave, int lane) {
@@ -339,10 +344,14 @@ struct OperandTile {
                 dw_off = kr * static_cast<int>(ld_) + r0_ + col;
                 dw_lim = r0_ + col < rlim_ ? kr : 0x40000000;  // k row; out-of-range column: never valid
             } else {
+                // the lane's LDS position in chunk j is row m + j DW_STEP,
+                // physical column f % BK, which holds the logical column
+                // given by that row's swizzle
                 const int m = f / BK;
-                const int kc = 4 * (((f % BK) / 4) ^ swz(m)) + f % 4;
-                dw_off = (r0_ + m) * static_cast<int>(ld_) + kc;
-                dw_lim = kc;
+#pragma unroll
+                for (int p = 0; p < DW_NC; ++p)
+                    dw_kc[p] = 4 * (((f % BK) / 4) ^ swz(m + p * DW_STEP)) + f % 4;
+                dw_off = (r0_ + m) * static_cast<int>(ld_);
                 dw_row = r0_ + m;
             }
         }
@@ -408,8 +417,9 @@ struct OperandTile {
                     off = dw_off + (k0 + j * DW_STEP) * static_cast<int>(ld);
                     ok = dw_lim + j * DW_STEP + k0 < K;
                 } else {                 // ... rows DW_STEP * j further down
-                    off = dw_off + j * DW_STEP * static_cast<int>(ld) + k0;
-                    ok = dw_row + j * DW_STEP < rlim && dw_lim + k0 < K;
+                    const int kc = dw_kc[j % DW_P];
+                    off = dw_off + j * DW_STEP * static_cast<int>(ld) + kc + k0;
+                    ok = dw_row + j * DW_STEP < rlim && kc + k0 < K;
                 }
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rsrc, (lptr_t)(&buf[(wave + j * NW) * 64]), 4,
@@ -432,14 +442,16 @@ struct OperandTile {
     // for the LDS arrays only reach that far, and without them it cannot tell
     // these reads from the direct loads of the other buffer and waits for
     // those loads before every K-step.
+    // `kb`: first chunk of 8 k that the wave reads (its k-group's share of
+    // the K-step); chunk indices passed to read() count from there.
     int rd, rg, rh;
-    __device__ __forceinline__ void init_read(int rbase, int half, int l32) {
+    __device__ __forceinline__ void init_read(int rbase, int half, int l32, int kb = 0) {
         if constexpr (KMAJOR) {
-            rd = 4 * half * LD + rbase + IL * l32;
+            rd = 4 * half * LD + rbase + IL * l32 + kb * 8 * LD;
         } else {
             rd = (rbase + l32) * LD;
             rg = SWZ ? swz(l32) : 0;
-            rh = half;
+            rh = half + 2 * kb;  // slot 2 (kb + kc) + half, before the swizzle
         }
         asm("" : "+v"(rd));
     }
@@ -518,15 +530,26 @@ struct OperandTile {
 // outputs in one row are FN adjacent floats, one vector store.  Likewise
 // for A's row blocks when A's tile is k-major (A transposed) and B's is
 // too: row block i of lane l32 is row FM l32 + i.
+//
+// KG > 1: K-groups.  The workgroup holds KG groups of WM x WN wavefronts
+// that all load each K-step's tiles together, but each group multiplies
+// only its own BK / KG slice of the step (group g: chunks of 8 k
+// g KC .. g KC + KC - 1), into accumulators for the whole tile.  The
+// groups' partial tiles are then added in LDS, group 0 + group 1 + ...,
+// a fixed order, and group 0 stores the sum.  For shapes with about one
+// tile per CU this puts KG times more wavefronts on each SIMD to hide
+// load and LDS latency, with no extra launch or workspace.
+//
 // One output tile of the pipelined kernel: the K loop and the epilogue for
 // the tile at (m0, n0), with the LDS buffers of the workgroup.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
-          bool GUARD, bool VEC, bool TA, bool TB, bool IL>
+          bool GUARD, bool VEC, bool TA, bool TB, bool IL, int KG = 1>
 struct RingTile {
-    static constexpr int NT = 64 * WM * WN, NW = WM * WN;
+    static constexpr int NWG = WM * WN;  // wavefronts per k-group
+    static constexpr int NW = NWG * KG, NT = 64 * NW;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
-    static constexpr int KC = BK / 8;  // chunks of 8 k per K-step
+    static constexpr int KC = BK / 8 / KG;  // chunks of 8 k per K-step and k-group
     // Interleave of A's row blocks: only when B's tile is k-major as well.
     // With A transposed and B transposed (TT) it issued a third fewer LDS
     // reads for the same LDS busy cycles, the waves waited longer to issue
@@ -540,7 +563,8 @@ struct RingTile {
     static constexpr int kMfmaPerChunk = FM * FN * 4;
     static constexpr int kPairs = kReadsPerChunk < kMfmaPerChunk ? kReadsPerChunk : kMfmaPerChunk;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32 x 32 blocks");
-    static_assert(BK % 16 == 0, "an even number of chunks per K-step");
+    static_assert(BK % (16 * KG) == 0, "an even number of chunks per K-step and k-group");
+    static_assert(NT <= 1024, "at most 16 wavefronts per workgroup");
     static_assert(STAGES == 2 || STAGES == 3, "two or three LDS buffers");
     static_assert(STAGES * (TileA::SIZE + TileB::SIZE) * 4 <= kLdsBytes, "LDS budget of a workgroup");
 
@@ -555,7 +579,8 @@ struct RingTile {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int wm = wave / WN, wn = wave % WN;
+        const int kg = wave / NWG, wg = wave % NWG;  // k-group, wavefront within it
+        const int wm = wg / WN, wn = wg % WN;
 
         TileA ta;
         TileB tb;
@@ -579,8 +604,8 @@ struct RingTile {
 
         const int half = lane >> 5;
         const int l32 = lane & 31;
-        ta.init_read(wm * WTM, half, l32);
-        tb.init_read(wn * WTN, half, l32);
+        ta.init_read(wm * WTM, half, l32, kg * KC);
+        tb.init_read(wn * WTN, half, l32, kg * KC);
 
         // Two fragment register sets: operands of one chunk of 8 k.
         float fa[2][FM][4];
@@ -704,6 +729,44 @@ struct RingTile {
             }
         }
 
+        if constexpr (KG > 1) {
+            // Sum of the k-groups' partial tiles, in group order, through the
+            // A buffers (every wavefront is done with them after the first
+            // barrier): CAP groups per round write their accumulators, one
+            // 256-byte row per register, and group 0 adds them.
+            constexpr int PER_WAVE = FM * FN * 16 * 64;
+            constexpr int CAP = (STAGES * TileA::SIZE) / (NWG * PER_WAVE);
+            static_assert(CAP >= 1, "LDS room for one partial tile");
+            float *red = &sA[0][0];
+#pragma unroll
+            for (int g0 = 1; g0 < KG; g0 += CAP) {
+                __syncthreads();
+                if (kg >= g0 && kg < g0 + CAP) {
+                    float *p = red + ((kg - g0) * NWG + wg) * PER_WAVE + lane;
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) p[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
+                }
+                __syncthreads();
+                if (kg == 0) {
+#pragma unroll
+                    for (int g = 0; g < CAP && g0 + g < KG; ++g) {
+                        const float *p = red + (g * NWG + wg) * PER_WAVE + lane;
+#pragma unroll
+                        for (int i = 0; i < FM; ++i)
+#pragma unroll
+                            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) acc[i][j][r] += p[((i * FN + j) * 16 + r) * 64];
+                    }
+                }
+            }
+            if (kg != 0) return;
+        }
+
         // accumulator register r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4,
         // column l % 32 of its block; with interleaved row blocks (ILA) row
         // rho of block i is row ILA * rho + i of the wave, else 32 i + rho
@@ -761,14 +824,14 @@ struct RingTile {
 };
 
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
-          bool GUARD, bool VEC, bool TA, bool TB, bool IL>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
+          bool GUARD, bool VEC, bool TA, bool TB, bool IL, int KG>
+__global__ __launch_bounds__(64 * WM * WN * KG) void gemm_mfma_ring_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n, int group_m, BatchArgs bt) {
     // DIRECT and GUARD together: direct loads clamped at the M and N edges
     // (see OperandTile) and guarded stores; K is whole K-steps.
-    using Full = RingTile<BM, BN, BK, WM, WN, PADA, PADB, STAGES, DIRECT, GUARD, VEC, TA, TB, IL>;
+    using Full = RingTile<BM, BN, BK, WM, WN, PADA, PADB, STAGES, DIRECT, GUARD, VEC, TA, TB, IL, KG>;
 
     __shared__ __align__(16) float sA[STAGES][Full::TileA::SIZE];
     __shared__ __align__(16) float sB[STAGES][Full::TileB::SIZE];
@@ -786,12 +849,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_ring_kernel(
 // allows (full tiles, 16-byte-aligned rows), register staging otherwise.
 // TRANS: also compiled for transposed operands (pipelined kernel only).
 // IL: interleaved column blocks for B as stored (pipelined kernel only).
+// KG: k-groups of WM x WN wavefronts (pipelined kernel only).
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int GROUP_M, int PIPE,
-          bool DIRECT = false, bool TRANS = false, bool IL = false>
+          bool DIRECT = false, bool TRANS = false, bool IL = false, int KG = 1>
 hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     static_assert(!TRANS || PIPE > 0, "transposed operands need the pipelined kernel");
     static_assert(!IL || PIPE > 0, "interleaved blocks need the pipelined kernel");
-    constexpr int NT = 64 * WM * WN;
+    static_assert(KG == 1 || PIPE > 0, "k-groups need the pipelined kernel");
+    constexpr int NT = 64 * WM * WN * KG;
     if ((p.ta || p.tb) && !TRANS) return hipErrorNotSupported;
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
     const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * p.batch;
@@ -802,8 +867,8 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     const dim3 g(static_cast<unsigned>(grid)), b(NT);
 #define GEMM_RING(D, G, V, TA, TB)                                                              \
     hipLaunchKernelGGL(                                                                         \
-        (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, D, G, V, TA, TB, IL>), g, b, \
-        0,                                                                                      \
+        (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, D, G, V, TA, TB, IL, KG>), g, \
+        b, 0,                                                                                   \
         stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, GROUP_M,   \
         batch_of(p))
 #define GEMM_RING_T(D, G, V)                                                                    \
@@ -830,7 +895,7 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     // fill, where the tile shape allows it and every element offset (with a
     // tile's overhang) stays below 2^29 floats, the buffers' 32-bit range.
     if constexpr (DIRECT && PIPE > 0) {
-        constexpr int NW = WM * WN;
+        constexpr int NW = WM * WN * KG;
         const int64_t a_rows = p.ta ? p.K : p.M, a_cols = p.ta ? p.M : p.K;
         const int64_t b_rows = p.tb ? p.N : p.K, b_cols = p.tb ? p.K : p.N;
         constexpr int64_t kSpan = int64_t{1} << 29;
@@ -920,6 +985,11 @@ const ConfigEntry kMfmaConfigs[] = {
     {"mfma3d_128x256x16_w2x4_swz_il", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3, true, true, true>, kCapTransposed},
     {"mfma3_64x128x16_w2x2_swz_il", launch_mfma<64, 128, 16, 2, 2, -1, 0, 8, 3, false, true, true>, kCapTransposed},
     {"mfma2d_256x256x32_w2x4_swz_g8_il", launch_mfma<256, 256, 32, 2, 4, -1, 0, 8, 2, true, true, true>, kCapTransposed},
+    // K-groups (k4: four groups of 2 x 2 wavefronts, 16 per workgroup, each
+    // group a quarter of every K-step): for shapes with about one tile per CU.
+    {"mfma2d_64x64x128_w2x2_k4_swz", launch_mfma<64, 64, 128, 2, 2, -1, 0, 8, 2, true, true, false, 4>, kCapTransposed},
+    {"mfma2d_64x64x64_w2x2_k4_swz", launch_mfma<64, 64, 64, 2, 2, -1, 0, 8, 2, true, true, false, 4>, kCapTransposed},
+    {"mfma3d_64x64x64_w2x2_k4_swz", launch_mfma<64, 64, 64, 2, 2, -1, 0, 8, 3, true, true, false, 4>, kCapTransposed},
 };
 
 }  // namespace

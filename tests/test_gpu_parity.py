@@ -339,7 +339,8 @@ BATCH_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4"), (1, 1, "lds_t32"),
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in (
         "mfma_64x64x32_w2x2_pa4_pb0", "mfma_256x256x16_w2x4_pa4_pb0", "mfma3_256x256x16_w4x4_swz_pb0",
         "mfma2p_256x256x32_w4x4_swz_pb0", "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz_g4",
-        "mfma2d_256x256x32_w2x4_swz_g4_il", "mfma2d_256x256x32_w4x4_swz_g4_il")]
+        "mfma2d_256x256x32_w2x4_swz_g4_il", "mfma2d_256x256x32_w4x4_swz_g4_il",
+        "mfma2d_64x64x128_w2x2_k4_swz", "mfma2d_64x64x64_w2x2_k4_swz")]
 
 
 def _run_batched(A3, B3, M, N, K, nb, sa, sb, sc, lda, ldb, ldc, kernel):
@@ -436,7 +437,9 @@ TRANS_CAPABLE = ["mfma2d_256x256x32_w4x4_swz", "mfma3d_256x128x32_w4x2_swz",
                  "mfma2d_256x256x32_w4x4_swz_g4_il", "mfma2d_256x256x32_w4x2_swz_g4_il",
                  "mfma2d_256x256x32_w2x4_swz_g4_il", "mfma3d_256x128x32_w4x2_swz_il",
                  "mfma3d_128x256x16_w2x4_swz_il", "mfma3_64x128x16_w2x2_swz_il",
-                 "mfma2d_256x256x32_w2x4_swz_g8_il", "mfma2d_256x256x32_w4x4_swz_g8_il"]
+                 "mfma2d_256x256x32_w2x4_swz_g8_il", "mfma2d_256x256x32_w4x4_swz_g8_il",
+                 "mfma2d_64x64x128_w2x2_k4_swz", "mfma2d_64x64x64_w2x2_k4_swz",
+                 "mfma3d_64x64x64_w2x2_k4_swz"]
 TRANS_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in TRANS_CAPABLE]
 OPS = ["NN", "NT", "TN", "TT"]
