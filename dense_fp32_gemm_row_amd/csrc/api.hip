@@ -206,11 +206,13 @@ int validate(bool ta, bool tb, int64_t batch, int64_t M, int64_t N, int64_t K, c
 // tuned table if there is one, else the cost model's choice.  The model
 // ("Tiling and Blocking for Reuse", choosing the tile size: reuse against
 // occupancy and tails, settled by measurement): a CU receives
-// n = ceil(tiles / CUs) tiles of a candidate and runs up to nrates of them
-// at once at the measured per-CU rate for that many, so the predicted time
-// is n * 2 * bm * bn * K / rate; rows that are not 16-byte aligned scale
-// the rate by the candidate's measured factor.  A batch multiplies the
-// tiles.  Transposed operands consider only configurations that take them.
+// n = ceil(tiles / CUs) tiles of a candidate, and the candidate's measured
+// per-CU rate for a share of min(n, nrates) tiles (the last level also
+// stands for larger shares, whose tiles queue behind those that fit at
+// once) gives the predicted time n * 2 * bm * bn * K / rate; rows that are
+// not 16-byte aligned scale the rate by the candidate's measured factor.  A
+// batch multiplies the tiles.  Transposed operands consider only
+// configurations that take them.
 void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant, int *config,
                    bool trans = false, bool aligned = true) {
     if (batch == 1 && !trans) {

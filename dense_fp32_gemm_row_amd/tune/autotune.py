@@ -12,11 +12,14 @@ The build turns that table into the dispatch table of gemm_f32.
 With --calibrate it also measures the cost model that gemm_f32 uses for
 shapes not in the table: every candidate of the table's "model" section runs
 on the calibration shapes below, and for each shape a CU's share is
-n = ceil(tiles / cus) tiles, run min(n, len(gflops_per_cu)) at a time; the
-per-CU rate 2 * bm * bn * K * n / (time - launch floor) is collected by that
-concurrency, and each entry of gflops_per_cu becomes the median of its
-group.  `unaligned` is the median ratio of the rate on shapes whose rows are
-not 16-byte aligned to the aligned rate at the same concurrency.
+n = ceil(tiles / cus) tiles; the per-CU rate 2 * bm * bn * K * n /
+(time - launch floor) is collected at level min(n, len(gflops_per_cu)), and
+each entry of gflops_per_cu becomes the median of its level.  The number of
+levels per candidate is set in the table (at least its occupancy, and two
+for a candidate that fits one tile per CU, since one tile per CU runs
+faster per CU than several in turn).  `unaligned` is the median ratio of
+the rate on shapes whose rows are not 16-byte aligned to the aligned rate
+at the same level.
 
     python -m dense_fp32_gemm_row_amd.tune.autotune --out tuned.json --calibrate
 
@@ -92,23 +95,23 @@ def calibrate_model(binding, model: dict, budget_ms: float) -> dict:
     out = {"cus": cus, "candidates": []}
     for cand in model["candidates"]:
         cfg, bm, bn = cand["config"], int(cand["bm"]), int(cand["bn"])
-        occ = len(cand["gflops_per_cu"])
+        levels = len(cand["gflops_per_cu"])
         floor = times[(cfg, 1, 1, 1)]
 
         def rate(M, N, K):
             tiles = math.ceil(M / bm) * math.ceil(N / bn)
             n = math.ceil(tiles / cus)
             ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
-            return min(n, occ), 2.0 * bm * bn * K * n / (ms * 1e-3) / 1e9
+            return min(n, levels), 2.0 * bm * bn * K * n / (ms * 1e-3) / 1e9
 
         groups: dict[int, list[float]] = {}
         for shape in CAL_SHAPES:
-            conc, r = rate(*shape)
-            groups.setdefault(conc, []).append(r)
+            level, r = rate(*shape)
+            groups.setdefault(level, []).append(r)
         rates = []
-        for conc in range(1, occ + 1):  # a level with no shape inherits the one below
-            rates.append(round(statistics.median(groups[conc]), 1) if conc in groups else rates[-1])
-        ratios = [r / rates[conc - 1] for conc, r in (rate(*s) for s in CAL_UNALIGNED)]
+        for level in range(1, levels + 1):  # a level with no shape inherits the one below
+            rates.append(round(statistics.median(groups[level]), 1) if level in groups else rates[-1])
+        ratios = [r / rates[level - 1] for level, r in (rate(*s) for s in CAL_UNALIGNED)]
         out["candidates"].append({**cand, "gflops_per_cu": rates,
                                   "unaligned": round(min(1.0, statistics.median(ratios)), 3)})
     return out

@@ -157,7 +157,7 @@ def test_cost_model_choices(lib):
         v, c = b.gemm_f32_select(M, N, K, lda or K, ldb or N, N)
         return b.gemm_f32_config_name(v, c)
 
-    assert pick(512, 512, 512).startswith("mfma_64x64")
+    assert "64x64" in pick(512, 512, 512)
     assert pick(8192, 8192, 8192 + 64) == "mfma2d_256x256x32_w4x4_swz_g4_il"
     assert "64x64" in pick(3072, 3072, 3072)
     assert pick(8192, 1024, 4096).startswith("mfma3d_256x128")
