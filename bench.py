@@ -305,7 +305,6 @@ def main() -> int:
     dC = torch.empty((nb, M, N) if nb > 1 else (M, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     flops = 2.0 * nb * M * N * K
-    call = binding.gemm_batched if nb > 1 else binding.gemm
 
     if args.stages:
         return run_stages(args, w, A, B, dA, dB, dC, stream, flops)
@@ -337,10 +336,10 @@ def main() -> int:
         splits = args.splitk or "library choice of"
         cname = (f"{cname if args.variant is not None else 'library choice'}, "
                  f"split-K ({splits} splits)")
-    elif args.variant is None:
-        fn = lambda: call(dA, dB, dC)  # noqa: E731  (gemm_f32 / gemm_f32_strided_batched)
+    elif args.variant is None:  # gemm_f32 / gemm_f32_strided_batched, arguments built once
+        fn = binding.prepare(dA, dB, dC, stream=stream, batched=nb > 1)
     else:
-        fn = lambda: call(dA, dB, dC, variant=v, config=c)  # noqa: E731
+        fn = binding.prepare(dA, dB, dC, variant=v, config=c, stream=stream, batched=nb > 1)
 
     dinfo = device_info(dev)
     with SclkSampler(dev, enabled=not args.no_sclk) as sclk:
@@ -418,8 +417,8 @@ def run_stages(args, w, A, B, dA, dB, dC, stream, flops) -> int:
         for c in range(binding.gemm_f32_config_count(v)):
             name = binding.gemm_f32_config_name(v, c)
             steps = args.steps if v >= 2 else max(2, min(args.steps, 3))
-            call = binding.gemm_batched if w.batch > 1 else binding.gemm
-            fn = lambda: call(dA, dB, dC, variant=v, config=c)  # noqa: E731
+            fn = binding.prepare(dA, dB, dC, variant=v, config=c, stream=stream,
+                                 batched=w.batch > 1)
             total, per = time_launches(fn, steps, 1, stream)
             avg = sum(per) / len(per)
             tf = flops / (avg / 1e3) / 1e12

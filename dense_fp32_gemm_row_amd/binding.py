@@ -198,7 +198,9 @@ def _operand(t, name: str, dims: int) -> tuple[int, int, int]:
     raise ValueError(f"{name} must be row-major or a transposed view of a row-major matrix")
 
 
-def _call(A, B, out, variant, config, stream, batched: bool):
+def _marshal(A, B, out, variant, config, stream, batched: bool):
+    """Checks the operands and returns (C entry point name, its arguments,
+    out) for out = A @ B."""
     import torch
 
     dims = 3 if batched else 2
@@ -225,18 +227,43 @@ def _call(A, B, out, variant, config, stream, batched: bool):
         c = config_id(v, config) if isinstance(config, str) else int(config)
     a, b, cp = A.data_ptr(), B.data_ptr(), out.data_ptr()
     if opa == OP_N and opb == OP_N and not batched:
-        rc = (gemm_f32(M, N, K, a, lda, b, ldb, cp, ldc, sp) if v == -1 else
-              gemm_f32_variant(v, c, M, N, K, a, lda, b, ldb, cp, ldc, sp))
-    elif opa == OP_N and opb == OP_N:
-        rc = (gemm_f32_strided_batched(nb, M, N, K, a, lda, sa, b, ldb, sb, cp, ldc, sc, sp)
-              if v == -1 else
-              gemm_f32_strided_batched_variant(v, c, nb, M, N, K, a, lda, sa, b, ldb, sb, cp,
-                                               ldc, sc, sp))
-    else:
-        rc = gemm_f32_ex(v, c, opa, opb, nb, M, N, K, a, lda, sa, b, ldb, sb, cp, ldc, sc, sp)
+        if v == -1:
+            return "gemm_f32", (M, N, K, a, lda, b, ldb, cp, ldc, sp), out
+        return "gemm_f32_variant", (v, c, M, N, K, a, lda, b, ldb, cp, ldc, sp), out
+    if opa == OP_N and opb == OP_N:
+        if v == -1:
+            return ("gemm_f32_strided_batched",
+                    (nb, M, N, K, a, lda, sa, b, ldb, sb, cp, ldc, sc, sp), out)
+        return ("gemm_f32_strided_batched_variant",
+                (v, c, nb, M, N, K, a, lda, sa, b, ldb, sb, cp, ldc, sc, sp), out)
+    return ("gemm_f32_ex",
+            (v, c, opa, opb, nb, M, N, K, a, lda, sa, b, ldb, sb, cp, ldc, sc, sp), out)
+
+
+def _call(A, B, out, variant, config, stream, batched: bool):
+    name, args, out = _marshal(A, B, out, variant, config, stream, batched)
+    rc = getattr(load(), name)(*args)
     if rc != GEMM_F32_OK:
         raise GemmError(rc, gemm_f32_last_error())
     return out
+
+
+def prepare(A, B, out, *, variant: int | str | None = None, config: int | str = -1,
+            stream=None, batched: bool = False):
+    """A callable with no arguments that enqueues ``out = A @ B`` (as gemm,
+    or gemm_batched when ``batched``), with the operands checked and the C
+    arguments built once: for launch loops, where the per-call checks of
+    gemm would cost more host time than a small product takes on the GPU.
+    A, B and out must stay alive and unchanged in place while it is used."""
+    name, args, _ = _marshal(A, B, out, variant, config, stream, batched)
+    fn = getattr(load(), name)
+
+    def launch():
+        rc = fn(*args)
+        if rc != GEMM_F32_OK:
+            raise GemmError(rc, gemm_f32_last_error())
+
+    return launch
 
 
 def gemm(A, B, out=None, *, variant: int | str | None = None, config: int | str = -1,

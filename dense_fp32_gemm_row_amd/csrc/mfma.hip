@@ -229,6 +229,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
     }
 }
 
+// Workgroup barrier for a loop whose direct global -> LDS loads run PENDING
+// instructions ahead: the wavefront waits until at most its PENDING most
+// recent vector-memory instructions are outstanding (they complete in
+// order, so its older loads have landed in LDS) and its LDS reads are done,
+// then meets the others.  __syncthreads() would wait for every outstanding
+// load, because its workgroup fence does.  The empty asm statements keep
+// the compiler from moving LDS accesses across the barrier, as the fence
+// did.
+template <int PENDING>
+__device__ __forceinline__ void barrier_after_older_loads() {
+    static_assert(PENDING >= 0 && PENDING < 64, "vmcnt is 6 bits");
+    // s_waitcnt: vmcnt in bits 3:0 and 15:14, lgkmcnt 0, expcnt (7) not waited on
+    __builtin_amdgcn_s_waitcnt((PENDING & 15) | ((PENDING >> 4) << 14) | (7 << 4));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // One operand of the pipelined kernel: the R x BK slice (R = BM rows of op(A)
 // or BN columns of op(B)) that one K-step stages through LDS.
 //
@@ -280,6 +298,7 @@ struct OperandTile {
     static constexpr bool DW_OK = dw_tile_ok(R, BK, NW, KMAJOR);
     static constexpr int J = DIRECT && !DW ? CH / NW : 1;
     static constexpr int JW = DW ? CHW / NW : 1;
+    static constexpr int LOADS = DW ? JW : DIRECT ? J : 0;  // direct-load instructions per K-step
     static constexpr int DW_P = KMAJOR || !DW_OK ? 1 : 32 / gcd(DW_STEP, 32);
     static constexpr int DW_NC = DW_P < JW ? DW_P : JW;  // distinct k columns of a lane
     static_assert(L * 4 * NT == R * BK, "even tile split");
@@ -565,7 +584,8 @@ struct RingTile {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32 x 32 blocks");
     static_assert(BK % (16 * KG) == 0, "an even number of chunks per K-step and k-group");
     static_assert(NT <= 1024, "at most 16 wavefronts per workgroup");
-    static_assert(STAGES == 2 || STAGES == 3, "two or three LDS buffers");
+    static_assert(STAGES == 2 || STAGES == 3 || (STAGES == 4 && DIRECT),
+                  "two or three LDS buffers, or four with direct loads");
     static_assert(STAGES * (TileA::SIZE + TileB::SIZE) * 4 <= kLdsBytes, "LDS budget of a workgroup");
 
 
@@ -658,27 +678,40 @@ struct RingTile {
             // Branch-free so that the reads stay ahead of the MFMAs they feed
             // (a branch here lets the compiler sink them back to their use).
             //
-            // Three buffers: the last chunk reads ahead into step t + 1 (tile t + 1
-            // was published by the previous barrier); the barrier ends the step.
+            // Three buffers, register staging: the last chunk reads ahead into
+            // step t + 1 (tile t + 1 was published by the previous barrier); the
+            // barrier ends the step.
             //
-            // Two buffers: the barrier sits before the last chunk.  By then the
-            // last chunk's fragments are in registers (so every read of buffer
-            // `cur` is done: write after read) and tile t + 1 has landed in buffer
-            // `nxt` (read after write), so right after the barrier the first
-            // fragments of step t + 1 are read while the last chunk's MFMAs run.
+            // Two buffers, and three with direct loads: the barrier sits before
+            // the last chunk.  By then the last chunk's fragments are in
+            // registers (so every read of buffer `cur` is done: write after
+            // read) and tile t + 1 has landed in buffer `nxt` (read after
+            // write), so right after the barrier the first fragments of step
+            // t + 1 are read while the last chunk's MFMAs run.  With three (four)
+            // buffers the loads of tile t + 2 (and t + 3) stay in flight across
+            // the barrier: each tile gets two (three) steps to land.
             //
             // In the last step the look-ahead read of buffer `nxt` is unused; it
             // stays inside the buffer, which nobody writes after the barrier.
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const int set = kc & 1;
-                if constexpr (STAGES == 2) {
+                if constexpr (STAGES == 2 || DIRECT) {
                     if (kc == KC - 1) {
                         store_step(nxt);  // register staging: stale but in-bounds in the last step
                         // keep all of the previous chunk's MFMAs ahead of the
                         // barrier: they cover the latency of the reads it waits for
                         __builtin_amdgcn_sched_barrier(0);
-                        __syncthreads();
+                        constexpr int L = TileA::LOADS + TileB::LOADS;
+                        if constexpr (STAGES == 2) {
+                            __syncthreads();
+                        } else if (STAGES == 4 && t + 3 < nk) {  // tiles t + 2, t + 3 in flight
+                            barrier_after_older_loads<STAGES == 4 ? 2 * L : 0>();
+                        } else if (t + 2 < nk) {                 // tile t + 2 in flight
+                            barrier_after_older_loads<L>();
+                        } else {
+                            barrier_after_older_loads<0>();
+                        }
                         read_frag(set ^ 1, nxt, 0);
                     } else {
                         read_frag(set ^ 1, cur, kc + 1);
@@ -701,7 +734,7 @@ struct RingTile {
                 if constexpr (kMfmaPerChunk > kPairs)
                     __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk - kPairs, 0);
             }
-            if constexpr (STAGES == 3) {
+            if constexpr (STAGES == 3 && !DIRECT) {
                 if (t + 2 < nk) store_step(ahead);
                 if (t + 1 < nk) __syncthreads();
             }
@@ -844,8 +877,9 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_mfma_ring_kernel(
     Full::run(M, N, K, A, lda, B, ldb, C, ldc, m0, n0, sA, sB);
 }
 
-// PIPE = 0: the first kernel; PIPE = 2 or 3: the pipelined kernel with that
-// many LDS buffers.  DIRECT: direct global -> LDS loads where the shape
+// PIPE = 0: the first kernel; PIPE = 2, 3 or 4: the pipelined kernel with
+// that many LDS buffers (four for direct loads only: where the shape needs
+// register staging, that kernel runs with three).  DIRECT: direct global -> LDS loads where the shape
 // allows (full tiles, 16-byte-aligned rows), register staging otherwise.
 // TRANS: also compiled for transposed operands (pipelined kernel only).
 // IL: interleaved column blocks for B as stored (pipelined kernel only).
@@ -867,8 +901,9 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     const dim3 g(static_cast<unsigned>(grid)), b(NT);
 #define GEMM_RING(D, G, V, TA, TB)                                                              \
     hipLaunchKernelGGL(                                                                         \
-        (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, PIPE, D, G, V, TA, TB, IL, KG>), g, \
-        b, 0,                                                                                   \
+        (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, ((D) || PIPE < 4 ? PIPE : 3), D, G, \
+                               V, TA, TB, IL, KG>),                                             \
+        g, b, 0,                                                                                \
         stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, GROUP_M,   \
         batch_of(p))
 #define GEMM_RING_T(D, G, V)                                                                    \
@@ -962,7 +997,8 @@ const ConfigEntry kMfmaConfigs[] = {
     {"mfma3_128x128x16_w2x2_swz_pb0", launch_mfma<128, 128, 16, 2, 2, -1, 0, 8, 3, false, true>, kCapTransposed},
     {"mfma3_64x64x16_w2x2_swz_pb0", launch_mfma<64, 64, 16, 2, 2, -1, 0, 8, 3, false, true>, kCapTransposed},
     // Pipelined kernel, direct global -> LDS loads on full tiles (register
-    // staging on edge tiles): mfma3d = three buffers, mfma2d = two buffers;
+    // staging on edge tiles): mfma3d = three buffers, mfma2d = two buffers,
+    // mfma4d = four;
     // 256x128 / 128x256 tiles fit two workgroups per CU at BK = 16; g4 / g16
     // change the column-strip height of the tile order.
     {"mfma3d_256x256x16_w4x4_swz", launch_mfma<256, 256, 16, 4, 4, -1, 0, 8, 3, true>, 0},
@@ -990,6 +1026,7 @@ const ConfigEntry kMfmaConfigs[] = {
     {"mfma2d_64x64x128_w2x2_k4_swz", launch_mfma<64, 64, 128, 2, 2, -1, 0, 8, 2, true, true, false, 4>, kCapTransposed},
     {"mfma2d_64x64x64_w2x2_k4_swz", launch_mfma<64, 64, 64, 2, 2, -1, 0, 8, 2, true, true, false, 4>, kCapTransposed},
     {"mfma3d_64x64x64_w2x2_k4_swz", launch_mfma<64, 64, 64, 2, 2, -1, 0, 8, 3, true, true, false, 4>, kCapTransposed},
+    {"mfma4d_64x64x64_w2x2_k4_swz", launch_mfma<64, 64, 64, 2, 2, -1, 0, 8, 4, true, true, false, 4>, kCapTransposed},
 };
 
 }  // namespace

@@ -11,9 +11,11 @@ it gives each LDS array, and those scopes reach loads only a few address
 offsets away from the array.  When they do not reach the fragment reads, the
 compiler waits for all outstanding global loads before the first LDS read
 of every K-step, which serialises the prefetch with the math (about 1.5% of
-the headline throughput).  These tests keep the one wait on global loads in
-each K loop where it belongs: right before the barrier that publishes the
-next tile.
+the headline throughput).  These tests keep the waits on global loads in
+each K loop where they belong: right before the barrier that publishes the
+next tile, and with three LDS buffers leaving the loads of the tile after it
+in flight (a wait for every load there gives the third buffer nothing to
+do).
 """
 
 from __future__ import annotations
@@ -88,10 +90,21 @@ def ring_kernels(asm: str):
         yield args, loops(body)
 
 
+def barrier_follows(lines: list[str], k: int) -> bool:
+    """An s_barrier right after line k (comments and empty inline-asm
+    markers between them do not count)."""
+    for ln in lines[k + 1:k + 8]:
+        if ln.startswith("s_barrier"):
+            return True
+        if ln and not ln.startswith((";", "//")):
+            return False
+    return False
+
+
 def test_direct_load_kernels_wait_only_at_the_barrier(mfma_asm):
-    checked = 0
+    checked = stages3 = 0
     for args, kloops in ring_kernels(mfma_asm):
-        # <BM, BN, BK, WM, WN, PADA, PADB, STAGES, DIRECT, GUARD, VEC, TA, TB, IL>
+        # <BM, BN, BK, WM, WN, PADA, PADB, STAGES, DIRECT, GUARD, VEC, TA, TB, IL, KG>
         if args[8] != "true":
             continue
         where = ", ".join(args)
@@ -100,13 +113,23 @@ def test_direct_load_kernels_wait_only_at_the_barrier(mfma_asm):
         assert len(direct) == 1, f"<{where}>: {len(direct)} K loops with direct loads"
         lines = [ln.strip() for ln in direct[0].splitlines()]
         waits = [k for k, ln in enumerate(lines) if ln.startswith("s_waitcnt") and "vmcnt" in ln]
-        assert len(waits) == 1, f"<{where}>: {len(waits)} waits on global loads in the K loop"
-        k = waits[0]
-        assert any(ln.startswith("s_barrier") for ln in lines[k + 1:k + 3]), \
-            f"<{where}>: the wait on global loads is not right before the barrier"
+        for k in waits:
+            assert barrier_follows(lines, k), \
+                f"<{where}>: a wait on global loads that is not right before a barrier: {lines[k]}"
+        counts = sorted(int(re.search(r"vmcnt\((\d+)\)", lines[k]).group(1)) for k in waits)
+        if args[7] == "2":
+            assert counts == [0], f"<{where}>: waits on global loads in the K loop: {counts}"
+        else:
+            # three (four) buffers: the loads of tile t + 2 (and t + 3) stay in
+            # flight across the barrier (nonzero counts), except near the end
+            nbuf = int(args[7])
+            assert len(counts) == nbuf - 1 and counts[0] == 0 and \
+                all(c == counts[1] * i for i, c in enumerate(counts)) and counts[1] > 0, \
+                f"<{where}>: waits on global loads in the K loop: {counts}"
+            stages3 += 1
         # the per-step global addresses advance by increments; a multiply per
         # K-step here cost the 16-wave kernels 11%
         muls = [ln for ln in lines if ln.startswith(("s_mul_i32", "s_mul_hi_u32"))]
         assert not muls, f"<{where}>: address multiplies in the K loop: {muls[:3]}"
         checked += 1
-    assert checked >= 10, f"only {checked} direct-load kernels found"
+    assert checked >= 10 and stages3 >= 4, f"only {checked} direct-load kernels found ({stages3} with three buffers)"

@@ -439,7 +439,7 @@ TRANS_CAPABLE = ["mfma2d_256x256x32_w4x4_swz", "mfma3d_256x128x32_w4x2_swz",
                  "mfma3d_128x256x16_w2x4_swz_il", "mfma3_64x128x16_w2x2_swz_il",
                  "mfma2d_256x256x32_w2x4_swz_g8_il", "mfma2d_256x256x32_w4x4_swz_g8_il",
                  "mfma2d_64x64x128_w2x2_k4_swz", "mfma2d_64x64x64_w2x2_k4_swz",
-                 "mfma3d_64x64x64_w2x2_k4_swz"]
+                 "mfma3d_64x64x64_w2x2_k4_swz", "mfma4d_64x64x64_w2x2_k4_swz"]
 TRANS_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in TRANS_CAPABLE]
 OPS = ["NN", "NT", "TN", "TT"]
@@ -511,7 +511,8 @@ SPLITK_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4"), (1, 1, "lds_t32"),
                   (2, 0, "regblock_128x128x8_t8x8_pad4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in (
         "mfma_64x64x32_w2x2_pa4_pb0", "mfma3_64x64x16_w2x2_swz_pb0", "mfma3_128x128x16_w2x2_swz_pb0",
-        "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz")]
+        "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz", "mfma2d_64x64x64_w2x2_k4_swz",
+        "mfma2d_64x64x128_w2x2_k4_swz")]
 
 
 @pytest.mark.parametrize("kernel", SPLITK_KERNELS, ids=[k[2] for k in SPLITK_KERNELS])
@@ -564,6 +565,30 @@ def test_splitk_deep_k_sampled():
     assert freivalds(A, B, C) <= 1e-5
 
 
+def test_prepared_call_matches_gemm():
+    """binding.prepare (arguments built once, for launch loops) enqueues the
+    same call as gemm / gemm_batched, for row-major, transposed and batched
+    operands, and keeps working on repeated launches."""
+    import torch
+
+    A, B = make_inputs(130, 70, 50, "uniform", seed=45)
+    dA, dB = to_dev(A), to_dev(B)
+    for a, b_, name in ((dA, dB, "NN"), (to_dev(np.ascontiguousarray(A.T)).T, dB, "TN")):
+        ref = to_host(b.gemm(a, b_))
+        out = torch.full((130, 70), float("nan"), device="cuda:0")
+        launch = b.prepare(a, b_, out)
+        for _ in range(3):
+            launch()
+        assert np.array_equal(to_host(out).view(np.uint32), ref.view(np.uint32)), name
+    d3 = to_dev(np.stack([A, A[::-1].copy()]))
+    dB3 = dB.expand(2, -1, -1)
+    for kw in ({}, {"variant": "mfma", "config": "mfma2d_64x64x64_w2x2_k4_swz"}):
+        ref = to_host(b.gemm_batched(d3, dB3, **kw))
+        out = torch.empty((2, 130, 70), device="cuda:0")
+        b.prepare(d3, dB3, out, batched=True, **kw)()
+        assert np.array_equal(to_host(out).view(np.uint32), ref.view(np.uint32)), kw
+
+
 def test_splitk_one_split_is_plain_product():
     A, B = make_inputs(200, 100, 64, "uniform", seed=44)
     dA, dB = to_dev(A), to_dev(B)
@@ -577,7 +602,7 @@ def test_splitk_one_split_is_plain_product():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("wname", ["square4096", "square8192", "ffn", "square8000", "square8191",
-                                   "ktail8100"])
+                                   "ktail8100", "deepk"])
 def test_full_size_sampled(wname):
     import torch
 
