@@ -235,11 +235,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(
 // order, so its older loads have landed in LDS) and its LDS reads are done,
 // then meets the others.  __syncthreads() would wait for every outstanding
 // load, because its workgroup fence does.  The empty asm statements keep
-// the compiler from moving LDS accesses across the barrier, as the fence
-// did.
+// the compiler from moving memory accesses across the wait (the count
+// assumes the newest loads were issued before it) and LDS accesses across
+// the barrier, as the fence did.
 template <int PENDING>
 __device__ __forceinline__ void barrier_after_older_loads() {
     static_assert(PENDING >= 0 && PENDING < 64, "vmcnt is 6 bits");
+    asm volatile("" ::: "memory");
     // s_waitcnt: vmcnt in bits 3:0 and 15:14, lgkmcnt 0, expcnt (7) not waited on
     __builtin_amdgcn_s_waitcnt((PENDING & 15) | ((PENDING >> 4) << 14) | (7 << 4));
     asm volatile("" ::: "memory");

@@ -244,8 +244,8 @@ const char *gemm_f32_last_error(void);
 int gemm_f32_config_count(int variant);
 
 /*
- * Name of a tile configuration, e.g. "mfma_256x256x16_w2x2"; NULL when the
- * variant or configuration does not exist.  Static storage.
+ * Name of a tile configuration, e.g. "mfma2d_256x256x32_w4x4_swz_g4_il";
+ * NULL when the variant or configuration does not exist.  Static storage.
  */
 const char *gemm_f32_config_name(int variant, int config_id);
 
