@@ -171,6 +171,33 @@ def test_edge_tiles_and_k_tail(v, c, name):
         assert_close(to_host(out), ref64, K, f"{name} uniform {M}x{N}x{K}")
 
 
+DEEP_PIPELINES = [(v, c, n) for v, c, n in ALL_CONFIGS
+                  if v == 3 and n.split("_")[0] in ("mfma3d", "mfma4d")]
+
+
+@pytest.mark.parametrize("v,c,name", DEEP_PIPELINES, ids=[n for _, _, n in DEEP_PIPELINES])
+def test_deep_pipeline_short_k(v, c, name):
+    """Three- and four-buffer direct-load loops hold the loads of one or two
+    later tiles in flight across each barrier, and wait for fewer of them in
+    the last K-steps.  Every trip count from 1 to 6 K-steps, with and without
+    a partial last step, with 16-byte-aligned rows (16-byte direct loads) and
+    without (4-byte direct loads, B's rows one float longer)."""
+    import torch
+
+    bk = int(name.split("_")[1].split("x")[2])
+    M, N = 256, 256  # whole tiles of every configuration: the unguarded loop
+    for steps in range(1, 7):
+        for K in (steps * bk, steps * bk + 8):
+            for bpad in (0, 1):
+                log(f"{name}: K={K} ({steps} K-steps), B padding {bpad}")
+                A, B = make_inputs(M, N, K, "int4", seed=50 + steps)
+                dB = torch.zeros((K, N + bpad), device="cuda:0")
+                dB[:, :N] = to_dev(B)
+                out = torch.empty((M, N), device="cuda:0")
+                b.gemm(to_dev(A), dB[:, :N], out, variant=v, config=c)
+                assert_exact(to_host(out), oracle.gemm(A, B), f"{name} K={K} pad={bpad}")
+
+
 @pytest.fixture(scope="module")
 def huge_strided():
     """Operands whose rows lie more than 2^31 floats apart from the start:
