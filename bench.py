@@ -9,6 +9,9 @@ Prints ONE JSON line with the throughput (TFLOP/s = 2 M N K / time), the
 dominant kernel's roofline position (measured live with HIP events on the
 stream the kernel runs on), the oracle timed on the host's cores on a bounded
 sample of the same workload, and a parity check of the timed output.
+Each step is its own launch with an event pair around it; with --graph the
+steps are captured into one HIP graph and timed as one replay, which removes
+the host's cost per launch (it bounds the small workloads).
 
 Other modes (results on stderr / in a file, not the contract line):
   --stages   time every kernel stage (naive, LDS-tiled, register-blocked,
@@ -186,6 +189,36 @@ def time_launches(fn, steps: int, warmup: int, stream):
     return total, per
 
 
+def time_graph(make_fn, steps: int, warmup: int, stream):
+    """Runs make_fn(stream)() warmup times, then captures `steps` launches of
+    make_fn(capture stream) into one HIP graph (torch.cuda.CUDAGraph) and times
+    a replay on `stream` with one event pair (after an untimed replay that
+    uploads the graph).  Returns (total_ms, [total_ms / steps])."""
+    import torch
+
+    eager = make_fn(stream)
+    for _ in range(warmup):
+        eager()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        fn = make_fn(cap)
+        for _ in range(steps):
+            fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        graph.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end)
+    return total, [total / steps]
+
+
 def cpu_baseline(A, B, target_s: float) -> dict:
     """The oracle, as it stands, on a bounded sample of rows of the same
     product, timed with the host's default OpenMP thread count."""
@@ -255,6 +288,9 @@ def main() -> int:
     ap.add_argument("--splitk", type=int, default=None, metavar="S",
                     help="time gemm_f32_splitk with S splits (partial products + reduction); "
                          "0 = the library's choice of splits")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as one captured HIP graph instead of one launch each "
+                         "(removes the host's launch cost; per-launch time is the replay / steps)")
     ap.add_argument("--no-sclk", action="store_true",
                     help="do not sample the engine clock during the timed region")
     ap.add_argument("--stages", action="store_true")
@@ -331,19 +367,25 @@ def main() -> int:
         need = binding.gemm_f32_splitk_workspace_size(M, N, K, args.splitk)
         work = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
         sv, sc = (None, -1) if args.variant is None else (v, c)
-        fn = lambda: binding.gemm_splitk(dA, dB, args.splitk, dC, work,  # noqa: E731
-                                         variant=sv, config=sc)
+
+        def make_fn(s):
+            return lambda: binding.gemm_splitk(dA, dB, args.splitk, dC, work, variant=sv,
+                                               config=sc, stream=s)
         splits = args.splitk or "library choice of"
         cname = (f"{cname if args.variant is not None else 'library choice'}, "
                  f"split-K ({splits} splits)")
-    elif args.variant is None:  # gemm_f32 / gemm_f32_strided_batched, arguments built once
-        fn = binding.prepare(dA, dB, dC, stream=stream, batched=nb > 1)
-    else:
-        fn = binding.prepare(dA, dB, dC, variant=v, config=c, stream=stream, batched=nb > 1)
+    else:  # gemm_f32 / gemm_f32_strided_batched (or the explicit kernel), arguments built once
+        kw = {} if args.variant is None else {"variant": v, "config": c}
+
+        def make_fn(s):
+            return binding.prepare(dA, dB, dC, stream=s, batched=nb > 1, **kw)
 
     dinfo = device_info(dev)
     with SclkSampler(dev, enabled=not args.no_sclk) as sclk:
-        total_ms, per = time_launches(fn, args.steps, args.warmup, stream)
+        if args.graph:
+            total_ms, per = time_graph(make_fn, args.steps, args.warmup, stream)
+        else:
+            total_ms, per = time_launches(make_fn(stream), args.steps, args.warmup, stream)
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
     value = flops * args.steps / (total_ms / 1e3) / 1e12
@@ -368,7 +410,8 @@ def main() -> int:
         "config": {"workload": w.name, "batch": nb, "M": M, "N": N, "K": K, "dist": w.dist,
                    "seed": w.seed, "ops": args.ops, "splitk": args.splitk,
                    "layout": "row-major C; A, B row-major, stored transposed where ops says T",
-                   "kernel": cname, "parallelism": "none"},
+                   "kernel": cname, "parallelism": "none",
+                   "timing": "one HIP graph of the steps" if args.graph else "one launch per step"},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),
