@@ -272,3 +272,58 @@ def test_splitk_validation(lib):
                              None) == b.GEMM_F32_ENOKERNEL
     # empty products need nothing
     assert call(M=0) == b.GEMM_F32_OK
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "gemm_f32.h"
+
+int main(void) {
+    /* every entry point, by address: the header declares them as C functions */
+    void (*fns[])(void) = {
+%(fns)s
+    };
+    int v, c, n = 0;
+    for (v = 0; v < GEMM_F32_NUM_VARIANTS; ++v) {
+        int count = gemm_f32_config_count(v);
+        if (count <= 0 || gemm_f32_config_name(v, 0) == NULL) return 1;
+        n += count;
+    }
+    if (gemm_f32_config_count(GEMM_F32_NUM_VARIANTS) != GEMM_F32_ENOKERNEL) return 2;
+    if (gemm_f32_select(8192, 8192, 8192, 8192, 8192, 8192, &v, &c) != GEMM_F32_OK) return 3;
+    /* invalid arguments are rejected on the host, before any device work */
+    if (gemm_f32(-1, 1, 1, NULL, 1, NULL, 1, NULL, 1, NULL) != GEMM_F32_EINVAL) return 4;
+    if (strlen(gemm_f32_last_error()) == 0) return 5;
+    if (gemm_f32(0, 5, 5, NULL, 5, NULL, 5, NULL, 5, NULL) != GEMM_F32_OK) return 6;
+    if (gemm_f32_splitk_workspace_size(1024, 1024, 65536, 0) <= 0) return 7;
+    printf("abi %%d configs %%d select %%s %%d\n", gemm_f32_abi_version(), n,
+           gemm_f32_config_name(v, c), (int)(sizeof fns / sizeof fns[0]));
+    return 0;
+}
+"""
+
+
+def test_header_serves_a_c_caller(lib, tmp_path):
+    """A plain C99 program includes the header (warnings are errors), takes
+    the address of every declared entry point, links against the library and
+    runs the calls that need no GPU: the ABI is usable without Python."""
+    import shutil
+    import subprocess
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    names = declared_functions()
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER % {"fns": "\n".join(f"        (void (*)(void))&{n}," for n in names)})
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(b.LIBRARY)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-I", os.path.join(ROOT, "include"), str(src), "-L", libdir, "-lgemm_f32",
+           f"-Wl,-rpath,{libdir}", "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
+    assert f"select mfma2d_256x256x32_w4x4_swz_g4_il {len(names)}" in run.stdout
