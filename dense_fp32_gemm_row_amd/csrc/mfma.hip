@@ -939,8 +939,13 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
         const bool spans_ok = (a_rows + 256) * p.lda + a_cols + 256 < kSpan &&
                               (b_rows + 256) * p.ldb + b_cols + 256 < kSpan;
         if (!vec && spans_ok) {
+        // 4-byte loads issue R * BK / 64 instructions per operand and K-step;
+        // with three or four buffers one or two K-steps of them stay in flight
+        // at a barrier, which the 6-bit load counter must be able to express.
+        constexpr int kDwLoads = (BM * BK / 64 + BN * BK / 64) / NW;
+        constexpr bool kDwCountOk = (PIPE > 2 ? PIPE - 2 : 0) * kDwLoads < 64;
 #define GEMM_DW(TA_, TB_)                                                                       \
-    if constexpr ((TRANS || (!TA_ && !TB_)) && dw_tile_ok(BM, BK, NW, TA_) &&                   \
+    if constexpr ((TRANS || (!TA_ && !TB_)) && kDwCountOk && dw_tile_ok(BM, BK, NW, TA_) &&     \
                   dw_tile_ok(BN, BK, NW, !TB_)) {                                               \
         if (p.ta == TA_ && p.tb == TB_) {                                                       \
             GEMM_RING(true, true, false, TA_, TB_);                                             \
@@ -1023,6 +1028,9 @@ const ConfigEntry kMfmaConfigs[] = {
     {"mfma3d_128x256x16_w2x4_swz_il", launch_mfma<128, 256, 16, 2, 4, -1, 0, 8, 3, true, true, true>, kCapTransposed},
     {"mfma3_64x128x16_w2x2_swz_il", launch_mfma<64, 128, 16, 2, 2, -1, 0, 8, 3, false, true, true>, kCapTransposed},
     {"mfma2d_256x256x32_w2x4_swz_g8_il", launch_mfma<256, 256, 32, 2, 4, -1, 0, 8, 2, true, true, true>, kCapTransposed},
+    // 128 x 128 tiles with direct loads and two buffers (64 KiB: two
+    // workgroups per CU).
+    {"mfma2d_128x128x32_w2x2_swz_il", launch_mfma<128, 128, 32, 2, 2, -1, 0, 8, 2, true, true, true>, kCapTransposed},
     // K-groups (k4: four groups of 2 x 2 wavefronts, 16 per workgroup, each
     // group a quarter of every K-step): for shapes with about one tile per CU.
     {"mfma2d_64x64x128_w2x2_k4_swz", launch_mfma<64, 64, 128, 2, 2, -1, 0, 8, 2, true, true, false, 4>, kCapTransposed},
