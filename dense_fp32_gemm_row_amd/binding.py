@@ -92,6 +92,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gemm_f32_select.restype = _int
     lib.gemm_f32_select.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64,
                                     ctypes.POINTER(_int), ctypes.POINTER(_int)]
+    lib.gemm_f32_plan.restype = _int
+    lib.gemm_f32_plan.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_int),
+                                  ctypes.POINTER(_int), ctypes.POINTER(_i64),
+                                  ctypes.POINTER(_int), ctypes.POINTER(_int)]
     lib.gemm_f32_abi_version.restype = _int
     lib.gemm_f32_abi_version.argtypes = []
     _LIB = lib
@@ -159,6 +163,19 @@ def gemm_f32_select(M, N, K, lda, ldb, ldc) -> tuple[int, int]:
     if rc != GEMM_F32_OK:
         raise GemmError(rc, gemm_f32_last_error())
     return v.value, c.value
+
+
+def gemm_f32_plan(M, N, K, lda, ldb, ldc) -> dict:
+    """How gemm_f32 runs one product: {"parts", "axis", "split", "configs": [(variant,
+    config_id), ...]} with one entry per launch."""
+    parts, axis, split = _int(), _int(), _i64()
+    v, c = (_int * 2)(), (_int * 2)()
+    rc = load().gemm_f32_plan(M, N, K, lda, ldb, ldc, ctypes.byref(parts), ctypes.byref(axis),
+                              ctypes.byref(split), v, c)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, gemm_f32_last_error())
+    return {"parts": parts.value, "axis": axis.value, "split": split.value,
+            "configs": [(v[i], c[i]) for i in range(parts.value)]}
 
 
 def gemm_f32_abi_version() -> int:

@@ -213,36 +213,114 @@ int validate(bool ta, bool tb, int64_t batch, int64_t M, int64_t N, int64_t K, c
 // not 16-byte aligned scale the rate by the candidate's measured factor.  A
 // batch multiplies the tiles.  Transposed operands consider only
 // configurations that take them.
+
+// Predicted microseconds of one candidate on a (batch of) M x N x K.
+double model_us(const ModelCandidate &m, int64_t batch, int64_t M, int64_t N, int64_t K,
+                bool aligned) {
+    const int64_t tiles = ((M + m.bm - 1) / m.bm) * ((N + m.bn - 1) / m.bn) * batch;
+    const int64_t n = (tiles + kModelCUs - 1) / kModelCUs;
+    const int level = static_cast<int>(n < m.nrates ? n : m.nrates);
+    const double rate = m.gflops_per_cu[level > 0 ? level - 1 : 0] * (aligned ? 1.0 : m.unaligned);
+    return static_cast<double>(n) * 2.0 * m.bm * m.bn * static_cast<double>(K) / (rate * 1e3);
+}
+
+// Whether model candidate m is compiled and, for transposed operands, takes them;
+// sets its configuration id.
+bool usable(const ModelCandidate &m, bool trans, int *id) {
+    int count = 0;
+    const ConfigEntry *cfgs = configs_of(GEMM_F32_VARIANT_MFMA, &count);
+    *id = find_config(GEMM_F32_VARIANT_MFMA, m.config);
+    return *id >= 0 && (!trans || (cfgs[*id].caps & kCapTransposed));
+}
+
+// The model's fastest candidate; returns its predicted microseconds.
+double best_candidate(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans, bool aligned,
+                      int *config) {
+    double best_t = 0.0;
+    *config = -1;
+    for (const ModelCandidate &m : kModel) {
+        int id = -1;
+        if (!usable(m, trans, &id)) continue;
+        const double t = model_us(m, batch, M, N, K, aligned);
+        if (*config < 0 || t < best_t) *config = id, best_t = t;
+    }
+    if (*config < 0) *config = 0;
+    return best_t;
+}
+
+bool exact_entry(int64_t M, int64_t N, int64_t K, int *variant, int *config) {
+    for (const TuneEntry &e : kTuneTable) {
+        if (e.M == M && e.N == N && e.K == K) {
+            const int id = find_config(e.variant, e.config);
+            if (id >= 0) {
+                *variant = e.variant;
+                *config = id;
+                return true;
+            }
+        }
+    }
+    return false;
+}
+
 void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant, int *config,
                    bool trans = false, bool aligned = true) {
-    if (batch == 1 && !trans) {
-        for (const TuneEntry &e : kTuneTable) {
-            if (e.M == M && e.N == N && e.K == K) {
-                const int id = find_config(e.variant, e.config);
-                if (id >= 0) {
-                    *variant = e.variant;
-                    *config = id;
-                    return;
+    if (batch == 1 && !trans && exact_entry(M, N, K, variant, config)) return;
+    *variant = GEMM_F32_VARIANT_MFMA;
+    best_candidate(batch, M, N, K, trans, aligned, config);
+}
+
+// How gemm_f32 runs one product: one launch, or two on complementary parts
+// of C.  Wave quantisation ("Tiling and Blocking for Reuse", choosing the
+// tile size: the tail of the last wave) can leave the last wave of large
+// tiles mostly empty, where small tiles lose per-CU rate everywhere.  A
+// split gives a first part of C rows (or columns) to large tiles in whole
+// waves and the rest to the model's choice for what remains: for each
+// candidate and each number w of waves (up to 64), the largest whole-tile
+// part with at most w * CUs tiles.  It is taken when the model predicts at
+// least kSplitGain less time, after kLaunchUs for the second launch.
+struct Plan {
+    int parts;            // 1 or 2
+    int axis;             // 0: split the rows of C, 1: its columns
+    int64_t split;        // rows (columns) of the first part
+    int variant[2], config[2];
+};
+constexpr double kLaunchUs = 5.0;
+constexpr double kSplitGain = 0.02;
+
+Plan plan_product(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
+    Plan plan{1, 0, 0, {GEMM_F32_VARIANT_MFMA, 0}, {0, 0}};
+    if (M <= 0 || N <= 0 || K <= 0) {  // nothing to split
+        select_config(1, M, N, K, &plan.variant[0], &plan.config[0], trans, aligned);
+        return plan;
+    }
+    if (!trans && exact_entry(M, N, K, &plan.variant[0], &plan.config[0])) return plan;
+    const double t1 = best_candidate(1, M, N, K, trans, aligned, &plan.config[0]);
+    double best_t = t1 * (1.0 - kSplitGain);
+    for (const ModelCandidate &m : kModel) {
+        int id = -1;
+        if (!usable(m, trans, &id)) continue;
+        for (int axis = 0; axis < 2; ++axis) {
+            const int64_t along = axis == 0 ? M : N, across = axis == 0 ? N : M;
+            const int64_t tile = axis == 0 ? m.bm : m.bn, other = axis == 0 ? m.bn : m.bm;
+            const int64_t lanes = (across + other - 1) / other;  // tiles per row (column) of tiles
+            for (int64_t w = 1; w <= 64; ++w) {
+                const int64_t first = (w * kModelCUs / lanes) * tile;
+                if (first <= 0) continue;
+                if (first >= along) break;
+                const int64_t m1 = axis == 0 ? first : M, n1 = axis == 0 ? N : first;
+                const int64_t m2 = axis == 0 ? M - first : M, n2 = axis == 0 ? N : N - first;
+                int c2 = -1;
+                const double t = model_us(m, 1, m1, n1, K, aligned) +
+                                 best_candidate(1, m2, n2, K, trans, aligned, &c2) + kLaunchUs;
+                if (t < best_t) {
+                    best_t = t;
+                    plan = Plan{2, axis, first, {GEMM_F32_VARIANT_MFMA, GEMM_F32_VARIANT_MFMA},
+                                {id, c2}};
                 }
             }
         }
     }
-    int count = 0;
-    const ConfigEntry *cfgs = configs_of(GEMM_F32_VARIANT_MFMA, &count);
-    int best = -1;
-    double best_t = 0.0;
-    for (const ModelCandidate &m : kModel) {
-        const int id = find_config(GEMM_F32_VARIANT_MFMA, m.config);
-        if (id < 0 || (trans && !(cfgs[id].caps & kCapTransposed))) continue;
-        const int64_t tiles = ((M + m.bm - 1) / m.bm) * ((N + m.bn - 1) / m.bn) * batch;
-        const int64_t n = (tiles + kModelCUs - 1) / kModelCUs;
-        const int conc = static_cast<int>(n < m.nrates ? n : m.nrates);
-        const double rate = m.gflops_per_cu[conc > 0 ? conc - 1 : 0] * (aligned ? 1.0 : m.unaligned);
-        const double t = static_cast<double>(n) * m.bm * m.bn * static_cast<double>(K) / rate;
-        if (best < 0 || t < best_t) best = id, best_t = t;
-    }
-    *variant = GEMM_F32_VARIANT_MFMA;
-    *config = best >= 0 ? best : 0;
+    return plan;
 }
 
 // Rows of A and B 16-byte aligned in every product (the direct-load kernels'
@@ -258,11 +336,18 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
         int64_t sb, float *C, int64_t ldc, int64_t sc, void *stream) {
     clear_error();
     int count = 0;
-    if (variant == -1) {  // the library's choice
+    Plan plan{1, 0, 0, {variant, variant}, {config_id, config_id}};
+    if (variant == -1) {  // the library's choice: one product may be split in two launches
         int rc = validate_sizes(M, N, K, lda, ldb, ldc, ta, tb);
         if (rc != GEMM_F32_OK) return rc;
-        select_config(batch > 0 ? batch : 1, M, N, K, &variant, &config_id, ta || tb,
-                      operands_aligned(A, lda, sa, B, ldb, sb));
+        const bool aligned = operands_aligned(A, lda, sa, B, ldb, sb);
+        if (batch == 1)
+            plan = plan_product(M, N, K, ta || tb, aligned);
+        else
+            select_config(batch > 0 ? batch : 1, M, N, K, &plan.variant[0], &plan.config[0],
+                          ta || tb, aligned);
+        variant = plan.variant[0];
+        config_id = plan.config[0];
     }
     const ConfigEntry *cfgs = configs_of(variant, &count);
     if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant);
@@ -294,7 +379,25 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
                         cfgs[config_id].name);
         const Problem p{static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), A, lda, B,
                         ldb, C, ldc, static_cast<int>(batch), sa, sb, sc, ta, tb};
-        err = cfgs[config_id].launch(p, s);
+        if (plan.parts == 1) {
+            err = cfgs[config_id].launch(p, s);
+        } else {  // the first rows (columns) of C, then the rest: sub-matrices of the operands
+            const int split = static_cast<int>(plan.split);
+            Problem first = p, rest = p;
+            if (plan.axis == 0) {
+                first.M = split;
+                rest.M = p.M - split;
+                rest.A = ta ? A + split : A + static_cast<int64_t>(split) * lda;
+                rest.C = C + static_cast<int64_t>(split) * ldc;
+            } else {
+                first.N = split;
+                rest.N = p.N - split;
+                rest.B = tb ? B + static_cast<int64_t>(split) * ldb : B + split;
+                rest.C = C + split;
+            }
+            err = cfgs[plan.config[0]].launch(first, s);
+            if (err == hipSuccess) err = cfgs[plan.config[1]].launch(rest, s);
+        }
     }
     if (err != hipSuccess)
         return fail(GEMM_F32_EHIP, "launch failed: %s", hipGetErrorString(err));
@@ -479,10 +582,30 @@ int gemm_f32_select(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, i
     if (rc != GEMM_F32_OK) return rc;
     if (variant == nullptr || config_id == nullptr)
         return fail(GEMM_F32_EINVAL, "NULL output pointer");
-    select_config(1, M, N, K, variant, config_id, false, lda % 4 == 0 && ldb % 4 == 0);
+    const Plan plan = plan_product(M, N, K, false, lda % 4 == 0 && ldb % 4 == 0);
+    *variant = plan.variant[0];
+    *config_id = plan.config[0];
     return GEMM_F32_OK;
 }
 
-int gemm_f32_abi_version(void) { return 1; }
+int gemm_f32_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                  int *parts, int *axis, int64_t *split, int *variant, int *config_id) {
+    clear_error();
+    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
+    if (rc != GEMM_F32_OK) return rc;
+    if (!parts || !axis || !split || !variant || !config_id)
+        return fail(GEMM_F32_EINVAL, "NULL output pointer");
+    const Plan plan = plan_product(M, N, K, false, lda % 4 == 0 && ldb % 4 == 0);
+    *parts = plan.parts;
+    *axis = plan.parts == 2 ? plan.axis : 0;
+    *split = plan.parts == 2 ? plan.split : (plan.axis == 0 ? M : N);
+    for (int i = 0; i < 2; ++i) {
+        variant[i] = plan.variant[i < plan.parts ? i : 0];
+        config_id[i] = plan.config[i < plan.parts ? i : 0];
+    }
+    return GEMM_F32_OK;
+}
+
+int gemm_f32_abi_version(void) { return 2; }
 
 }  // extern "C"

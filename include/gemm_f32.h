@@ -69,7 +69,9 @@ extern "C" {
  * selects for the shape ("Tiling and Blocking for Reuse", "choosing the tile
  * size"): a built-in table of shapes tuned by measurement on MI355X, and for
  * other shapes a cost model whose per-CU rates were measured there (it
- * accounts for how many tiles each CU receives and runs at once).
+ * accounts for how many tiles each CU receives and runs at once).  The model
+ * may split C in two parts with different tile sizes, run as two launches
+ * on `stream` (gemm_f32_plan reports how).
  *
  *   M, N, K    sizes, 0 <= M, N, K <= 2^31 - 1
  *   A, lda     M x K operand, lda >= max(1, K)
@@ -251,14 +253,33 @@ const char *gemm_f32_config_name(int variant, int config_id);
 
 /*
  * The variant and configuration gemm_f32 would run for these arguments
- * (sizes and leading dimensions only; no pointer is dereferenced).
- * Returns GEMM_F32_OK or GEMM_F32_EINVAL.
+ * (sizes and leading dimensions only; no pointer is dereferenced).  Where
+ * gemm_f32 splits the product in two launches (see gemm_f32_plan), the
+ * configuration of the first.  Returns GEMM_F32_OK or GEMM_F32_EINVAL.
  */
 int gemm_f32_select(int64_t M, int64_t N, int64_t K,
                     int64_t lda, int64_t ldb, int64_t ldc,
                     int *variant, int *config_id);
 
-/* ABI version of this header: 1. */
+/*
+ * How gemm_f32 runs one product with these sizes and leading dimensions:
+ * *parts = 1 (one launch of variant[0], config_id[0]) or 2.  With 2, C is
+ * split along *axis (0: rows, 1: columns) after *split rows (columns): the
+ * first part runs variant[0], config_id[0] and the rest variant[1],
+ * config_id[1], one launch each, in that order, on the same stream.  The
+ * split exists because the last wave of large output tiles can be mostly
+ * empty ("Tiling and Blocking for Reuse", choosing the tile size: tail
+ * effects); the first part takes large tiles in whole waves across all CUs
+ * and the rest the cost model's choice for what remains, when the model
+ * predicts at least 2% less time.  variant and config_id point to arrays of
+ * two; with one part both entries describe it.  Returns GEMM_F32_OK or
+ * GEMM_F32_EINVAL.
+ */
+int gemm_f32_plan(int64_t M, int64_t N, int64_t K,
+                  int64_t lda, int64_t ldb, int64_t ldc,
+                  int *parts, int *axis, int64_t *split, int *variant, int *config_id);
+
+/* ABI version of this header: 2 (2 added gemm_f32_plan). */
 int gemm_f32_abi_version(void);
 
 #ifdef __cplusplus

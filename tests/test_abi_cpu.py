@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert b.gemm_f32_abi_version() == 1
+    assert b.gemm_f32_abi_version() == 2
 
 
 def test_strerror(lib):
@@ -327,3 +327,25 @@ def test_header_serves_a_c_caller(lib, tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
     assert f"select mfma2d_256x256x32_w4x4_swz_g4_il {len(names)}" in run.stdout
+
+
+def test_split_plans(lib):
+    """gemm_f32 splits a product in two launches where the last wave of large
+    tiles would be mostly empty, never for tuned shapes or shapes that fill
+    whole waves, and the parts are whole tiles of the first part's
+    configuration; gemm_f32_select reports the first part."""
+    def plan(M, N, K):
+        return b.gemm_f32_plan(M, N, K, max(K, 1), N, N)
+
+    for M, N, K in [(3584, 3584, 3584), (4608, 4608, 4608), (3000, 3000, 1000), (4096, 11008, 4096)]:
+        p = plan(M, N, K)
+        assert p["parts"] == 2, (M, N, K, p)
+        name = b.gemm_f32_config_name(*p["configs"][0])
+        bm, bn = (int(x) for x in name.split("_")[1].split("x")[:2])
+        extent, tile = (M, bm) if p["axis"] == 0 else (N, bn)
+        assert 0 < p["split"] < extent and p["split"] % tile == 0, (name, p)
+        assert b.gemm_f32_select(M, N, K, K, N, N) == p["configs"][0]
+    for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096), (8192, 14336, 4096), (1000, 1023, 777),
+                    (256, 256, 256), (4608, 4608, 0)]:
+        p = plan(M, N, K)
+        assert p["parts"] == 1 and len(p["configs"]) == 1, (M, N, K, p)

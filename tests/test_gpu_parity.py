@@ -674,6 +674,39 @@ def test_splitk_one_split_is_plain_product():
 # full-size workloads in the benchmark's launch configuration
 # --------------------------------------------------------------------------
 
+SPLIT_SHAPES = [(3584, 3584, 3584), (3000, 3000, 1000), (4607, 4609, 1001), (1800, 9000, 1024)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=["x".join(map(str, s)) for s in SPLIT_SHAPES])
+@pytest.mark.parametrize("ops", ["NN", "TN", "NT"])
+def test_split_products(shape, ops):
+    """Products that gemm_f32 runs as two launches on complementary parts of
+    C (rows or columns, see gemm_f32_plan), with operands stored as given
+    and transposed, and with rows that are not 16-byte aligned (4607 x 4609
+    x 1001): sampled rows (including both sides of a row split) exact against
+    the oracle on integer inputs, a Freivalds check of all of C, and C inside
+    a NaN guard band."""
+    import torch
+
+    M, N, K = shape
+    plan = b.gemm_f32_plan(M, N, K, K, N, N)
+    if ops == "NN":
+        assert plan["parts"] == 2, plan
+    log(f"split product {M}x{N}x{K} {ops}: plan {plan}")
+    A, B = make_inputs(M, N, K, "int4", seed=70)
+    buf = torch.full((M, N + 3), float("nan"), device="cuda:0")
+    b.gemm(_stored(A, ops[0]), _stored(B, ops[1]), buf[:, :N])
+    assert bool(torch.isnan(buf[:, N:]).all()), "write outside C's columns"
+    C = to_host(buf[:, :N])
+    rows = set(sample_rows(M, count=12))
+    if plan["parts"] == 2 and plan["axis"] == 0:
+        rows |= {plan["split"] - 1, plan["split"]}
+    rows = sorted(rows)
+    ref32, _ = oracle_rows(A, B, rows)
+    assert_exact(C[rows], ref32, f"{shape} {ops}")
+    assert freivalds(A, B, C) <= 1e-5
+
+
 @pytest.mark.parametrize("wname", ["square4096", "square8192", "ffn", "square8000", "square8191",
                                    "ktail8100", "deepk"])
 def test_full_size_sampled(wname):
