@@ -224,13 +224,29 @@ double model_us(const ModelCandidate &m, int64_t batch, int64_t M, int64_t N, in
     return static_cast<double>(n) * 2.0 * m.bm * m.bn * static_cast<double>(K) / (rate * 1e3);
 }
 
-// Whether model candidate m is compiled and, for transposed operands, takes them;
-// sets its configuration id.
-bool usable(const ModelCandidate &m, bool trans, int *id) {
-    int count = 0;
-    const ConfigEntry *cfgs = configs_of(GEMM_F32_VARIANT_MFMA, &count);
-    *id = find_config(GEMM_F32_VARIANT_MFMA, m.config);
-    return *id >= 0 && (!trans || (cfgs[*id].caps & kCapTransposed));
+// Configuration ids of the model's candidates (-1: not compiled) and whether
+// each takes transposed operands, resolved once.
+constexpr int kModelSize = static_cast<int>(sizeof(kModel) / sizeof(kModel[0]));
+struct ModelIds {
+    int id[kModelSize];
+    bool trans[kModelSize];
+};
+const ModelIds &model_ids() {
+    static const ModelIds ids = [] {
+        ModelIds r{};
+        int count = 0;
+        const ConfigEntry *cfgs = configs_of(GEMM_F32_VARIANT_MFMA, &count);
+        for (int i = 0; i < kModelSize; ++i) {
+            r.id[i] = find_config(GEMM_F32_VARIANT_MFMA, kModel[i].config);
+            r.trans[i] = r.id[i] >= 0 && (cfgs[r.id[i]].caps & kCapTransposed);
+        }
+        return r;
+    }();
+    return ids;
+}
+bool usable(int i, bool trans) {
+    const ModelIds &ids = model_ids();
+    return ids.id[i] >= 0 && (!trans || ids.trans[i]);
 }
 
 // The model's fastest candidate; returns its predicted microseconds.
@@ -238,11 +254,10 @@ double best_candidate(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans
                       int *config) {
     double best_t = 0.0;
     *config = -1;
-    for (const ModelCandidate &m : kModel) {
-        int id = -1;
-        if (!usable(m, trans, &id)) continue;
-        const double t = model_us(m, batch, M, N, K, aligned);
-        if (*config < 0 || t < best_t) *config = id, best_t = t;
+    for (int i = 0; i < kModelSize; ++i) {
+        if (!usable(i, trans)) continue;
+        const double t = model_us(kModel[i], batch, M, N, K, aligned);
+        if (*config < 0 || t < best_t) *config = model_ids().id[i], best_t = t;
     }
     if (*config < 0) *config = 0;
     return best_t;
@@ -273,11 +288,14 @@ void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant,
 // of C.  Wave quantisation ("Tiling and Blocking for Reuse", choosing the
 // tile size: the tail of the last wave) can leave the last wave of large
 // tiles mostly empty, where small tiles lose per-CU rate everywhere.  A
-// split gives a first part of C rows (or columns) to large tiles in whole
-// waves and the rest to the model's choice for what remains: for each
-// candidate and each number w of waves (up to 64), the largest whole-tile
-// part with at most w * CUs tiles.  It is taken when the model predicts at
-// least kSplitGain less time, after kLaunchUs for the second launch.
+// split runs a first slab of C rows (or columns) with one candidate, sized
+// to whole waves of its tiles, and the rest with the model's choice for the
+// remaining shape: for each candidate and each number w of waves (up to
+// kSplitWaves), the largest whole-tile slab with at most w * CUs tiles.  It
+// is taken when the model predicts at least kSplitGain less time, after
+// kLaunchUs for the second launch.  Products the model puts under
+// kSplitMinUs are not searched: a split could save less there than the
+// search costs on the host.
 struct Plan {
     int parts;            // 1 or 2
     int axis;             // 0: split the rows of C, 1: its columns
@@ -286,8 +304,10 @@ struct Plan {
 };
 constexpr double kLaunchUs = 5.0;
 constexpr double kSplitGain = 0.02;
+constexpr int64_t kSplitWaves = 16;
+constexpr double kSplitMinUs = 100.0;
 
-Plan plan_product(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
+Plan search_plan(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
     Plan plan{1, 0, 0, {GEMM_F32_VARIANT_MFMA, 0}, {0, 0}};
     if (M <= 0 || N <= 0 || K <= 0) {  // nothing to split
         select_config(1, M, N, K, &plan.variant[0], &plan.config[0], trans, aligned);
@@ -295,15 +315,17 @@ Plan plan_product(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
     }
     if (!trans && exact_entry(M, N, K, &plan.variant[0], &plan.config[0])) return plan;
     const double t1 = best_candidate(1, M, N, K, trans, aligned, &plan.config[0]);
+    if (t1 < kSplitMinUs) return plan;
     double best_t = t1 * (1.0 - kSplitGain);
-    for (const ModelCandidate &m : kModel) {
-        int id = -1;
-        if (!usable(m, trans, &id)) continue;
+    for (int i = 0; i < kModelSize; ++i) {
+        if (!usable(i, trans)) continue;
+        const ModelCandidate &m = kModel[i];
+        const int id = model_ids().id[i];
         for (int axis = 0; axis < 2; ++axis) {
             const int64_t along = axis == 0 ? M : N, across = axis == 0 ? N : M;
             const int64_t tile = axis == 0 ? m.bm : m.bn, other = axis == 0 ? m.bn : m.bm;
             const int64_t lanes = (across + other - 1) / other;  // tiles per row (column) of tiles
-            for (int64_t w = 1; w <= 64; ++w) {
+            for (int64_t w = 1; w <= kSplitWaves; ++w) {
                 const int64_t first = (w * kModelCUs / lanes) * tile;
                 if (first <= 0) continue;
                 if (first >= along) break;
@@ -321,6 +343,23 @@ Plan plan_product(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
         }
     }
     return plan;
+}
+
+// search_plan with the last result of the calling thread kept: a loop over
+// one shape searches once.
+Plan plan_product(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
+    struct Key {
+        int64_t M, N, K;
+        bool trans, aligned;
+    };
+    thread_local Key last{-1, -1, -1, false, false};
+    thread_local Plan last_plan{};
+    if (M == last.M && N == last.N && K == last.K && trans == last.trans &&
+        aligned == last.aligned)
+        return last_plan;
+    last_plan = search_plan(M, N, K, trans, aligned);
+    last = Key{M, N, K, trans, aligned};
+    return last_plan;
 }
 
 // Rows of A and B 16-byte aligned in every product (the direct-load kernels'
