@@ -766,18 +766,24 @@ struct RingTile {
 
         if constexpr (KG > 1) {
             // Sum of the k-groups' partial tiles, in group order, through the
-            // A buffers (every wavefront is done with them after the first
-            // barrier): CAP groups per round write their accumulators, one
-            // 256-byte row per register, and group 0 adds them.
+            // LDS buffers (every wavefront is done with them after the first
+            // barrier): a wavefront's partial tile is one slot of PER_WAVE
+            // floats, one 256-byte row per register; slots fill the A buffers,
+            // then the B buffers.  CAP groups per round write their slots and
+            // group 0 adds them.
             constexpr int PER_WAVE = FM * FN * 16 * 64;
-            constexpr int CAP = (STAGES * TileA::SIZE) / (NWG * PER_WAVE);
+            constexpr int SLOTS_A = (STAGES * TileA::SIZE) / PER_WAVE;
+            constexpr int SLOTS = SLOTS_A + (STAGES * TileB::SIZE) / PER_WAVE;
+            constexpr int CAP = SLOTS / NWG;
             static_assert(CAP >= 1, "LDS room for one partial tile");
-            float *red = &sA[0][0];
+            auto slot = [&](int q) -> float * {
+                return q < SLOTS_A ? &sA[0][0] + q * PER_WAVE : &sB[0][0] + (q - SLOTS_A) * PER_WAVE;
+            };
 #pragma unroll
             for (int g0 = 1; g0 < KG; g0 += CAP) {
                 __syncthreads();
                 if (kg >= g0 && kg < g0 + CAP) {
-                    float *p = red + ((kg - g0) * NWG + wg) * PER_WAVE + lane;
+                    float *p = slot((kg - g0) * NWG + wg) + lane;
 #pragma unroll
                     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -789,7 +795,7 @@ struct RingTile {
                 if (kg == 0) {
 #pragma unroll
                     for (int g = 0; g < CAP && g0 + g < KG; ++g) {
-                        const float *p = red + (g * NWG + wg) * PER_WAVE + lane;
+                        const float *p = slot(g * NWG + wg) + lane;
 #pragma unroll
                         for (int i = 0; i < FM; ++i)
 #pragma unroll
