@@ -284,8 +284,8 @@ void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant,
     best_candidate(batch, M, N, K, trans, aligned, config);
 }
 
-// How gemm_f32 runs one product: one launch, or two on complementary parts
-// of C.  Wave quantisation ("Tiling and Blocking for Reuse", choosing the
+// How gemm_f32 runs one product, or every product of a strided batch alike:
+// one launch, or two on complementary parts of C.  Wave quantisation ("Tiling and Blocking for Reuse", choosing the
 // tile size: the tail of the last wave) can leave the last wave of large
 // tiles mostly empty, where small tiles lose per-CU rate everywhere.  A
 // split runs a first slab of C rows (or columns) with one candidate, sized
@@ -307,14 +307,16 @@ constexpr double kSplitGain = 0.02;
 constexpr int64_t kSplitWaves = 16;
 constexpr double kSplitMinUs = 100.0;
 
-Plan search_plan(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
+Plan search_plan(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
     Plan plan{1, 0, 0, {GEMM_F32_VARIANT_MFMA, 0}, {0, 0}};
-    if (M <= 0 || N <= 0 || K <= 0) {  // nothing to split
-        select_config(1, M, N, K, &plan.variant[0], &plan.config[0], trans, aligned);
+    if (M <= 0 || N <= 0 || K <= 0 || batch <= 0) {  // nothing to split
+        select_config(batch > 0 ? batch : 1, M, N, K, &plan.variant[0], &plan.config[0], trans,
+                      aligned);
         return plan;
     }
-    if (!trans && exact_entry(M, N, K, &plan.variant[0], &plan.config[0])) return plan;
-    const double t1 = best_candidate(1, M, N, K, trans, aligned, &plan.config[0]);
+    if (batch == 1 && !trans && exact_entry(M, N, K, &plan.variant[0], &plan.config[0]))
+        return plan;
+    const double t1 = best_candidate(batch, M, N, K, trans, aligned, &plan.config[0]);
     if (t1 < kSplitMinUs) return plan;
     double best_t = t1 * (1.0 - kSplitGain);
     for (int i = 0; i < kModelSize; ++i) {
@@ -324,7 +326,8 @@ Plan search_plan(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
         for (int axis = 0; axis < 2; ++axis) {
             const int64_t along = axis == 0 ? M : N, across = axis == 0 ? N : M;
             const int64_t tile = axis == 0 ? m.bm : m.bn, other = axis == 0 ? m.bn : m.bm;
-            const int64_t lanes = (across + other - 1) / other;  // tiles per row (column) of tiles
+            // tiles per row (column) of tiles, over the whole batch
+            const int64_t lanes = (across + other - 1) / other * batch;
             for (int64_t w = 1; w <= kSplitWaves; ++w) {
                 const int64_t first = (w * kModelCUs / lanes) * tile;
                 if (first <= 0) continue;
@@ -332,8 +335,12 @@ Plan search_plan(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
                 const int64_t m1 = axis == 0 ? first : M, n1 = axis == 0 ? N : first;
                 const int64_t m2 = axis == 0 ? M - first : M, n2 = axis == 0 ? N : N - first;
                 int c2 = -1;
-                const double t = model_us(m, 1, m1, n1, K, aligned) +
-                                 best_candidate(1, m2, n2, K, trans, aligned, &c2) + kLaunchUs;
+                const double t = model_us(m, batch, m1, n1, K, aligned) +
+                                 best_candidate(batch, m2, n2, K, trans, aligned, &c2) + kLaunchUs;
+                // one configuration in two launches only looks faster: each
+                // launch would count at the one-tile-per-CU rate, but the
+                // second still waits for the first and starts from cold
+                if (c2 == id) continue;
                 if (t < best_t) {
                     best_t = t;
                     plan = Plan{2, axis, first, {GEMM_F32_VARIANT_MFMA, GEMM_F32_VARIANT_MFMA},
@@ -347,18 +354,18 @@ Plan search_plan(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
 
 // search_plan with the last result of the calling thread kept: a loop over
 // one shape searches once.
-Plan plan_product(int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
+Plan plan_product(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
     struct Key {
-        int64_t M, N, K;
+        int64_t batch, M, N, K;
         bool trans, aligned;
     };
-    thread_local Key last{-1, -1, -1, false, false};
+    thread_local Key last{-1, -1, -1, -1, false, false};
     thread_local Plan last_plan{};
-    if (M == last.M && N == last.N && K == last.K && trans == last.trans &&
+    if (batch == last.batch && M == last.M && N == last.N && K == last.K && trans == last.trans &&
         aligned == last.aligned)
         return last_plan;
-    last_plan = search_plan(M, N, K, trans, aligned);
-    last = Key{M, N, K, trans, aligned};
+    last_plan = search_plan(batch, M, N, K, trans, aligned);
+    last = Key{batch, M, N, K, trans, aligned};
     return last_plan;
 }
 
@@ -376,15 +383,10 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
     clear_error();
     int count = 0;
     Plan plan{1, 0, 0, {variant, variant}, {config_id, config_id}};
-    if (variant == -1) {  // the library's choice: one product may be split in two launches
+    if (variant == -1) {  // the library's choice: the products may be split in two launches
         int rc = validate_sizes(M, N, K, lda, ldb, ldc, ta, tb);
         if (rc != GEMM_F32_OK) return rc;
-        const bool aligned = operands_aligned(A, lda, sa, B, ldb, sb);
-        if (batch == 1)
-            plan = plan_product(M, N, K, ta || tb, aligned);
-        else
-            select_config(batch > 0 ? batch : 1, M, N, K, &plan.variant[0], &plan.config[0],
-                          ta || tb, aligned);
+        plan = plan_product(batch, M, N, K, ta || tb, operands_aligned(A, lda, sa, B, ldb, sb));
         variant = plan.variant[0];
         config_id = plan.config[0];
     }
@@ -621,7 +623,7 @@ int gemm_f32_select(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, i
     if (rc != GEMM_F32_OK) return rc;
     if (variant == nullptr || config_id == nullptr)
         return fail(GEMM_F32_EINVAL, "NULL output pointer");
-    const Plan plan = plan_product(M, N, K, false, lda % 4 == 0 && ldb % 4 == 0);
+    const Plan plan = plan_product(1, M, N, K, false, lda % 4 == 0 && ldb % 4 == 0);
     *variant = plan.variant[0];
     *config_id = plan.config[0];
     return GEMM_F32_OK;
@@ -634,7 +636,7 @@ int gemm_f32_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int
     if (rc != GEMM_F32_OK) return rc;
     if (!parts || !axis || !split || !variant || !config_id)
         return fail(GEMM_F32_EINVAL, "NULL output pointer");
-    const Plan plan = plan_product(M, N, K, false, lda % 4 == 0 && ldb % 4 == 0);
+    const Plan plan = plan_product(1, M, N, K, false, lda % 4 == 0 && ldb % 4 == 0);
     *parts = plan.parts;
     *axis = plan.parts == 2 ? plan.axis : 0;
     *split = plan.parts == 2 ? plan.split : (plan.axis == 0 ? M : N);

@@ -136,7 +136,9 @@ int gemm_f32_variant(int variant, int config_id,
  *
  * No C region may overlap any A or B region (checked on the address ranges
  * spanned by the whole batch).  The configuration is chosen from the shape
- * of one product and the total number of tiles.  Returns as gemm_f32.
+ * of one product and the total number of tiles; every product may be split
+ * in two parts as gemm_f32 splits one (two launches over the whole batch).
+ * Returns as gemm_f32.
  */
 int gemm_f32_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                              const float *A, int64_t lda, int64_t strideA,

@@ -707,6 +707,34 @@ def test_split_products(shape, ops):
     assert freivalds(A, B, C) <= 1e-5
 
 
+SPLIT_BATCHES = [(2, 3840, 3840, 1024), (2, 3328, 3328, 1024), (2, 3584, 3584, 1024)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_BATCHES, ids=["x".join(map(str, s)) for s in SPLIT_BATCHES])
+def test_split_batches(shape):
+    """Strided batches whose products the library splits in two parts (rows
+    for 3584^2 x 1024, columns for 3328^2 x 1024 and 3840^2 x 1024):
+    sampled rows of every product exact against the oracle on integer
+    inputs, a Freivalds check of every product, and every C inside a NaN
+    guard band."""
+    import torch
+
+    nb, M, N, K = shape
+    log(f"split batch {shape}")
+    A, B = make_inputs(nb * M, N, K, "int4", seed=71)
+    A3 = A.reshape(nb, M, K)
+    B3 = np.stack([B, (B[::-1] * -1).copy()])
+    buf = torch.full((nb, M, N + 3), float("nan"), device="cuda:0")
+    b.gemm_batched(to_dev(A3), to_dev(B3), buf[:, :, :N])
+    assert bool(torch.isnan(buf[:, :, N:]).all()), "write outside C's columns"
+    got = to_host(buf[:, :, :N])
+    rows = sorted(set(sample_rows(M, count=10)))
+    for i in range(nb):
+        ref32, _ = oracle_rows(A3[i], B3[i], rows)
+        assert_exact(got[i][rows], ref32, f"{shape} product {i}")
+        assert freivalds(A3[i], B3[i], got[i]) <= 1e-5
+
+
 @pytest.mark.parametrize("wname", ["square4096", "square8192", "ffn", "square8000", "square8191",
                                    "ktail8100", "deepk"])
 def test_full_size_sampled(wname):
