@@ -345,9 +345,12 @@ def main() -> int:
     if args.stages:
         return run_stages(args, w, A, B, dA, dB, dC, stream, flops)
 
+    plan = None
     if args.variant is None:
-        v, c = (binding.gemm_f32_select(M, N, K, K, N, N) if nb == 1 and args.ops == "NN"
-                else (None, None))
+        v, c = None, None
+        if nb == 1 and args.ops == "NN":
+            plan = binding.gemm_f32_plan(M, N, K, K, N, N)
+            v, c = plan["configs"][0]
     else:
         v = binding.VARIANTS[args.variant]
         if args.config:
@@ -358,6 +361,10 @@ def main() -> int:
             c = 0
     cname = (binding.gemm_f32_config_name(v, c) if v is not None
              else f"library choice ({'batched ' if nb > 1 else ''}{args.ops})")
+    if plan is not None and plan["parts"] == 2:  # two launches on complementary parts of C
+        part = "rows" if plan["axis"] == 0 else "columns"
+        cname = (f"{cname} ({part} below {plan['split']}) + "
+                 f"{binding.gemm_f32_config_name(*plan['configs'][1])}")
     log(f"kernel {cname}")
 
     if args.splitk is not None:
