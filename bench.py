@@ -363,7 +363,7 @@ def main() -> int:
              else f"library choice ({'batched ' if nb > 1 else ''}{args.ops})")
     if plan is not None and plan["parts"] == 2:  # two launches on complementary parts of C
         part = "rows" if plan["axis"] == 0 else "columns"
-        cname = (f"{cname} ({part} below {plan['split']}) + "
+        cname = (f"{cname} (first {plan['split']} {part}) + "
                  f"{binding.gemm_f32_config_name(*plan['configs'][1])}")
     log(f"kernel {cname}")
 
