@@ -735,6 +735,61 @@ def test_split_batches(shape):
         assert freivalds(A3[i], B3[i], got[i]) <= 1e-5
 
 
+def _random_case(rng):
+    """One seeded random problem: sizes, leading-dimension padding, operand
+    forms, batch and kernel (the library's choice or a random MFMA
+    configuration that takes the operand forms)."""
+    M, N, K = (int(x) for x in rng.integers(1, 700, size=3))
+    ops = str(rng.choice(["NN", "NT", "TN", "TT"]))
+    nb = int(rng.integers(1, 4))
+    pads = [int(x) for x in rng.integers(0, 6, size=3)]
+    if rng.random() < 0.4:
+        kernel = (None, -1, "select")
+    else:
+        pool = [k for k in MFMA_CONFIGS if ops == "NN" or k[2] in TRANS_CAPABLE]
+        kernel = pool[int(rng.integers(0, len(pool)))]
+    return M, N, K, ops, nb, pads, kernel
+
+
+def _stored_batch(X3: np.ndarray, op: str, pad: int):
+    """Device batch holding op(X_b) = X_b: each matrix stored as given (or as
+    its transpose) with `pad` extra floats per row, as a strided view."""
+    import torch
+
+    S = X3 if op == "N" else np.ascontiguousarray(np.swapaxes(X3, 1, 2))
+    nb, r, c = S.shape
+    buf = np.zeros((nb, r, c + pad), dtype=np.float32)
+    buf[:, :, :c] = S
+    dev = torch.from_numpy(buf).to("cuda:0")[:, :, :c]
+    return dev if op == "N" else dev.transpose(1, 2)
+
+
+def test_random_problems_exact():
+    """200 seeded random problems (sizes up to 700, padded rows, all operand
+    forms, batches of 1 to 3, the library's choice or a random MFMA
+    configuration) on integer inputs: every product exact against the
+    oracle, and C's padding untouched."""
+    import torch
+
+    rng = np.random.default_rng(2024)
+    for case in range(200):
+        M, N, K, ops, nb, pads, (v, c, name) = _random_case(rng)
+        log(f"random case {case}: {nb} x {M}x{N}x{K} {ops} pads {pads} on {name}")
+        A = rng.integers(-4, 5, size=(nb, M, K)).astype(np.float32)
+        B = rng.integers(-4, 5, size=(nb, K, N)).astype(np.float32)
+        dA, dB = _stored_batch(A, ops[0], pads[0]), _stored_batch(B, ops[1], pads[1])
+        buf = torch.full((nb, M, N + pads[2]), float("nan"), device="cuda:0")
+        out = buf[:, :, :N]
+        if nb == 1:
+            b.gemm(dA[0], dB[0], out[0], variant=v, config=c)
+        else:
+            b.gemm_batched(dA, dB, out, variant=v, config=c)
+        got = to_host(buf)
+        assert np.isnan(got[:, :, N:]).all(), f"case {case}: write outside C's columns"
+        for i in range(nb):
+            assert_exact(got[i, :, :N], oracle.gemm(A[i], B[i]), f"case {case} product {i} on {name}")
+
+
 @pytest.mark.parametrize("wname", ["square4096", "square8192", "ffn", "square8000", "square8191",
                                    "ktail8100", "deepk"])
 def test_full_size_sampled(wname):
