@@ -767,8 +767,9 @@ def _stored_batch(X3: np.ndarray, op: str, pad: int):
 def test_random_problems_exact():
     """200 seeded random problems (sizes up to 700, padded rows, all operand
     forms, batches of 1 to 3, the library's choice or a random MFMA
-    configuration) on integer inputs: every product exact against the
-    oracle, and C's padding untouched."""
+    configuration, a quarter of the single row-major products as split-K)
+    on integer inputs: every product exact against the oracle, and C's
+    padding untouched."""
     import torch
 
     rng = np.random.default_rng(2024)
@@ -780,7 +781,11 @@ def test_random_problems_exact():
         dA, dB = _stored_batch(A, ops[0], pads[0]), _stored_batch(B, ops[1], pads[1])
         buf = torch.full((nb, M, N + pads[2]), float("nan"), device="cuda:0")
         out = buf[:, :, :N]
-        if nb == 1:
+        if nb == 1 and ops == "NN" and rng.random() < 0.25:  # split-K with 2 to 7 splits
+            splits = int(rng.integers(2, 8))
+            log(f"  as split-K with {splits} splits")
+            b.gemm_splitk(dA[0], dB[0], splits, out[0], variant=v, config=c)
+        elif nb == 1:
             b.gemm(dA[0], dB[0], out[0], variant=v, config=c)
         else:
             b.gemm_batched(dA, dB, out, variant=v, config=c)
