@@ -795,6 +795,42 @@ def test_random_problems_exact():
             assert_exact(got[i, :, :N], oracle.gemm(A[i], B[i]), f"case {case} product {i} on {name}")
 
 
+def test_random_large_problems():
+    """10 seeded random products large enough for the library to split some
+    of them in two launches (M, N 2000-6000, K 500-3000, all operand forms,
+    padded rows), library's choice, integer inputs: sampled rows (both sides
+    of a row split) exact against the oracle, and a Freivalds check."""
+    import torch
+
+    rng = np.random.default_rng(77)
+    splits = 0
+    for case in range(10):
+        M, N = (int(x) for x in rng.integers(2000, 6001, size=2))
+        K = int(rng.integers(500, 3001))
+        ops = str(rng.choice(["NN", "NT", "TN", "TT"]))
+        pads = [int(x) for x in rng.integers(0, 5, size=3)]
+        plan = b.gemm_f32_plan(M, N, K, K + pads[0], N + pads[1], N + pads[2])
+        splits += plan["parts"] == 2
+        log(f"large random case {case}: {M}x{N}x{K} {ops} pads {pads} plan {plan}")
+        A = rng.integers(-4, 5, size=(1, M, K)).astype(np.float32)
+        B = rng.integers(-4, 5, size=(1, K, N)).astype(np.float32)
+        dA, dB = _stored_batch(A, ops[0], pads[0])[0], _stored_batch(B, ops[1], pads[1])[0]
+        buf = torch.full((M, N + pads[2]), float("nan"), device="cuda:0")
+        b.gemm(dA, dB, buf[:, :N])
+        got = to_host(buf)
+        assert np.isnan(got[:, N:]).all(), f"case {case}: write outside C's columns"
+        C = got[:, :N]
+        rows = set(sample_rows(M, count=8))
+        if plan["parts"] == 2 and plan["axis"] == 0:
+            rows |= {plan["split"] - 1, plan["split"]}
+        rows = sorted(rows)
+        ref32, _ = oracle_rows(A[0], B[0], rows)
+        assert_exact(C[rows], ref32, f"large case {case}")
+        assert freivalds(A[0], B[0], C) <= 1e-5
+        del dA, dB, buf
+    log(f"{splits} of 10 large random products were split (row-major plan)")
+
+
 @pytest.mark.parametrize("wname", ["square4096", "square8192", "ffn", "square8000", "square8191",
                                    "ktail8100", "deepk"])
 def test_full_size_sampled(wname):
