@@ -96,7 +96,8 @@ int gemm_f32(int64_t M, int64_t N, int64_t K,
  *   variant    one of GEMM_F32_VARIANT_*
  *   config_id  index of a compiled tile configuration of that variant
  *              (0 <= config_id < gemm_f32_config_count(variant)), or -1 for
- *              the configuration the library would pick for this shape
+ *              the configuration the library would pick for this shape as
+ *              one launch (never split as gemm_f32 may split it)
  *
  * The naive kernel follows "Tiled Matrix Multiplication in CUDA", section 5
  * (with the bounds guard of "Tiling and Blocking for Reuse"); the LDS kernel
