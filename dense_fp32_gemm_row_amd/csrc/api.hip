@@ -209,8 +209,10 @@ int validate(bool ta, bool tb, int64_t batch, int64_t M, int64_t N, int64_t K, c
 // n = ceil(tiles / CUs) tiles of a candidate, and the candidate's measured
 // per-CU rate for a share of min(n, nrates) tiles (the last level also
 // stands for larger shares, whose tiles queue behind those that fit at
-// once) gives the predicted time n * 2 * bm * bn * K / rate; rows that are
-// not 16-byte aligned scale the rate by the candidate's measured factor.  A
+// once) gives the predicted time n * 2 * bm * bn * (K + k0) / rate, k0 being
+// the tile's fixed cost (prologue, and stores of C that no other
+// workgroup's math hides) in k; rows that are not 16-byte aligned scale the
+// rate by the candidate's measured factor.  A
 // batch multiplies the tiles.  Transposed operands consider only
 // configurations that take them.
 
@@ -221,7 +223,8 @@ double model_us(const ModelCandidate &m, int64_t batch, int64_t M, int64_t N, in
     const int64_t n = (tiles + kModelCUs - 1) / kModelCUs;
     const int level = static_cast<int>(n < m.nrates ? n : m.nrates);
     const double rate = m.gflops_per_cu[level > 0 ? level - 1 : 0] * (aligned ? 1.0 : m.unaligned);
-    return static_cast<double>(n) * 2.0 * m.bm * m.bn * static_cast<double>(K) / (rate * 1e3);
+    return static_cast<double>(n) * 2.0 * m.bm * m.bn * (static_cast<double>(K) + m.k0) /
+           (rate * 1e3);
 }
 
 // Configuration ids of the model's candidates (-1: not compiled) and whether

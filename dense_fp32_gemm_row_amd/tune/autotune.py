@@ -14,7 +14,11 @@ shapes not in the table: every candidate of the table's "model" section runs
 on the calibration shapes below, and for each shape a CU's share is
 n = ceil(tiles / cus) tiles; the per-CU rate 2 * bm * bn * K * n /
 (time - launch floor) is collected at level min(n, len(gflops_per_cu)), and
-each entry of gflops_per_cu becomes the median of its level.  The number of
+each entry of gflops_per_cu becomes the median of its level.  A tile also
+has a fixed cost, its prologue and the stores of C that no other
+workgroup's math hides, counted as k0 more k: on the short-K shapes below
+k0 is the median of what the time needs beyond K at those rates, and the
+rates are then fitted again with K + k0.  The number of
 levels per candidate is set in the table (at least its occupancy, and two
 for a candidate that fits one tile per CU, since one tile per CU runs
 faster per CU than several in turn).  `unaligned` is the median ratio of
@@ -65,6 +69,9 @@ CAL_SHAPES = ([(n, n, 8192) for n in (512, 768, 1024, 1280, 1536, 1792)] +
               [(1024, 8192, 8192), (8192, 1024, 4096), (2048, 2048, 8192), (4096, 2048, 1024),
                (3000, 3000, 3000)])
 CAL_UNALIGNED = [(1000, 1023, 7777), (2049, 2049, 2049), (3001, 3001, 3001)]
+# short K and many output tiles: where a tile's fixed cost (its prologue, and
+# the stores of C that no other workgroup's math hides) shows
+CAL_SHORTK = [(8192, 8192, 64), (8192, 8192, 128), (16384, 16384, 128), (16384, 16384, 256)]
 
 
 def calibrate_model(binding, model: dict, budget_ms: float) -> dict:
@@ -76,7 +83,7 @@ def calibrate_model(binding, model: dict, budget_ms: float) -> dict:
 
     cus = int(model["cus"])
     times: dict[tuple, float] = {}
-    for M, N, K in CAL_SHAPES + CAL_UNALIGNED + [(1, 1, 1)]:
+    for M, N, K in CAL_SHAPES + CAL_UNALIGNED + CAL_SHORTK + [(1, 1, 1)]:
         g = torch.Generator(device="cuda").manual_seed(0)
         dA = torch.rand((M, K), device="cuda", generator=g)
         dB = torch.rand((K, N), device="cuda", generator=g)
@@ -98,21 +105,39 @@ def calibrate_model(binding, model: dict, budget_ms: float) -> dict:
         levels = len(cand["gflops_per_cu"])
         floor = times[(cfg, 1, 1, 1)]
 
-        def rate(M, N, K):
-            tiles = math.ceil(M / bm) * math.ceil(N / bn)
-            n = math.ceil(tiles / cus)
-            ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
-            return min(n, levels), 2.0 * bm * bn * K * n / (ms * 1e-3) / 1e9
+        def share(M, N):
+            n = math.ceil(math.ceil(M / bm) * math.ceil(N / bn) / cus)
+            return n, min(n, levels)
 
-        groups: dict[int, list[float]] = {}
-        for shape in CAL_SHAPES:
-            level, r = rate(*shape)
-            groups.setdefault(level, []).append(r)
-        rates = []
-        for level in range(1, levels + 1):  # a level with no shape inherits the one below
-            rates.append(round(statistics.median(groups[level]), 1) if level in groups else rates[-1])
-        ratios = [r / rates[level - 1] for level, r in (rate(*s) for s in CAL_UNALIGNED)]
-        out["candidates"].append({**cand, "gflops_per_cu": rates,
+        def fit_rates(k0):
+            groups: dict[int, list[float]] = {}
+            for M, N, K in CAL_SHAPES:
+                n, level = share(M, N)
+                ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
+                groups.setdefault(level, []).append(2.0 * bm * bn * (K + k0) * n / (ms * 1e-3) / 1e9)
+            rates = []
+            for level in range(1, levels + 1):  # a level with no shape inherits the one below
+                rates.append(statistics.median(groups[level]) if level in groups else rates[-1])
+            return rates
+
+        def fit_k0(rates):
+            extra = []
+            for M, N, K in CAL_SHORTK:
+                n, level = share(M, N)
+                ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
+                extra.append(ms * 1e-3 * rates[level - 1] * 1e9 / (n * 2.0 * bm * bn) - K)
+            return max(0.0, statistics.median(extra))
+
+        k0 = fit_k0(fit_rates(0.0))
+        rates = fit_rates(k0)
+        k0 = fit_k0(rates)
+        ratios = []
+        for M, N, K in CAL_UNALIGNED:
+            n, level = share(M, N)
+            ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
+            ratios.append(2.0 * bm * bn * (K + k0) * n / (ms * 1e-3) / 1e9 / rates[level - 1])
+        out["candidates"].append({**cand, "gflops_per_cu": [round(r, 1) for r in rates],
+                                  "k0": round(k0, 1),
                                   "unaligned": round(min(1.0, statistics.median(ratios)), 3)})
     return out
 

@@ -43,12 +43,14 @@ def render(table: dict) -> str:
         '    {-1, -1, -1, 3, ""},',
         "};",
         "// Cost model for shapes not listed (see tune/table.json): per-CU",
-        "// throughput of each candidate with 1, 2, ... of its tiles on a CU.",
+        "// throughput of each candidate with 1, 2, ... of its tiles on a CU, and",
+        "// a tile's fixed cost as k0 more k.",
         "struct ModelCandidate {",
         "    const char *config;",
         "    int bm, bn, nrates;",
         "    float gflops_per_cu[4];",
         "    float unaligned;",
+        "    float k0;",
         "};",
         f'constexpr int kModelCUs = {int(table["model"]["cus"])};',
         "constexpr ModelCandidate kModel[] = {",
@@ -59,7 +61,7 @@ def render(table: dict) -> str:
             raise ValueError(f"{c['config']}: 1 to 4 rates")
         padded = ", ".join(f"{x:.1f}f" for x in rates + [rates[-1]] * (4 - len(rates)))
         lines.append(f'    {{"{c["config"]}", {int(c["bm"])}, {int(c["bn"])}, {len(rates)}, '
-                     f'{{{padded}}}, {float(c["unaligned"]):.3f}f}},')
+                     f'{{{padded}}}, {float(c["unaligned"]):.3f}f, {float(c.get("k0", 0.0)):.1f}f}},')
     lines += [
         "};",
         "}  // namespace gemm_f32_impl",
