@@ -65,9 +65,11 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kLdsBytes = 160 * 1024;  // LDS available to one workgroup on gfx950
 
-// Four consecutive floats of one row starting at column `col`: a 16-byte load
-// when the row is 16-byte aligned (VEC), zeros outside [0, limit) and for
-// rows that do not exist (GUARD).
+// Four consecutive floats of one row starting at column `col`, zeros outside
+// [0, limit) and for rows that do not exist (GUARD).  Four in-range floats are
+// one 16-byte load: an aligned one when the row is 16-byte aligned (VEC),
+// else four 4-byte loads that the compiler merges into one load, which
+// global memory accepts at 4-byte alignment.
 template <bool GUARD, bool VEC>
 __device__ __forceinline__ float4 load_row4(const float *row_ptr, int col, int limit, bool row_ok) {
     if constexpr (!GUARD) {
@@ -76,8 +78,9 @@ __device__ __forceinline__ float4 load_row4(const float *row_ptr, int col, int l
     } else {
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (row_ok) {
-            if (VEC && col + 3 < limit) {
-                v = *reinterpret_cast<const float4 *>(row_ptr + col);
+            if (col + 3 < limit) {
+                if constexpr (VEC) v = *reinterpret_cast<const float4 *>(row_ptr + col);
+                else v = make_float4(row_ptr[col], row_ptr[col + 1], row_ptr[col + 2], row_ptr[col + 3]);
             } else {
                 if (col + 0 < limit) v.x = row_ptr[col + 0];
                 if (col + 1 < limit) v.y = row_ptr[col + 1];

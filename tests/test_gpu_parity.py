@@ -232,6 +232,42 @@ def test_offsets_beyond_2_31(v, c, name, huge_strided):
     assert_exact(to_host(out), oracle.gemm(A, B), name)
 
 
+@pytest.fixture(scope="module")
+def huge_unaligned():
+    """Operands whose rows are not 16-byte aligned and lie so far apart that
+    a tile's offsets pass 2^29 floats (the range of 4-byte buffer loads):
+    A has 5 rows lda = 2^27 + 3 floats apart, B 67 rows ldb = 2^22 + 1
+    floats apart (about 3.2 GB of device memory)."""
+    import torch
+
+    M, N, K = 5, 9, 67
+    lda, ldb = (1 << 27) + 3, (1 << 22) + 1
+    A, B = make_inputs(M, N, K, "int4", seed=43)
+    bufA = torch.empty((M - 1) * lda + K, dtype=torch.float32, device="cuda:0")
+    bufB = torch.empty((K - 1) * ldb + N, dtype=torch.float32, device="cuda:0")
+    dA = bufA.as_strided((M, K), (lda, 1))
+    dB = bufB.as_strided((K, N), (ldb, 1))
+    dA.copy_(to_dev(A))
+    dB.copy_(to_dev(B))
+    yield A, B, dA, dB
+    del dA, dB, bufA, bufB
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_unaligned_rows_register_staging(v, c, name, huge_unaligned):
+    """Rows not 16-byte aligned beyond the 4-byte direct loads' range: the
+    register-staged loads, 16 bytes at 4-byte alignment where four floats
+    are in range, zero fill per element at the edges of M, N and K."""
+    import torch
+
+    A, B, dA, dB = huge_unaligned
+    log(f"unaligned rows beyond 2^29 floats on {name}")
+    out = torch.full((A.shape[0], B.shape[1]), float("nan"), device="cuda:0")
+    b.gemm(dA, dB, out, variant=v, config=c)
+    assert_exact(to_host(out), oracle.gemm(A, B), name)
+
+
 # --------------------------------------------------------------------------
 # the small workloads in full, library choice and every MFMA configuration
 # --------------------------------------------------------------------------
