@@ -937,9 +937,14 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
                                stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,       \
                                tiles_m, tiles_n, GROUP_M, batch_of(p));                         \
     } while (0)
-    // Rows not 16-byte aligned: 4-byte direct loads with range-checked zero
-    // fill, where the tile shape allows it and every element offset (with a
-    // tile's overhang) stays below 2^29 floats, the buffers' 32-bit range.
+    // Edge tiles of 16-byte-aligned rows clamp their direct loads by whole
+    // 16-byte groups, which needs the k-major operands' row length (M for A
+    // transposed, N for B as stored) to be a multiple of 4.
+    const bool clamp_ok = !edge_mn || ((!p.ta || p.M % 4 == 0) && (p.tb || p.N % 4 == 0));
+    // Rows not 16-byte aligned, or edge tiles that cannot clamp: 4-byte
+    // direct loads with range-checked zero fill, where the tile shape allows
+    // it and every element offset (with a tile's overhang) stays below 2^29
+    // floats, the buffers' 32-bit range.
     if constexpr (DIRECT && PIPE > 0) {
         constexpr int NW = WM * WN * KG;
         const int64_t a_rows = p.ta ? p.K : p.M, a_cols = p.ta ? p.M : p.K;
@@ -947,7 +952,7 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
         constexpr int64_t kSpan = int64_t{1} << 29;
         const bool spans_ok = (a_rows + 256) * p.lda + a_cols + 256 < kSpan &&
                               (b_rows + 256) * p.ldb + b_cols + 256 < kSpan;
-        if (!vec && spans_ok) {
+        if ((!vec || !clamp_ok) && spans_ok) {
         // 4-byte loads issue R * BK / 64 instructions per operand and K-step;
         // with three or four buffers one or two K-steps of them stay in flight
         // at a barrier, which the 6-bit load counter must be able to express.
@@ -970,11 +975,9 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     }
     // Direct-load configurations with aligned rows keep direct loads for
     // any shape: loads past M or N are clamped into the operands (GUARD:
-    // guarded stores; k-major operand tiles need their row length, M for A
-    // transposed and N for B as stored, a multiple of 4), and a partial last
-    // K-step is staged at the end of the K loop.
+    // guarded stores), and a partial last K-step is staged at the end of the
+    // K loop.
     constexpr bool kDirectAny = DIRECT && PIPE > 0;
-    const bool clamp_ok = !edge_mn || ((!p.ta || p.M % 4 == 0) && (p.tb || p.N % 4 == 0));
     if (!edge_mn && !edge_k) {
         if (vec) GEMM_MFMA_LAUNCH(DIRECT, false, true);
         else GEMM_MFMA_LAUNCH(false, false, false);
