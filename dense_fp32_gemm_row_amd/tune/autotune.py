@@ -68,7 +68,8 @@ CAL_SHAPES = ([(n, n, 8192) for n in (512, 768, 1024, 1280, 1536, 1792)] +
               [(n, n, n) for n in (2048, 2560, 3072, 3584, 4096, 5120, 6144, 8192)] +
               [(1024, 8192, 8192), (8192, 1024, 4096), (2048, 2048, 8192), (4096, 2048, 1024),
                (3000, 3000, 3000)])
-CAL_UNALIGNED = [(1000, 1023, 7777), (2049, 2049, 2049), (3001, 3001, 3001), (4096, 4096, 4095)]
+CAL_UNALIGNED = [(1000, 1023, 7777), (2049, 2049, 2049), (3001, 3001, 3001), (4096, 4096, 4095),
+                 (8192, 8192, 2047)]
 # short K and many output tiles: where a tile's fixed cost (its prologue, and
 # the stores of C that no other workgroup's math hides) shows
 CAL_SHORTK = [(8192, 8192, 64), (8192, 8192, 128), (16384, 16384, 128), (16384, 16384, 256)]
