@@ -24,7 +24,10 @@
 //    16-byte-aligned rows, loads past M or N are clamped into the operand
 //    (they only feed outputs that are never stored) and a partial last
 //    K-step is staged through registers; without aligned rows, 4-byte
-//    buffer loads return zero for every element outside the operand.
+//    buffer loads return zero for every element outside the operand.  The
+//    pipelined kernel's register staging clamps its loads the same way over
+//    the whole K-steps and stages the K-step of the last k as a zero-filled
+//    tail, so its K loop has no per-element checks either.
 //
 // This file holds two kernels: the first MFMA kernel (gemm_mfma_kernel,
 // register staging, two LDS buffers) and the pipelined one
@@ -400,6 +403,41 @@ struct OperandTile {
         }
     }
 
+    // Clamped register staging (edge tiles without per-element checks),
+    // for K-steps that hold neither a k past K nor the operand's last k row
+    // (k-major flavour): every load stays inside the operand's storage, and
+    // the values of rows or columns past the R extent only feed outputs that
+    // are never stored.  Row flavour: a row past the extent loads the last
+    // row.  K-major flavour: a 4-column group that starts inside the extent
+    // loads as it is, its columns past the extent coming from the row's
+    // padding or the next row (a k row below the last one, so still inside
+    // the storage when ld >= 4); a group wholly past the extent loads the
+    // row's last group.  The slot's source is fixed for the tile; a K-step
+    // adds k0 (row flavour) or k0 rows (k-major).
+    const float *cp[L];
+    __device__ __forceinline__ void init_clamp() {
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            if constexpr (KMAJOR) {
+                const int last = (rlim - 1) & ~3;  // start of the last group inside the extent
+                const int col = r0 + co[i] < rlim ? r0 + co[i] : last;
+                cp[i] = X + static_cast<int64_t>(ro[i]) * ld + col;
+            } else {
+                const int row = r0 + ro[i] < rlim ? r0 + ro[i] : rlim - 1;
+                cp[i] = X + static_cast<int64_t>(row) * ld + co[i];
+            }
+        }
+    }
+    __device__ __forceinline__ void load_clamped(int k0) {
+        const int64_t step = KMAJOR ? static_cast<int64_t>(k0) * ld : k0;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const float *q = cp[i] + step;
+            if constexpr (VEC) reg[i] = *reinterpret_cast<const float4 *>(q);
+            else reg[i] = make_float4(q[0], q[1], q[2], q[3]);
+        }
+    }
+
     // Register staging of the tile of K-step starting at k0 (G: with zero
     // fill outside the operand; the direct-load kernels use it for a
     // partial last K-step).
@@ -567,8 +605,12 @@ struct OperandTile {
 // One output tile of the pipelined kernel: the K loop and the epilogue for
 // the tile at (m0, n0), with the LDS buffers of the workgroup.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
-          bool GUARD, bool VEC, bool TA, bool TB, bool IL, int KG = 1>
+          bool GUARD, bool VEC, bool TA, bool TB, bool IL, int KG = 1, bool CL = false>
 struct RingTile {
+    // CL: register staging of an edge launch with clamped loads over the
+    // whole K-steps and the partial last K-step as a zero-filled tail.
+    static_assert(!CL || (GUARD && !DIRECT), "clamped loads: register staging with edges");
+    static constexpr bool TAIL = (DIRECT && VEC) || CL;  // a partial last K-step runs after the loop
     static constexpr int NWG = WM * WN;  // wavefronts per k-group
     static constexpr int NW = NWG * KG, NT = 64 * NW;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -611,10 +653,17 @@ struct RingTile {
         TileB tb;
         ta.init(A, lda, m0, M, tid, wave, lane);
         tb.init(B, ldb, n0, N, tid, wave, lane);
+        if constexpr (CL) {
+            ta.init_clamp();
+            tb.init_clamp();
+        }
         auto load_step = [&](int k0, int buf) {
             if constexpr (DIRECT) {
                 ta.load_direct(k0, K, sA[buf]);
                 tb.load_direct(k0, K, sB[buf]);
+            } else if constexpr (CL) {
+                ta.load_clamped(k0);
+                tb.load_clamped(k0);
             } else {
                 ta.load(k0, K);
                 tb.load(k0, K);
@@ -664,7 +713,9 @@ struct RingTile {
         // with K / BK as the trip count the compiler recomputed the global
         // addresses with a 64-bit multiply every K-step instead of advancing
         // them, and the 16-wave kernels lost 11%.)
-        const int nk = (K + BK - 1) / BK - (DIRECT && VEC && (K % BK) ? 1 : 0);
+        // With clamped loads the K-step that holds the last k always goes to
+        // the tail, whole or partial.
+        const int nk = CL ? (K - 1) / BK : (K + BK - 1) / BK - (TAIL && (K % BK) ? 1 : 0);
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st) {
             if (st < nk) {
@@ -746,13 +797,13 @@ struct RingTile {
             cur = nxt;
         }
 
-        // Tail of the direct-load kernels: the partial last K-step, staged
-        // through registers with zero fill past K (and past the M / N edges),
-        // once all waves are done with the loop's buffers.  One exposed
-        // global-load latency per tile; its registers are not live in the
-        // loop.
-        if constexpr (DIRECT && VEC) {
-            if (K % BK) {
+        // Tail of the direct-load and clamped kernels: the partial last
+        // K-step, staged through registers with zero fill past K (and past
+        // the M / N edges), once all waves are done with the loop's buffers.
+        // One exposed global-load latency per tile; its registers are not
+        // live in the loop.
+        if constexpr (TAIL) {
+            if (CL || K % BK) {
                 ta.template load<true>(nk * BK, K);
                 tb.template load<true>(nk * BK, K);
                 __syncthreads();
@@ -868,14 +919,14 @@ struct RingTile {
 };
 
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
-          bool GUARD, bool VEC, bool TA, bool TB, bool IL, int KG>
+          bool GUARD, bool VEC, bool TA, bool TB, bool IL, int KG, bool CL>
 __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_mfma_ring_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n, int group_m, BatchArgs bt) {
     // DIRECT and GUARD together: direct loads clamped at the M and N edges
     // (see OperandTile) and guarded stores; K is whole K-steps.
-    using Full = RingTile<BM, BN, BK, WM, WN, PADA, PADB, STAGES, DIRECT, GUARD, VEC, TA, TB, IL, KG>;
+    using Full = RingTile<BM, BN, BK, WM, WN, PADA, PADB, STAGES, DIRECT, GUARD, VEC, TA, TB, IL, KG, CL>;
 
     __shared__ __align__(16) float sA[STAGES][Full::TileA::SIZE];
     __shared__ __align__(16) float sB[STAGES][Full::TileB::SIZE];
@@ -910,28 +961,28 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     const bool edge_mn = (p.M % BM) || (p.N % BN);
     const bool edge_k = (p.K % BK) != 0;
     const dim3 g(static_cast<unsigned>(grid)), b(NT);
-#define GEMM_RING(D, G, V, TA, TB)                                                              \
+#define GEMM_RING(D, G, V, TA, TB, CL_)                                                        \
     hipLaunchKernelGGL(                                                                         \
         (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, ((D) || PIPE < 4 ? PIPE : 3), D, G, \
-                               V, TA, TB, IL, KG>),                                             \
+                               V, TA, TB, IL, KG, CL_>),                                             \
         g, b, 0,                                                                                \
         stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, GROUP_M,   \
         batch_of(p))
-#define GEMM_RING_T(D, G, V)                                                                    \
+#define GEMM_RING_T(D, G, V, CL_)                                                               \
     do {                                                                                        \
         if constexpr (TRANS) {                                                                  \
-            if (p.ta && p.tb) GEMM_RING(D, G, V, true, true);                                   \
-            else if (p.ta) GEMM_RING(D, G, V, true, false);                                     \
-            else if (p.tb) GEMM_RING(D, G, V, false, true);                                     \
-            else GEMM_RING(D, G, V, false, false);                                              \
+            if (p.ta && p.tb) GEMM_RING(D, G, V, true, true, CL_);                              \
+            else if (p.ta) GEMM_RING(D, G, V, true, false, CL_);                                \
+            else if (p.tb) GEMM_RING(D, G, V, false, true, CL_);                                \
+            else GEMM_RING(D, G, V, false, false, CL_);                                         \
         } else {                                                                                \
-            GEMM_RING(D, G, V, false, false);                                                   \
+            GEMM_RING(D, G, V, false, false, CL_);                                              \
         }                                                                                       \
     } while (0)
-#define GEMM_MFMA_LAUNCH(D, G, V)                                                               \
+#define GEMM_MFMA_LAUNCH(D, G, V, CL_)                                                          \
     do {                                                                                        \
         if constexpr (PIPE > 0)                                                                 \
-            GEMM_RING_T(D, G, V);                                                               \
+            GEMM_RING_T(D, G, V, CL_);                                                          \
         else                                                                                    \
             hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, WM, WN, PADA, PADB, G, V>), g, b, 0, \
                                stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc,       \
@@ -962,7 +1013,7 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     if constexpr ((TRANS || (!TA_ && !TB_)) && kDwCountOk && dw_tile_ok(BM, BK, NW, TA_) &&     \
                   dw_tile_ok(BN, BK, NW, !TB_)) {                                               \
         if (p.ta == TA_ && p.tb == TB_) {                                                       \
-            GEMM_RING(true, true, false, TA_, TB_);                                             \
+            GEMM_RING(true, true, false, TA_, TB_, false);                                             \
             return hipGetLastError();                                                           \
         }                                                                                       \
     }
@@ -979,16 +1030,26 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     // K loop.
     constexpr bool kDirectAny = DIRECT && PIPE > 0;
     if (!edge_mn && !edge_k) {
-        if (vec) GEMM_MFMA_LAUNCH(DIRECT, false, true);
-        else GEMM_MFMA_LAUNCH(false, false, false);
+        if (vec) GEMM_MFMA_LAUNCH(DIRECT, false, true, false);
+        else GEMM_MFMA_LAUNCH(false, false, false, false);
     } else if (kDirectAny && vec && clamp_ok) {
         if constexpr (kDirectAny) {
-            if (edge_mn) GEMM_RING_T(true, true, true);
-            else GEMM_RING_T(true, false, true);
+            if (edge_mn) GEMM_RING_T(true, true, true, false);
+            else GEMM_RING_T(true, false, true, false);
         }
     } else {
-        if (vec) GEMM_MFMA_LAUNCH(false, true, true);
-        else GEMM_MFMA_LAUNCH(false, true, false);
+        // Register staging with edges: clamped loads (no per-element checks
+        // in the K loop) when every k-major operand's rows are at least 4
+        // floats apart, so that a group's reads past its row stay inside
+        // the operand.
+        const bool clamp_regs = (p.tb || p.ldb >= 4) && (!p.ta || p.lda >= 4);
+        if (clamp_regs) {
+            if (vec) GEMM_MFMA_LAUNCH(false, true, true, true);
+            else GEMM_MFMA_LAUNCH(false, true, false, true);
+        } else {
+            if (vec) GEMM_MFMA_LAUNCH(false, true, true, false);
+            else GEMM_MFMA_LAUNCH(false, true, false, false);
+        }
     }
 #undef GEMM_MFMA_LAUNCH
 #undef GEMM_RING_T

@@ -268,6 +268,43 @@ def test_unaligned_rows_register_staging(v, c, name, huge_unaligned):
     assert_exact(to_host(out), oracle.gemm(A, B), name)
 
 
+CLAMP_CASES = [  # M, N, K, lda, ldb: row lengths under 4 with rows 4 floats apart, odd strides
+    (5, 3, 37, 37, 4), (70, 2, 33, 35, 4), (3, 65, 20, 21, 66), (257, 259, 47, 49, 261),
+    (1, 4, 17, 17, 4), (33, 7, 16, 16, 7)]
+
+
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_clamped_edges_exact_storage(v, c, name):
+    """Edge tiles of register-staged kernels load clamped: rows past M or N
+    read the last row, 4-column groups past N the row's last group, and a
+    group that starts inside the row reads past its end (never in the last
+    k row, which the zero-filled tail stages).  Every operand is allocated to
+    exactly its last element; A transposed covers the k-major flavour of A."""
+    import torch
+
+    ops_list = ["NN", "TN"] if v == 3 and name in TRANS_CAPABLE else ["NN"]
+    for M, N, K, lda, ldb in CLAMP_CASES:
+        for ops in ops_list:
+            log(f"clamped edges {ops} {M}x{N}x{K} lda={lda} ldb={ldb} on {name}")
+            A, B = make_inputs(M, N, K, "int4", seed=61)
+            if ops[0] == "T":  # A stored K x M, rows lda' apart
+                lda_t = max(M, 4) if M < 4 else M + 1
+                bufA = torch.empty((K - 1) * lda_t + M, device="cuda:0")
+                stored = bufA.as_strided((K, M), (lda_t, 1))
+                stored.copy_(to_dev(np.ascontiguousarray(A.T)))
+                dA = stored.t()
+            else:
+                bufA = torch.empty((M - 1) * lda + K, device="cuda:0")
+                dA = bufA.as_strided((M, K), (lda, 1))
+                dA.copy_(to_dev(A))
+            bufB = torch.empty((K - 1) * ldb + N, device="cuda:0")
+            dB = bufB.as_strided((K, N), (ldb, 1))
+            dB.copy_(to_dev(B))
+            out = torch.full((M, N), float("nan"), device="cuda:0")
+            b.gemm(dA, dB, out, variant=v, config=c)
+            assert_exact(to_host(out), oracle.gemm(A, B), f"{name} {ops} {M}x{N}x{K}")
+
+
 # --------------------------------------------------------------------------
 # the small workloads in full, library choice and every MFMA configuration
 # --------------------------------------------------------------------------
