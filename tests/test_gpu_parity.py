@@ -441,7 +441,7 @@ BATCH_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4"), (1, 1, "lds_t32"),
         "mfma2p_256x256x32_w4x4_swz_pb0", "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz_g4",
         "mfma2d_256x256x32_w2x4_swz_g4_il", "mfma2d_256x256x32_w4x4_swz_g4_il",
         "mfma2d_64x64x128_w2x2_k4_swz", "mfma2d_64x64x64_w2x2_k4_swz",
-        "mfma3_256x256x16_w4x4_swz_g4_il")]
+        "mfma3_256x256x16_w4x4_swz_g4_il", "mfma2_64x64x64_w2x2_k4_swz")]
 
 
 def _run_batched(A3, B3, M, N, K, nb, sa, sb, sc, lda, ldb, ldc, kernel):
@@ -541,7 +541,7 @@ TRANS_CAPABLE = ["mfma2d_256x256x32_w4x4_swz", "mfma3d_256x128x32_w4x2_swz",
                  "mfma2d_256x256x32_w2x4_swz_g8_il", "mfma2d_256x256x32_w4x4_swz_g8_il",
                  "mfma2d_64x64x128_w2x2_k4_swz", "mfma2d_64x64x64_w2x2_k4_swz",
                  "mfma3d_64x64x64_w2x2_k4_swz", "mfma4d_64x64x64_w2x2_k4_swz",
-                 "mfma3_256x256x16_w4x4_swz_g4_il",
+                 "mfma3_256x256x16_w4x4_swz_g4_il", "mfma2_64x64x64_w2x2_k4_swz",
                  "mfma2d_128x128x32_w2x2_swz_il"]
 TRANS_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in TRANS_CAPABLE]
