@@ -372,12 +372,20 @@ Plan plan_product(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans, bo
     return last_plan;
 }
 
-// Rows of A and B 16-byte aligned in every product (the direct-load kernels'
-// fast path).
+// Rows of A and B 16-byte aligned in every product.
 bool operands_aligned(const float *A, int64_t lda, int64_t sa, const float *B, int64_t ldb,
                       int64_t sb) {
     return reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(B) % 16 == 0 &&
            lda % 4 == 0 && ldb % 4 == 0 && sa % 4 == 0 && sb % 4 == 0;
+}
+
+// The cost model's "aligned" class: where the direct-load kernels keep
+// 16-byte loads.  That takes 16-byte-aligned rows, and edge tiles clamp by
+// whole 16-byte groups, which needs the row length of each operand stored
+// k-major (N for B as stored, M for A transposed) to be a multiple of 4;
+// otherwise those kernels fall back to 4-byte loads, as for unaligned rows.
+bool direct_fast(bool rows_aligned, int64_t M, int64_t N, bool ta, bool tb) {
+    return rows_aligned && (tb || N % 4 == 0) && (!ta || M % 4 == 0);
 }
 
 int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, int64_t N,
@@ -389,7 +397,8 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
     if (variant == -1) {  // the library's choice: the products may be split in two launches
         int rc = validate_sizes(M, N, K, lda, ldb, ldc, ta, tb);
         if (rc != GEMM_F32_OK) return rc;
-        plan = plan_product(batch, M, N, K, ta || tb, operands_aligned(A, lda, sa, B, ldb, sb));
+        plan = plan_product(batch, M, N, K, ta || tb,
+                            direct_fast(operands_aligned(A, lda, sa, B, ldb, sb), M, N, ta, tb));
         variant = plan.variant[0];
         config_id = plan.config[0];
     }
@@ -410,7 +419,7 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
         if (config_id == -1) {
             int v = 0;
             select_config(batch, M, N, K, &v, &config_id, ta || tb,
-                          operands_aligned(A, lda, sa, B, ldb, sb));
+                          direct_fast(operands_aligned(A, lda, sa, B, ldb, sb), M, N, ta, tb));
             if (v != variant) {  // first configuration of the asked variant that fits
                 config_id = 0;
                 if (ta || tb)
@@ -542,7 +551,8 @@ int gemm_f32_splitk(int variant, int config_id, int64_t splits, int64_t M, int64
         return fail(GEMM_F32_EINVAL, "workspace overlaps A, B or C");
     // partial products: a strided batch over the K splits into the workspace
     int v = variant, c = config_id;
-    const bool aligned = operands_aligned(A, lda, len, B, ldb, static_cast<int64_t>(len) * ldb);
+    const bool aligned = direct_fast(
+        operands_aligned(A, lda, len, B, ldb, static_cast<int64_t>(len) * ldb), M, N, false, false);
     if (v == -1) select_config(used, M, N, len, &v, &c, false, aligned);
     int count = 0;
     const ConfigEntry *cfgs = configs_of(v, &count);
@@ -626,7 +636,8 @@ int gemm_f32_select(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, i
     if (rc != GEMM_F32_OK) return rc;
     if (variant == nullptr || config_id == nullptr)
         return fail(GEMM_F32_EINVAL, "NULL output pointer");
-    const Plan plan = plan_product(1, M, N, K, false, lda % 4 == 0 && ldb % 4 == 0);
+    const bool fast = direct_fast(lda % 4 == 0 && ldb % 4 == 0, M, N, false, false);
+    const Plan plan = plan_product(1, M, N, K, false, fast);
     *variant = plan.variant[0];
     *config_id = plan.config[0];
     return GEMM_F32_OK;
@@ -639,7 +650,8 @@ int gemm_f32_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int
     if (rc != GEMM_F32_OK) return rc;
     if (!parts || !axis || !split || !variant || !config_id)
         return fail(GEMM_F32_EINVAL, "NULL output pointer");
-    const Plan plan = plan_product(1, M, N, K, false, lda % 4 == 0 && ldb % 4 == 0);
+    const bool fast = direct_fast(lda % 4 == 0 && ldb % 4 == 0, M, N, false, false);
+    const Plan plan = plan_product(1, M, N, K, false, fast);
     *parts = plan.parts;
     *axis = plan.parts == 2 ? plan.axis : 0;
     *split = plan.parts == 2 ? plan.split : (plan.axis == 0 ? M : N);
