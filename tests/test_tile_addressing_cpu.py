@@ -1,0 +1,105 @@
+"""Host-side model of the clamped register staging in csrc/mfma.hip
+(OperandTile::init, init_clamp, load_clamped, and RingTile's split of K
+into whole K-steps plus a tail).
+
+Edge tiles ("Tiled GEMM: Matrix Multiplication in CUDA", section 7.1) must
+not read outside an operand, and every element that reaches a stored output
+must be the right one.  The kernel does not check elements inside its K
+loop; it relies on clamping, and this test checks the clamping rules over a
+grid of tile shapes, operand extents, K and leading dimensions:
+
+* every address the K loop loads lies inside the operand's storage,
+  (rows - 1) * ld + cols floats;
+* every in-range position of a staged tile holds its own element.
+
+The slot mapping restated here: element e = tid + i * NT of a tile with R
+rows (row flavour: R rows of BK k values; k-major flavour: BK k rows of R
+columns) is stored in 16-byte slots.  Row flavour: row e / (BK / 4), k
+column 4 (e % (BK / 4)).  K-major: k row e / (R / 4), column 4 (e % (R / 4)).
+"""
+
+import numpy as np
+import pytest
+
+# (R, BK, NT): tile extent, K-step, threads of the workgroup -- the staged
+# tiles of the configurations (256 x 256 x 16 with 16 wavefronts, 128 x 128 x
+# 16 and 64 x 64 x 16 with 4, the 64 x 64 x 64 k-group tile with 16, and an
+# 8-wavefront 256 x 256 x 16 tile)
+TILES = [(256, 16, 1024), (128, 16, 256), (64, 16, 256), (64, 64, 1024), (256, 16, 512)]
+EXTENTS = [1, 3, 4, 5, 63, 65, 255, 257, 774]
+KS = [1, 2, 15, 16, 17, 33, 64, 100]
+
+
+def slots(R, BK, NT, kmajor):
+    e = np.arange(R * BK // 4)  # one entry per 16-byte slot (tid + i * NT over all i)
+    assert (R * BK) % (4 * NT) == 0
+    if kmajor:
+        return e // (R // 4), (e % (R // 4)) * 4  # k row, column
+    return e // (BK // 4), (e % (BK // 4)) * 4    # row, k column
+
+
+def clamped_addresses(R, BK, NT, kmajor, rlim, K, ld):
+    """Addresses (first float of each 16-byte load) of every K-loop load of
+    every tile, and the logical (row, column) each of the 4 floats stands for
+    in the staged tile."""
+    ro, co = slots(R, BK, NT, kmajor)
+    nk = (K - 1) // BK  # whole K-steps in the loop; the step of the last k is the tail
+    out = []
+    for r0 in range(0, rlim, R):
+        if kmajor:
+            last = (rlim - 1) & ~3
+            col = np.where(r0 + co < rlim, r0 + co, last)
+            base = ro * ld + col
+        else:
+            row = np.where(r0 + ro < rlim, r0 + ro, rlim - 1)
+            base = row * ld + co
+        for t in range(nk):
+            k0 = t * BK
+            addr = base + (k0 * ld if kmajor else k0)
+            out.append((r0, k0, addr, ro, co))
+    return out
+
+
+def check(R, BK, NT, kmajor, rlim, K, ld):
+    rows, cols = (K, rlim) if kmajor else (rlim, K)
+    size = (rows - 1) * ld + cols
+    n = 0
+    for r0, k0, addr, ro, co in clamped_addresses(R, BK, NT, kmajor, rlim, K, ld):
+        assert addr.min() >= 0 and addr.max() + 3 < size, (R, BK, kmajor, rlim, K, ld, r0, k0)
+        for j in range(4):
+            if kmajor:  # position (k row ro + k0, column r0 + co + j)
+                valid = r0 + co + j < rlim
+                want = (ro + k0) * ld + r0 + co + j
+            else:       # position (row r0 + ro, k column k0 + co + j)
+                valid = r0 + ro < rlim
+                want = (r0 + ro) * ld + k0 + co + j
+            assert np.array_equal((addr + j)[valid], want[valid]), (R, BK, kmajor, rlim, K, ld)
+        n += addr.size
+    return n
+
+
+@pytest.mark.parametrize("R,BK,NT", TILES)
+@pytest.mark.parametrize("kmajor", [True, False], ids=["kmajor", "rows"])
+def test_clamped_loads_stay_inside_and_fill_in_range_positions(R, BK, NT, kmajor):
+    n = 0
+    for rlim in EXTENTS:
+        for K in KS:
+            width = rlim if kmajor else K
+            for ld in sorted({width, width + 3, 4 * ((width + 3) // 4) + 4}):
+                if kmajor and ld < 4:
+                    continue  # the launcher keeps the checked kernel for these
+                n += check(R, BK, NT, kmajor, rlim, K, ld)
+    assert n > 0
+
+
+def test_model_catches_a_missing_tail():
+    """Running the K-step of the last k inside the loop (nk = ceil(K / BK))
+    would read past the storage of a k-major operand whose last group
+    straddles the row end: the model must see that."""
+    R, BK, NT, rlim, K, ld = 64, 16, 256, 5, 32, 5
+    ro, co = slots(R, BK, NT, True)
+    last = (rlim - 1) & ~3
+    base = ro * ld + np.where(co < rlim, co, last)
+    k0 = (K // BK - 1) * BK  # the last whole step, which holds k = K - 1
+    addr = base + k0 * ld
+    assert addr.max() + 3 >= (K - 1) * ld + rlim
