@@ -1,6 +1,8 @@
-"""Host-side model of the clamped register staging in csrc/mfma.hip
-(OperandTile::init, init_clamp, load_clamped, and RingTile's split of K
-into whole K-steps plus a tail).
+"""Host-side models of two edge-tile load schemes in csrc/mfma.hip: the
+clamped register staging (OperandTile::init, init_clamp, load_clamped, and
+RingTile's split of K into whole K-steps plus a tail), and the 4-byte direct
+loads into LDS with range-checked zero fill (OperandTile::init and
+load_direct for rows that are not 16-byte aligned), at the end of the file.
 
 Edge tiles ("Tiled GEMM: Matrix Multiplication in CUDA", section 7.1) must
 not read outside an operand, and every element that reaches a stored output
@@ -103,3 +105,82 @@ def test_model_catches_a_missing_tail():
     k0 = (K // BK - 1) * BK  # the last whole step, which holds k = K - 1
     addr = base + k0 * ld
     assert addr.max() + 3 >= (K - 1) * ld + rlim
+
+
+# --------------------------------------------------------------------------
+# 4-byte direct loads into LDS (rows not 16-byte aligned): one float per lane
+# and chunk; a lane whose element is out of range gets an offset outside the
+# buffer, which the hardware turns into zero.  Restated from
+# OperandTile::init (DW) and load_direct.
+# --------------------------------------------------------------------------
+
+def dw_tile_ok(R, BK, NW, kmajor):
+    return (R * BK // 64) % NW == 0 and ((64 * NW) % R == 0 if kmajor else (64 * NW) % BK == 0)
+
+
+def swz(m, S):
+    # the kernel's shift: log2 S for S = 2, 4, 8, and 4 for every larger S
+    log2s = {2: 1, 4: 2, 8: 3}.get(S, 4)
+    r = m & 31
+    return (r ^ (r >> log2s)) & (S - 1)
+
+
+def dw_stage(R, BK, NW, kmajor, r0, k0, rlim, K, ld):
+    """LDS image of one K-step: the global element offset each position
+    receives, -1 for a zero fill."""
+    lds = np.full(R * BK, -2, dtype=np.int64)
+    step = 64 * NW // R if kmajor else 64 * NW // BK
+    jw = (R * BK // 64) // NW
+    S = BK // 4
+    p_period = 1 if kmajor else 32 // np.gcd(step, 32)
+    for w in range(NW):
+        f = w * 64 + np.arange(64)
+        if kmajor:
+            kr, col = f // R, f % R
+            off0 = kr * ld + r0 + col
+            lim = np.where(r0 + col < rlim, kr, 0x40000000)
+        else:
+            m = f // BK
+            off0 = (r0 + m) * ld
+        for j in range(jw):
+            pos = (w + j * NW) * 64 + np.arange(64)
+            if kmajor:
+                off = off0 + (k0 + j * step) * ld
+                ok = lim + j * step + k0 < K
+            else:
+                p = j % p_period
+                kc = 4 * (((f % BK) // 4) ^ np.array([swz(x, S) for x in m + p * step])) + f % 4
+                off = off0 + j * step * ld + kc + k0
+                ok = (r0 + m + j * step < rlim) & (kc + k0 < K)
+            assert (lds[pos] == -2).all(), "a position written twice"
+            lds[pos] = np.where(ok, off, -1)
+    assert (lds != -2).all(), "a position never written"
+    return lds
+
+
+DW_TILES = [(256, 32, 16), (64, 64, 16), (128, 32, 4), (128, 16, 8), (256, 16, 8), (256, 32, 8),
+            (64, 128, 16)]
+
+
+@pytest.mark.parametrize("R,BK,NW", DW_TILES)
+@pytest.mark.parametrize("kmajor", [True, False], ids=["kmajor", "rows"])
+def test_four_byte_direct_loads_fill_each_position(R, BK, NW, kmajor):
+    if not dw_tile_ok(R, BK, NW, kmajor):
+        pytest.skip("tile shape not used with 4-byte loads")
+    S = BK // 4
+    for rlim, K in [(R, BK), (R - 1, BK - 3), (R + 5, 3 * BK + 1), (7, 5)]:
+        ld = (K if not kmajor else rlim) + 1
+        for r0 in range(0, rlim, R):
+            for k0 in range(0, K, BK):
+                lds = dw_stage(R, BK, NW, kmajor, r0, k0, rlim, K, ld)
+                if kmajor:  # position (k row, column): LD = R
+                    krow, col = np.divmod(np.arange(R * BK), R)
+                    valid = (k0 + krow < K) & (r0 + col < rlim)
+                    want = (k0 + krow) * ld + r0 + col
+                else:       # position (row, physical column), logical column via the swizzle
+                    row, pc = np.divmod(np.arange(R * BK), BK)
+                    lc = 4 * ((pc // 4) ^ np.array([swz(x, S) for x in row])) + pc % 4
+                    valid = (r0 + row < rlim) & (k0 + lc < K)
+                    want = (r0 + row) * ld + k0 + lc
+                assert np.array_equal(lds[valid], want[valid]), (R, BK, NW, kmajor, rlim, K, r0, k0)
+                assert (lds[~valid] == -1).all(), (R, BK, NW, kmajor, rlim, K, r0, k0)
