@@ -1,8 +1,9 @@
-"""Host-side models of two edge-tile load schemes in csrc/mfma.hip: the
+"""Host-side models of the edge-tile load schemes in csrc/mfma.hip: the
 clamped register staging (OperandTile::init, init_clamp, load_clamped, and
-RingTile's split of K into whole K-steps plus a tail), and the 4-byte direct
-loads into LDS with range-checked zero fill (OperandTile::init and
-load_direct for rows that are not 16-byte aligned), at the end of the file.
+RingTile's split of K into whole K-steps plus a tail), then the 4-byte
+direct loads into LDS with range-checked zero fill (rows that are not
+16-byte aligned) and the clamped 16-byte direct loads (aligned rows), both
+from OperandTile::init and load_direct.
 
 Edge tiles ("Tiled GEMM: Matrix Multiplication in CUDA", section 7.1) must
 not read outside an operand, and every element that reaches a stored output
@@ -184,3 +185,62 @@ def test_four_byte_direct_loads_fill_each_position(R, BK, NW, kmajor):
                     want = (r0 + row) * ld + k0 + lc
                 assert np.array_equal(lds[valid], want[valid]), (R, BK, NW, kmajor, rlim, K, r0, k0)
                 assert (lds[~valid] == -1).all(), (R, BK, NW, kmajor, rlim, K, r0, k0)
+
+
+# --------------------------------------------------------------------------
+# 16-byte direct loads into LDS with 16-byte-aligned rows: each lane moves
+# 16 bytes of a 1 KiB chunk; at edge tiles the rows past the extent load the
+# last row (row flavour) and the 16-byte groups past it the last group
+# (k-major, extent a multiple of 4).  Whole K-steps only.  Restated from
+# OperandTile::init (direct, not DW) and load_direct.
+# --------------------------------------------------------------------------
+
+def vec_stage(R, BK, NW, kmajor, r0, k0, rlim, ld):
+    """Global element offset of each LDS position of one K-step."""
+    S = BK // 4
+    lds = np.full(R * BK, -2, dtype=np.int64)
+    lane = np.arange(64)
+    for c in range(R * BK // 256):  # chunk c belongs to wavefront c % NW
+        if kmajor:
+            f = c * 256 + lane * 4
+            col = np.minimum(r0 + f % R, rlim - 4)
+            src = (f // R) * ld + col + k0 * ld
+        else:
+            m = c * (64 // S) + lane // S
+            q = (lane % S) ^ np.array([swz(x, S) for x in m])
+            row = np.minimum(r0 + m, rlim - 1)
+            src = row * ld + 4 * q + k0
+        for t in range(4):
+            pos = c * 256 + lane * 4 + t
+            assert (lds[pos] == -2).all()
+            lds[pos] = src + t
+    assert (lds != -2).all()
+    return lds
+
+
+VEC_TILES = [(256, 32, 16), (128, 32, 4), (128, 16, 8), (256, 16, 8), (64, 64, 16), (64, 128, 16)]
+
+
+@pytest.mark.parametrize("R,BK,NW", VEC_TILES)
+@pytest.mark.parametrize("kmajor", [True, False], ids=["kmajor", "rows"])
+def test_clamped_direct_loads_fill_in_range_positions(R, BK, NW, kmajor):
+    S = BK // 4
+    for rlim in ([R, R - 4, R + 8, 4, 12] if kmajor else [R, R - 1, R + 5, 1, 7]):
+        K = 3 * BK
+        ld = (rlim if kmajor else K) + 4
+        rows, cols = (K, rlim) if kmajor else (rlim, K)
+        size = (rows - 1) * ld + cols
+        for r0 in range(0, rlim, R):
+            for k0 in range(0, K, BK):
+                lds = vec_stage(R, BK, NW, kmajor, r0, k0, rlim, ld)
+                assert lds.min() >= 0 and lds.max() < size, (R, BK, kmajor, rlim, r0, k0)
+                if kmajor:
+                    krow, col = np.divmod(np.arange(R * BK), R)
+                    valid = r0 + col < rlim
+                    want = (k0 + krow) * ld + r0 + col
+                else:
+                    row, pc = np.divmod(np.arange(R * BK), BK)
+                    lc = 4 * ((pc // 4) ^ np.array([swz(x, S) for x in row])) + pc % 4
+                    valid = r0 + row < rlim
+                    want = (r0 + row) * ld + k0 + lc
+                assert np.array_equal(lds[valid], want[valid]), (R, BK, NW, kmajor, rlim, r0, k0)
