@@ -27,7 +27,10 @@
  * allocates nothing on these calls and keeps no pointer after returning.
  * C is overwritten in its M x N region only; the padding columns
  * ldc - N of every row, and everything outside the region, are never read
- * or written.  C must not overlap A or B.
+ * or written.  C must not overlap A or B.  A and B are read only inside
+ * their storage, from the first element to the last element of the last
+ * row; the kernels may read padding elements between rows, whose values
+ * (NaN included) never reach C.
  *
  * Streams and threading: every compute call only enqueues work on `stream`
  * (a hipStream_t; NULL means the null stream) and returns; the caller
