@@ -360,6 +360,32 @@ def test_leading_dimensions_and_guard_band(variant):
 
 
 @pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
+def test_nan_padding_never_reaches_c(v, c, name):
+    """The padding between the rows of A and B is NaN: kernels may read it
+    (clamped edge loads do), but no such value may reach C."""
+    import torch
+
+    ops_list = ["NN", "TN"] if v == 3 and name in TRANS_CAPABLE else ["NN"]
+    for M, N, K in [(300, 277, 129), (520, 774, 100), (257, 263, 131)]:
+        for ops in ops_list:
+            log(f"NaN padding {ops} {M}x{N}x{K} on {name}")
+            A, B = make_inputs(M, N, K, "int4", seed=71)
+            if ops[0] == "T":  # A stored K x M with 3 NaN columns per row
+                bufA = torch.full((K, M + 3), float("nan"), device="cuda:0")
+                bufA[:, :M] = to_dev(np.ascontiguousarray(A.T))
+                dA = bufA[:, :M].t()
+            else:
+                bufA = torch.full((M, K + 3), float("nan"), device="cuda:0")
+                bufA[:, :K] = to_dev(A)
+                dA = bufA[:, :K]
+            bufB = torch.full((K, N + 5), float("nan"), device="cuda:0")
+            bufB[:, :N] = to_dev(B)
+            out = torch.empty((M, N), device="cuda:0")
+            b.gemm(dA, bufB[:, :N], out, variant=v, config=c)
+            assert_exact(to_host(out), oracle.gemm(A, B), f"{name} {ops} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("v,c,name", ALL_CONFIGS, ids=CONFIG_IDS)
 def test_deterministic(v, c, name):
     log(f"determinism on {name}")
     A, B = make_inputs(320, 288, 300, "uniform", seed=9)
