@@ -909,11 +909,14 @@ def test_random_problems_exact():
     forms, batches of 1 to 3, the library's choice or a random MFMA
     configuration, a quarter of the single row-major products as split-K)
     on integer inputs: every product exact against the oracle, and C's
-    padding untouched."""
+    padding untouched.  GEMM_F32_RANDOM_CASES and GEMM_F32_RANDOM_SEED set
+    another count or seed for a longer run."""
+    import os
+
     import torch
 
-    rng = np.random.default_rng(2024)
-    for case in range(200):
+    rng = np.random.default_rng(int(os.environ.get("GEMM_F32_RANDOM_SEED", "2024")))
+    for case in range(int(os.environ.get("GEMM_F32_RANDOM_CASES", "200"))):
         M, N, K, ops, nb, pads, (v, c, name) = _random_case(rng)
         log(f"random case {case}: {nb} x {M}x{N}x{K} {ops} pads {pads} on {name}")
         A = rng.integers(-4, 5, size=(nb, M, K)).astype(np.float32)
