@@ -141,24 +141,3 @@ def gemm(A: np.ndarray, B: np.ndarray, *, rows=None, threads: int = 0,
     if rc != 0:
         raise RuntimeError(f"oracle_gemm failed with code {rc}")
     return (C, C64) if return_f64 else C
-
-
-def gemm_into(A: np.ndarray, B: np.ndarray, C: np.ndarray, *, threads: int = 0,
-              lib: ctypes.CDLL | None = None) -> None:
-    """Writes ``A x B`` into the first N columns of a row-major float32 ``C``
-    whose leading dimension may exceed N; the rest of C is left untouched."""
-    lib = lib or load()
-    M, K = A.shape
-    N = B.shape[1]
-    if C.dtype != np.float32 or C.ndim != 2 or C.shape[0] != M or C.shape[1] < N:
-        raise ValueError("C must be float32 with M rows and at least N columns")
-    if C.strides[1] != 4 or C.strides[0] % 4:
-        raise ValueError("C rows must be contiguous")
-    A, lda = _as_rows(A, "A")
-    B, ldb = _as_rows(B, "B")
-    ldc = C.strides[0] // 4 if M > 1 else C.shape[1]
-    rc = lib.oracle_gemm(
-        M, N, K, A.ctypes.data_as(_fp), lda, B.ctypes.data_as(_fp), ldb,
-        None, M, C.ctypes.data_as(_fp), max(ldc, 1), None, 1, int(threads))
-    if rc != 0:
-        raise RuntimeError(f"oracle_gemm failed with code {rc}")

@@ -29,16 +29,6 @@ def test_thread_count_invariance():
     assert np.array_equal(one.view(np.uint32), many.view(np.uint32))
 
 
-def test_gemm_into_leaves_padding():
-    from dense_fp32_gemm_row_amd.workloads import make_inputs
-
-    A, B = make_inputs(13, 17, 9, "int4", seed=4)
-    C = np.full((13, 24), np.nan, dtype=np.float32)
-    oracle.gemm_into(A, B, C)
-    assert np.isnan(C[:, 17:]).all()
-    assert np.array_equal(C[:, :17], oracle.gemm(A, B))
-
-
 def test_invalid_arguments_rejected():
     lib = oracle.load()
     # lda < K
