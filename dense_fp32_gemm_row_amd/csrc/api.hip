@@ -73,9 +73,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     }
 }
 
-// Split geometry: `want` splits of K rounded to whole multiples of 32 (so
-// every kernel's K step divides a split); returns the split length and sets
-// the number of splits actually used.
+// Split geometry: `want` splits of K, the length rounded up to a multiple of
+// 32; returns the split length and sets the number of splits actually used.
+// A kernel whose K-step does not divide the length (BK = 64 or 128) runs its
+// K-checked path on every slice.
 int split_len(int64_t K, int64_t want, int64_t *used) {
     int64_t len = (K + want - 1) / want;
     len = ((len + 31) / 32) * 32;

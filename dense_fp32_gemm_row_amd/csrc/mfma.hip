@@ -959,7 +959,9 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool vec = rows_aligned16(p.A, p.lda, p.sa) && rows_aligned16(p.B, p.ldb, p.sb);
     const bool edge_mn = (p.M % BM) || (p.N % BN);
-    const bool edge_k = (p.K % BK) != 0;
+    // Split-K products run over K slices of p.ksplit (the last one shorter):
+    // every slice must be whole K-steps for the kernels without a K check.
+    const bool edge_k = (p.K % BK) != 0 || (p.ksplit > 0 && (p.ksplit % BK) != 0);
     const dim3 g(static_cast<unsigned>(grid)), b(NT);
 #define GEMM_RING(D, G, V, TA, TB, CL_)                                                        \
     hipLaunchKernelGGL(                                                                         \

@@ -21,6 +21,8 @@ columns) is stored in 16-byte slots.  Row flavour: row e / (BK / 4), k
 column 4 (e % (BK / 4)).  K-major: k row e / (R / 4), column 4 (e % (R / 4)).
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -244,3 +246,68 @@ def test_clamped_direct_loads_fill_in_range_positions(R, BK, NW, kmajor):
                     valid = r0 + row < rlim
                     want = (r0 + row) * ld + k0 + lc
                 assert np.array_equal(lds[valid], want[valid]), (R, BK, NW, kmajor, rlim, r0, k0)
+
+
+# --------------------------------------------------------------------------
+# Split-K slices: the partial products run as a strided batch whose product
+# b covers k in [b * len, min((b + 1) * len, K)), len a multiple of 32
+# (gemm_f32_splitk).  A kernel reads a slice through the K loop its launcher
+# picks for the whole launch: without a K check it runs ceil(len_b / BK)
+# whole K-steps, so it may only be picked when every slice is whole K-steps.
+# Restated from launch_mfma's edge_k rule and RingTile's step counts.
+# --------------------------------------------------------------------------
+
+def mfma_bk(name):
+    """K-step of an MFMA configuration, from its name (..._BMxBNxBK_...)."""
+    import re
+
+    return int(re.search(r"_(\d+)x(\d+)x(\d+)_", name).group(3))
+
+
+def slice_reads(K, length, used, BK, edge_k):
+    """For each slice b, the k range [lo, hi) of the operands that its
+    whole-step K loop loads (the partial or clamped tail is zero filled past
+    the slice and not counted here)."""
+    out = []
+    for b in range(used):
+        kb = min(length, K - b * length)
+        if edge_k:
+            nk = kb // BK  # checked kernels: whole steps inside the slice, then a tail
+        else:
+            nk = -(-kb // BK)  # no K check: every step of the slice is loaded whole
+        out.append((b * length, b * length + nk * BK, b * length + kb))
+    return out
+
+
+def _edge_k(K, length, BK):
+    return K % BK != 0 or length % BK != 0
+
+
+@pytest.mark.parametrize("K,splits", [(4160, 4), (1029, 7), (1029, 3), (1024, 4), (65536, 16),
+                                      (8192, 3), (777, 2), (4096, 5)])
+def test_splitk_slices_stay_inside_their_k_range(K, splits):
+    from dense_fp32_gemm_row_amd import binding as b
+
+    if not os.path.exists(b.LIBRARY):
+        pytest.skip("library not built")
+    b.load()
+    M = N = 256
+    ws = b.gemm_f32_splitk_workspace_size(M, N, K, splits)
+    used = ws // (4 * M * N) if ws else 1
+    length = -(-K // splits)
+    length = max(32, -(-length // 32) * 32)
+    assert used == -(-K // length)
+    for name in b.config_names(b.VARIANT_MFMA):
+        BK = mfma_bk(name)
+        for lo, hi, end in slice_reads(K, length, used, BK, _edge_k(K, length, BK)):
+            assert lo <= hi <= end, (name, K, splits, lo, hi, end)
+
+
+def test_splitk_model_sees_the_unchecked_overrun():
+    """The model has teeth: deciding the K check on K alone (K = 4160 is
+    whole 64-k steps, the 1056-k slices are not) lets slice 0 read into
+    slice 1 and the last slice read past K."""
+    K, length, used, BK = 4160, 1056, 4, 64
+    reads = slice_reads(K, length, used, BK, K % BK != 0)
+    assert reads[0][1] > reads[0][2]
+    assert reads[-1][1] > K
