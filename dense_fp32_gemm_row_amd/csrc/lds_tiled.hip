@@ -1,29 +1,34 @@
-// Stage 2: shared-memory (LDS) tiling in phases.
+// Stage 2: the K dimension in T-wide phases through LDS.
 //
-// Prior art: the tiled kernels of "Tiled Matrix Multiplication in CUDA",
-// section 7, and "Tiled GEMM: Matrix Multiplication in CUDA", sections 2
-// and 4.  A T x T workgroup computes one T x T tile of C.  The K dimension is
-// walked in phases of T: every thread copies one element of the current A
-// tile and one of the current B tile into LDS, the workgroup waits (the
-// read-after-write barrier), every thread adds T products from LDS into its
-// register, and the workgroup waits again before the tiles are overwritten
-// (the write-after-read barrier).  Each element fetched from global memory is
-// reused T times, so requested traffic falls by T and the arithmetic
-// intensity rises to T / 4 FLOP per byte ("Tiled GEMM: Matrix Multiplication
-// in CUDA", section 2, the intensity table).
+// Prior art: the shared-memory tiled kernels of "Tiled Matrix Multiplication
+// in CUDA" (section 7) and "Tiled GEMM: Matrix Multiplication in CUDA"
+// (sections 2 and 4).  This stage is that method by design, so the steps
+// match the pages' (copy, barrier, partial dot products, barrier); the code
+// below is its own.
+//
+// One T x T workgroup owns one T x T block of C, a lane per cell.  For each
+// phase of T values of k the workgroup first copies the T x T block of A
+// (C's rows, the phase's k) and the T x T block of B (the phase's k, C's
+// columns) into LDS, one element of each per lane, and waits: every lane
+// then finds all T of its A values and T of its B values in LDS.  Each lane
+// adds its T products, and the workgroup waits again before the next phase
+// overwrites the blocks.  An element loaded from global memory serves T
+// lanes, so requested traffic falls by T against the naive kernel and the
+// intensity becomes T / 4 FLOP per byte ("Tiled GEMM: Matrix Multiplication
+// in CUDA", section 2).
 //
 // Ragged shapes ("Tiled GEMM: Matrix Multiplication in CUDA", section 7.1):
-// the grid is rounded up, loads outside A or B write 0.0 into LDS so the
-// extra products add nothing, and the store is guarded.
+// blocks that reach past M, N or K are padded with zeros in LDS, which add
+// nothing to any sum, and only cells inside C are stored.
 //
-// Padding (section 7.2 of the same page): the row reads of tileA are
-// broadcasts and the column reads of tileB hit consecutive banks, so this
-// kernel needs no padding; the PAD = 1 configurations exist to show that in
-// the bank-conflict counters.
+// LDS banks (section 7.2 of the same page): in the product loop all lanes
+// of a row read one A value (a broadcast) and consecutive lanes read
+// consecutive B values, so no padding is needed; PAD = 1 builds exist to
+// show that in the bank-conflict counters.
 //
-// The products of one cell are added in ascending k with fused
-// multiply-adds, exactly as in the naive kernel, so the two give identical
-// results ("Tiled Matrix Multiplication in CUDA", section 8).
+// Each cell's products are added in ascending k with fused multiply-adds,
+// the order of the naive kernel, so both stages return the same bits
+// ("Tiled Matrix Multiplication in CUDA", section 8).
 
 #include "gemm_internal.h"
 
@@ -35,32 +40,37 @@ __global__ __launch_bounds__(T * T) void gemm_lds_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
     int tiles_m, int tiles_n, BatchArgs bt) {
-    __shared__ float tileA[T][T + PAD];
-    __shared__ float tileB[T][T + PAD];
+    // s_a[r][q]: A at (block row r, phase k q); s_b[q][c]: B at (phase k q,
+    // block column c)
+    __shared__ float s_a[T][T + PAD];
+    __shared__ float s_b[T][T + PAD];
 
-    const int tx = threadIdx.x, ty = threadIdx.y;
-    const int tile = batch_select(blockIdx.x, tiles_m * tiles_n, bt, A, B, C, K);
-    const int tile_row = tile / tiles_n;
-    const int tile_col = tile - tile_row * tiles_n;
-    const int row = tile_row * T + ty;
-    const int col = tile_col * T + tx;
-    const bool row_ok = row < M, col_ok = col < N;
-    const float *a_row = A + static_cast<int64_t>(row_ok ? row : 0) * lda;
+    const int lx = threadIdx.x;  // cell column in the block; k offset of the A copy
+    const int ly = threadIdx.y;  // cell row in the block; k offset of the B copy
+    const int blk = batch_select(blockIdx.x, tiles_m * tiles_n, bt, A, B, C, K);
+    const int bi = blk / tiles_n, bj = blk - (blk / tiles_n) * tiles_n;
+    const int i = bi * T + ly, j = bj * T + lx;  // this lane's cell of C
+    const bool in_m = i < M, in_n = j < N;
 
-    float acc = 0.0f;
-    const int phases = (K + T - 1) / T;
-    for (int phase = 0; phase < phases; ++phase) {
-        const int a_col = phase * T + tx;  // A walks right
-        const int b_row = phase * T + ty;  // B walks down
-        tileA[ty][tx] = (row_ok && a_col < K) ? a_row[a_col] : 0.0f;
-        tileB[ty][tx] = (b_row < K && col_ok) ? B[static_cast<int64_t>(b_row) * ldb + col] : 0.0f;
-        __syncthreads();  // read after write: the whole tile is in LDS
+    // The elements this lane copies in phase p: A(i, pT + lx) and
+    // B(pT + ly, j).  Both pointers advance by one phase per iteration.
+    const float *pa = A + static_cast<int64_t>(in_m ? i : 0) * lda + lx;
+    const float *pb = B + static_cast<int64_t>(ly) * ldb + (in_n ? j : 0);
+    const int64_t pb_step = static_cast<int64_t>(T) * ldb;
+
+    float sum = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += T) {
+        s_a[ly][lx] = (in_m && k0 + lx < K) ? *pa : 0.0f;
+        s_b[ly][lx] = (in_n && k0 + ly < K) ? *pb : 0.0f;
+        pa += T;
+        pb += pb_step;
+        __syncthreads();  // both blocks are complete in LDS
 
 #pragma unroll
-        for (int k = 0; k < T; ++k) acc = fmaf(tileA[ty][k], tileB[k][tx], acc);
-        __syncthreads();  // write after read: nobody still reads this tile
+        for (int q = 0; q < T; ++q) sum = fmaf(s_a[ly][q], s_b[q][lx], sum);
+        __syncthreads();  // no lane still reads them when the next phase writes
     }
-    if (row_ok && col_ok) C[static_cast<int64_t>(row) * ldc + col] = acc;
+    if (in_m && in_n) C[static_cast<int64_t>(i) * ldc + j] = sum;
 }
 
 template <int T, int PAD>
