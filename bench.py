@@ -113,61 +113,6 @@ def device_info(dev) -> dict:
     return info
 
 
-class SclkSampler:
-    """Samples the device's current engine clock from the amdgpu driver's
-    pp_dpm_sclk file (the level marked '*') in a thread, while the timed
-    region runs.  Reports nothing where the file is absent or unreadable."""
-
-    def __init__(self, dev, period_s: float = 0.05, enabled: bool = True):
-        import threading
-
-        import torch
-
-        p = torch.cuda.get_device_properties(dev)
-        self.path = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
-                     f"{p.pci_device_id:02x}.0/pp_dpm_sclk")
-        self.period = period_s
-        self.enabled = enabled
-        self.samples: list[int] = []
-        self.stop = threading.Event()
-        self.thread = threading.Thread(target=self._run, daemon=True)
-
-    def _read(self) -> int | None:
-        try:
-            with open(self.path) as f:
-                for line in f:
-                    if "*" in line:
-                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
-                        return int(m.group(1)) if m else None
-        except OSError:
-            return None
-        return None
-
-    def _run(self):
-        while not self.stop.is_set():
-            v = self._read()
-            if v is not None:
-                self.samples.append(v)
-            self.stop.wait(self.period)
-
-    def __enter__(self):
-        if self.enabled and os.access(self.path, os.R_OK):
-            self.thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self.stop.set()
-        if self.thread.is_alive():
-            self.thread.join()
-
-    def summary(self) -> dict | None:
-        if not self.samples:
-            return None
-        v = sorted(self.samples)
-        return {"samples": len(v), "min_mhz": v[0], "median_mhz": v[len(v) // 2],
-                "max_mhz": v[-1], "source": "pp_dpm_sclk"}
-
-
 def time_launches(fn, steps: int, warmup: int, stream):
     """Runs fn() warmup times, then `steps` times with an event pair around
     each launch on `stream`.  Returns (total_ms, per-launch ms list)."""
@@ -219,9 +164,26 @@ def time_graph(make_fn, steps: int, warmup: int, stream):
     return total, [total / steps]
 
 
-def cpu_baseline(A, B, target_s: float) -> dict:
-    """The oracle, as it stands, on a bounded sample of rows of the same
-    product, timed with the host's default OpenMP thread count."""
+def oracle_rows_plan(M: int, per_row_s: float, full_limit_s: float, target_s: float):
+    """Rows the oracle computes: all of them when that takes at most
+    full_limit_s, else enough evenly spaced rows (at least 512, the first and
+    last included) for about target_s.  None stands for every row."""
+    if per_row_s * M <= full_limit_s:
+        return None
+    n = int(min(M, max(512, target_s / max(per_row_s, 1e-9))))
+    import numpy as np
+
+    return sorted(set(np.linspace(0, M - 1, n).astype(np.int64).tolist()))
+
+
+def oracle_leg(A, B, C, full_limit_s: float, target_s: float, check: bool, baseline: bool):
+    """The oracle, as it stands, with the host's default OpenMP thread count,
+    on the timed output's product: every row when the whole product takes at
+    most full_limit_s on this host (8192^3 takes about 12 s on 16 cores),
+    else a bounded sample of evenly spaced rows.  The one run gives both the
+    CPU baseline (its rate, scaled per FLOP) and the parity check of every
+    computed cell against the oracle's FP64 sums; a sampled check adds a
+    Freivalds projection of the whole product.  Returns (parity, baseline)."""
     import numpy as np
 
     import oracle
@@ -229,47 +191,48 @@ def cpu_baseline(A, B, target_s: float) -> dict:
     M, K = A.shape
     N = B.shape[1]
     threads = oracle.default_threads()
-    probe = list(range(threads))
+    probe = list(range(min(M, threads)))
     t0 = time.perf_counter()
     oracle.gemm(A, B, rows=probe, threads=threads)
     per_row = (time.perf_counter() - t0) / len(probe)
-    n = int(min(M, max(threads, target_s / max(per_row, 1e-9))))
-    n = max(threads, n - n % threads) if n < M else M
-    rng_rows = sorted(set(np.linspace(0, M - 1, n).astype(np.int64).tolist()))
+    rows = oracle_rows_plan(M, per_row, full_limit_s, target_s)
     t0 = time.perf_counter()
-    oracle.gemm(A, B, rows=rng_rows, threads=threads)
+    _, ref = oracle.gemm(A, B, rows=rows, threads=threads, return_f64=True)
     t = time.perf_counter() - t0
-    flops = 2.0 * len(rng_rows) * N * K
-    return {
-        "value": round(flops / t / 1e12, 6),
-        "unit": "TFLOP/s",
-        "cores": threads,
-        "cpu_model": cpu_model(),
-        "kind": "oracle",
-        "sample": f"{len(rng_rows)} of {M} output rows (evenly spaced), each a full "
-                  f"{K}x{N} sweep; {t:.1f} s wall, FP64 accumulation",
-    }
-
-
-def parity_check(A, B, C) -> dict:
-    """Sampled rows against the oracle plus a Freivalds projection."""
-    import numpy as np
-
-    import oracle
-
-    M, K = A.shape
-    rng = np.random.default_rng(1)
-    rows = sorted(set([0, M - 1] + [int(r) for r in rng.integers(0, M, size=14)]))
-    _, ref = oracle.gemm(A, B, rows=rows, return_f64=True)
-    got = C[rows].astype(np.float64)
-    max_err = float(np.abs(got - ref).max())
-    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-    x = rng.choice([-1.0, 1.0], size=B.shape[1])
-    fr_ref = A.astype(np.float64) @ (B.astype(np.float64) @ x)
-    fr = float(np.linalg.norm(C.astype(np.float64) @ x - fr_ref) / np.linalg.norm(fr_ref))
-    ok = (not np.isnan(C).any()) and max_err <= 1e-4 * math.sqrt(K) and rel <= 1e-5 and fr <= 1e-5
-    return {"rows": len(rows), "max_abs_err": max_err, "rel_fro": rel, "freivalds": fr,
-            "tol_max": 1e-4 * math.sqrt(K), "tol_rel": 1e-5, "ok": bool(ok)}
+    nrows = M if rows is None else len(rows)
+    parity = cpu = None
+    if check:
+        got = (C if rows is None else C[rows]).astype(np.float64)
+        err = np.abs(got - ref)
+        max_err = float(err.max()) if err.size else 0.0
+        norm = float(np.linalg.norm(ref))
+        rel = float(np.linalg.norm(got - ref) / norm) if norm > 0 else 0.0
+        del got, err
+        tol_max, tol_rel = 1e-4 * math.sqrt(max(K, 1)), 1e-5
+        ok = (not np.isnan(C).any()) and max_err <= tol_max and rel <= tol_rel
+        parity = {"cells_checked": nrows * N, "cells": M * N, "max_abs_err": max_err,
+                  "rel_fro": rel, "tol_max": tol_max, "tol_rel": tol_rel}
+        if rows is not None:
+            rng = np.random.default_rng(1)
+            x = rng.choice([-1.0, 1.0], size=N)
+            fr_ref = A.astype(np.float64) @ (B.astype(np.float64) @ x)
+            fr = float(np.linalg.norm(C.astype(np.float64) @ x - fr_ref) / np.linalg.norm(fr_ref))
+            parity["freivalds"] = fr
+            ok = ok and fr <= tol_rel
+        parity["ok"] = bool(ok)
+    if baseline:
+        what = (f"all {M} output rows" if rows is None else
+                f"{nrows} of {M} output rows (evenly spaced)")
+        cpu = {
+            "value": round(2.0 * nrows * N * K / t / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": threads,
+            "cpu_model": cpu_model(),
+            "kind": "oracle",
+            "sample": f"{what} of the {M}x{N}x{K} product, each a full {K}x{N} sweep; "
+                      f"{t:.1f} s wall, FP64 accumulation",
+        }
+    return parity, cpu
 
 
 def main() -> int:
@@ -280,7 +243,12 @@ def main() -> int:
     ap.add_argument("--workload", default="square8192")
     ap.add_argument("--variant", default=None, help="naive|lds|regblock|mfma (default: library choice)")
     ap.add_argument("--config", default=None, help="configuration name of the variant")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle time budget when the whole product would take longer than "
+                         "--full-oracle-seconds (then a sample of rows is computed)")
+    ap.add_argument("--full-oracle-seconds", type=float, default=90.0,
+                    help="the oracle computes every row of the product when its estimate is "
+                         "at most this")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--ops", default="NN", choices=["NN", "NT", "TN", "TT"],
@@ -291,8 +259,6 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as one captured HIP graph instead of one launch each "
                          "(removes the host's launch cost; per-launch time is the replay / steps)")
-    ap.add_argument("--no-sclk", action="store_true",
-                    help="do not sample the engine clock during the timed region")
     ap.add_argument("--stages", action="store_true")
     ap.add_argument("--stage-variants", default="naive,lds,regblock,mfma",
                     help="variants that --stages times")
@@ -388,11 +354,10 @@ def main() -> int:
             return binding.prepare(dA, dB, dC, stream=s, batched=nb > 1, **kw)
 
     dinfo = device_info(dev)
-    with SclkSampler(dev, enabled=not args.no_sclk) as sclk:
-        if args.graph:
-            total_ms, per = time_graph(make_fn, args.steps, args.warmup, stream)
-        else:
-            total_ms, per = time_launches(make_fn(stream), args.steps, args.warmup, stream)
+    if args.graph:
+        total_ms, per = time_graph(make_fn, args.steps, args.warmup, stream)
+    else:
+        total_ms, per = time_launches(make_fn(stream), args.steps, args.warmup, stream)
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
     value = flops * args.steps / (total_ms / 1e3) / 1e12
@@ -432,27 +397,33 @@ def main() -> int:
                           "min": round(min(per), 4), "max": round(max(per), 4)},
             "flops_per_launch": flops,
         },
-        "device": dict(dinfo, sclk_during_timing=sclk.summary()),
+        "device": dinfo,
     }
 
     rc = 0
-    if not args.no_check:
+    if not (args.no_check and args.no_cpu_baseline):
         C = dC.cpu().numpy()
-        if nb > 1:  # first and last product of the batch
-            checks = [parity_check(A[i], B[i], C[i]) for i in (0, nb - 1)]
+        products = [0, nb - 1] if nb > 1 else [None]
+        checks = []
+        for i in products:
+            Ai, Bi, Ci = (A, B, C) if i is None else (A[i], B[i], C[i])
+            par, cpu = oracle_leg(Ai, Bi, Ci, args.full_oracle_seconds, args.cpu_seconds,
+                                  check=not args.no_check,
+                                  baseline=not args.no_cpu_baseline and i in (None, 0))
+            if par is not None:
+                checks.append(par)
+            if cpu is not None:
+                result["cpu_baseline"] = cpu
+                log(f"cpu baseline {cpu}")
+        if checks:
             result["parity"] = max(checks, key=lambda r: r["rel_fro"])
             result["parity"]["ok"] = all(r["ok"] for r in checks)
-            result["parity"]["products_checked"] = [0, nb - 1]
-        else:
-            result["parity"] = parity_check(A, B, C)
-        log(f"parity {result['parity']}")
-        if not result["parity"]["ok"]:
-            rc = 1
+            if nb > 1:
+                result["parity"]["products_checked"] = products
+            log(f"parity {result['parity']}")
+            if not result["parity"]["ok"]:
+                rc = 1
         del C
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(A[0] if nb > 1 else A, B[0] if nb > 1 else B,
-                                              args.cpu_seconds)
-        log(f"cpu baseline {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
     return rc
 

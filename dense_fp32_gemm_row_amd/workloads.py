@@ -20,11 +20,13 @@ Distributions:
 Workloads (sizes are M x N x K; A is M x K, B is K x N, all row-major):
   * ``square256``    256 x 256 x 256, uniform (and ``square256_int4``)
   * ``square4096``   4096 x 4096 x 4096, uniform
-  * ``square8192``   8192 x 8192 x 8192, uniform (the headline shape)
+  * ``square8192``   8192 x 8192 x 8192, uniform (the headline shape), and
+                     ``square8192_int4`` with integer inputs: partial sums stay
+                     below 16 * 8192 = 2**17, so the whole product is exact
   * ``ragged``       1000 x 1023 x 777, uniform (and ``ragged_int4``); no
                      dimension is a multiple of 32 or 64
   * ``ffn``          M = 8192 tokens, K = 4096, N = 14336, normal (an FFN
-                     up-projection shape)
+                     up-projection shape), and ``ffn_int4`` with integer inputs
   * ``batched64_1024`` 64 independent 1024 x 1024 x 1024 products, uniform
                      (A is 64 x M x K, B is 64 x K x N, drawn in that order)
   * ``deepk``        1024 x 1024 x 65536, uniform: few output tiles and a long
@@ -66,9 +68,11 @@ WORKLOADS: dict[str, Workload] = {
         Workload("square256_int4", 256, 256, 256, "int4"),
         Workload("square4096", 4096, 4096, 4096, "uniform"),
         Workload("square8192", 8192, 8192, 8192, "uniform"),
+        Workload("square8192_int4", 8192, 8192, 8192, "int4"),
         Workload("ragged", 1000, 1023, 777, "uniform"),
         Workload("ragged_int4", 1000, 1023, 777, "int4"),
         Workload("ffn", 8192, 14336, 4096, "normal"),
+        Workload("ffn_int4", 8192, 14336, 4096, "int4"),
         Workload("batched64_1024", 1024, 1024, 1024, "uniform", batch=64),
         Workload("deepk", 1024, 1024, 65536, "uniform"),
         Workload("square8000", 8000, 8000, 8000, "uniform"),

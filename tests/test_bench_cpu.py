@@ -57,3 +57,34 @@ def test_more_than_one_gpu_is_refused():
     assert res.returncode == 2
     assert "one GPU" in res.stderr
     assert res.stdout == ""
+
+
+def test_oracle_rows_plan():
+    assert bench.oracle_rows_plan(8192, 12.0 / 8192, 90.0, 15.0) is None
+    rows = bench.oracle_rows_plan(8192, 1.0, 90.0, 15.0)
+    assert len(rows) == 512 and rows[0] == 0 and rows[-1] == 8191
+    rows = bench.oracle_rows_plan(100000, 0.01, 90.0, 15.0)
+    assert len(rows) == 1500 and rows[0] == 0 and rows[-1] == 99999
+
+
+def test_oracle_leg_checks_every_cell_and_times_the_run():
+    """With a whole-product budget the leg checks every cell: one wrong cell
+    anywhere fails it; the baseline reports the rows it ran."""
+    import numpy as np
+
+    import oracle
+    from dense_fp32_gemm_row_amd.workloads import make_inputs
+
+    A, B = make_inputs(300, 200, 100, "uniform", seed=3)
+    C = oracle.gemm(A, B)
+    par, cpu = bench.oracle_leg(A, B, C, 90.0, 15.0, check=True, baseline=True)
+    assert par["ok"] and par["cells_checked"] == 300 * 200 and "freivalds" not in par
+    assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and "all 300 output rows" in cpu["sample"]
+    bad = C.copy()
+    bad[217, 133] += np.float32(0.05)
+    par, _ = bench.oracle_leg(A, B, bad, 90.0, 15.0, check=True, baseline=False)
+    assert not par["ok"]
+    bad = C.copy()
+    bad[5, 7] = np.nan
+    par, _ = bench.oracle_leg(A, B, bad, 90.0, 15.0, check=True, baseline=False)
+    assert not par["ok"]
