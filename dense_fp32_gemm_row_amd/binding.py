@@ -79,6 +79,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gemm_f32_splitk.restype = _int
     lib.gemm_f32_splitk.argtypes = [_int, _int, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
                                     _i64, _vp, _i64, _vp]
+    lib.gemm_f32_splitk_noalloc.restype = _int
+    lib.gemm_f32_splitk_noalloc.argtypes = [_int, _int, _i64, _i64, _i64, _i64, _vp, _i64, _vp,
+                                            _i64, _vp, _i64, _vp]
     lib.gemm_f32_splitk_workspace_size.restype = _i64
     lib.gemm_f32_splitk_workspace_size.argtypes = [_i64, _i64, _i64, _i64]
     lib.gemm_f32_strerror.restype = ctypes.c_char_p
@@ -134,6 +137,15 @@ def gemm_f32_splitk(variant, config_id, splits, M, N, K, A, lda, B, ldb, C, ldc,
                     workspace_bytes, stream=None) -> int:
     return load().gemm_f32_splitk(variant, config_id, splits, M, N, K, A, lda, B, ldb, C, ldc,
                                   workspace, workspace_bytes, stream)
+
+
+def gemm_f32_splitk_noalloc(variant, config_id, splits, M, N, K, A, lda, B, ldb, C, ldc,
+                            stream=None) -> int:
+    return load().gemm_f32_splitk_noalloc(variant, config_id, splits, M, N, K, A, lda, B, ldb, C,
+                                          ldc, stream)
+
+
+SPLITK_SCRATCH_BYTES = 33554432  # GEMM_F32_SPLITK_SCRATCH_BYTES
 
 
 def gemm_f32_splitk_workspace_size(M, N, K, splits) -> int:
@@ -297,11 +309,17 @@ def gemm(A, B, out=None, *, variant: int | str | None = None, config: int | str 
 
 
 def gemm_splitk(A, B, splits: int, out=None, workspace=None, *, variant: int | str | None = None,
-                config: int | str = -1, stream=None):
+                config: int | str = -1, stream=None, noalloc: bool = False):
     """``out = A @ B`` as `splits` partial products over K plus a fixed-order
     reduction (gemm_f32_splitk).  ``workspace`` is a float32 GPU tensor of at
-    least gemm_f32_splitk_workspace_size bytes; allocated here when None."""
+    least gemm_f32_splitk_workspace_size bytes; allocated here when None.
+    With ``noalloc`` the call goes to gemm_f32_splitk_noalloc, whose partial
+    products use the library's static scratch (no workspace; ``out`` must be
+    given, so that nothing is allocated)."""
     import torch
+
+    if noalloc and (workspace is not None or out is None):
+        raise ValueError("noalloc takes an out tensor and no workspace")
 
     M, K = A.shape
     K2, N = B.shape
@@ -314,7 +332,7 @@ def gemm_splitk(A, B, splits: int, out=None, workspace=None, *, variant: int | s
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     opc, ldc, _ = _operand(out, "out", 2)
-    need = gemm_f32_splitk_workspace_size(M, N, K, splits)
+    need = 0 if noalloc else gemm_f32_splitk_workspace_size(M, N, K, splits)
     if workspace is None and need:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=A.device)
     wptr = workspace.data_ptr() if workspace is not None else None
@@ -325,8 +343,12 @@ def gemm_splitk(A, B, splits: int, out=None, workspace=None, *, variant: int | s
     else:
         v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
         c = config_id(v, config) if isinstance(config, str) else int(config)
-    rc = gemm_f32_splitk(v, c, splits, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
-                         out.data_ptr(), ldc, wptr, wbytes, sp)
+    if noalloc:
+        rc = gemm_f32_splitk_noalloc(v, c, splits, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                     out.data_ptr(), ldc, sp)
+    else:
+        rc = gemm_f32_splitk(v, c, splits, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                             out.data_ptr(), ldc, wptr, wbytes, sp)
     if rc != GEMM_F32_OK:
         raise GemmError(rc, gemm_f32_last_error())
     return out

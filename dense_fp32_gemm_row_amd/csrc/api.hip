@@ -11,6 +11,7 @@
 #include <cstring>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/gemm_f32.h"
 #include "gemm_internal.h"
@@ -458,6 +459,128 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
     return GEMM_F32_OK;
 }
 
+// gemm_f32_splitk and gemm_f32_splitk_noalloc.  `scratch_of` supplies the
+// workspace once the arguments are valid and the bytes it must hold are
+// known: the caller's buffer, or the library's static one.
+template <class Scratch>
+int splitk(int variant, int config_id, int64_t splits, int64_t M, int64_t N, int64_t K,
+           const float *A, int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
+           Scratch scratch_of, void *stream) {
+    if (splits < 0 || splits > 0xffff)
+        return fail(GEMM_F32_EINVAL, "splits=%lld outside [0, 65535]", (long long)splits);
+    if (splits == 0 && M > 0 && N > 0 && K > 0 && M <= 0x7fffffff && N <= 0x7fffffff &&
+        K <= 0x7fffffff)
+        splits = auto_splits(M, N, K);
+    if (splits == 0) splits = 1;
+    if (variant < -1) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant);
+    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
+    if (rc != GEMM_F32_OK) return rc;
+    int64_t used = 1;
+    const int len = K > 0 ? split_len(K, splits, &used) : 0;
+    if (used <= 1 || M == 0 || N == 0)  // one split: the plain product, no workspace
+        return run(variant, variant == -1 ? -1 : config_id, false, false, 1, M, N, K, A, lda, 0, B,
+                   ldb, 0, C, ldc, 0, stream);
+    rc = validate(false, false, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0);
+    if (rc != GEMM_F32_OK) return rc;
+    const int64_t need = used * M * N * static_cast<int64_t>(sizeof(float));
+    float *W = nullptr;
+    rc = scratch_of(need, stream, &W);
+    if (rc != GEMM_F32_OK) return rc;
+    const Span sw = {reinterpret_cast<uintptr_t>(W), reinterpret_cast<uintptr_t>(W) + need};
+    if (overlaps(sw, span_of(A, M, K, lda)) || overlaps(sw, span_of(B, K, N, ldb)) ||
+        overlaps(sw, span_of(C, M, N, ldc)))
+        return fail(GEMM_F32_EINVAL, "workspace overlaps A, B or C");
+    // partial products: a strided batch over the K splits into the workspace
+    int v = variant, c = config_id;
+    const bool aligned = direct_fast(
+        operands_aligned(A, lda, len, B, ldb, static_cast<int64_t>(len) * ldb), M, N, false, false);
+    if (v == -1) select_config(used, M, N, len, &v, &c, false, aligned);
+    int count = 0;
+    const ConfigEntry *cfgs = configs_of(v, &count);
+    if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", v);
+    if (c == -1) {
+        int vv = 0;
+        select_config(used, M, N, len, &vv, &c, false, aligned);
+        if (vv != v) c = 0;
+    }
+    if (c < 0 || c >= count)
+        return fail(GEMM_F32_ENOKERNEL, "variant %d has no configuration %d", v, c);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Problem p{static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), A, lda, B,
+                    ldb, W, N, static_cast<int>(used), len, static_cast<int64_t>(len) * ldb,
+                    M * N, false, false, len};
+    hipError_t err = cfgs[c].launch(p, st);
+    if (err == hipSuccess) {
+        const bool vec4 = (N % 4) == 0 && (ldc % 4) == 0 &&
+                          reinterpret_cast<uintptr_t>(C) % 16 == 0 &&
+                          reinterpret_cast<uintptr_t>(W) % 16 == 0;
+        const int64_t items = M * (vec4 ? N / 4 : N);
+        const unsigned grid = static_cast<unsigned>(std::min<int64_t>((items + 255) / 256, 8192));
+        if (vec4)
+            hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(grid), dim3(256), 0, st, W, M * N,
+                               static_cast<int>(used), static_cast<int>(M), static_cast<int>(N), C,
+                               ldc);
+        else
+            hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(grid), dim3(256), 0, st, W, M * N,
+                               static_cast<int>(used), static_cast<int>(M), static_cast<int>(N), C,
+                               ldc);
+        err = hipGetLastError();
+    }
+    if (err != hipSuccess) return fail(GEMM_F32_EHIP, "launch failed: %s", hipGetErrorString(err));
+    return GEMM_F32_OK;
+}
+
+// Library-owned scratch of gemm_f32_splitk_noalloc, for callers that
+// cannot allocate device memory.  Each device holds its own copy for the
+// life of the process.  In host code `scratch` names a host-side stand-in:
+// its device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address is passed to
+// kernels.  The split-K kernels overwrite every element they later read, so
+// nothing needs clearing between calls.
+constexpr int64_t kScratchBytes = int64_t{GEMM_F32_SPLITK_SCRATCH_BYTES};
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    float *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch_slots[kMaxDevices];
+
+// Device address of the scratch on the device that runs `stream` (the
+// current device for the null stream).
+int scratch_address(void *stream, float **out) {
+    int current = -1;
+    hipError_t err = hipGetDevice(&current);
+    if (err != hipSuccess) return fail(GEMM_F32_EHIP, "hipGetDevice: %s", hipGetErrorString(err));
+    int dev = current;
+    if (stream != nullptr) {
+        hipDevice_t d = 0;
+        err = hipStreamGetDevice(static_cast<hipStream_t>(stream), &d);
+        if (err != hipSuccess)
+            return fail(GEMM_F32_EHIP, "hipStreamGetDevice: %s", hipGetErrorString(err));
+        dev = static_cast<int>(d);
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(GEMM_F32_EINVAL, "device %d out of range", dev);
+    ScratchSlot &slot = g_scratch_slots[dev];
+    std::call_once(slot.once, [&] {
+        if (dev != current && (slot.err = hipSetDevice(dev)) != hipSuccess) return;
+        void *p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (slot.err == hipSuccess) slot.ptr = static_cast<float *>(p);
+        if (dev != current) {
+            const hipError_t back = hipSetDevice(current);
+            if (slot.err == hipSuccess) slot.err = back;
+        }
+    });
+    if (slot.err != hipSuccess || slot.ptr == nullptr)
+        return fail(GEMM_F32_EHIP, "scratch address on device %d: %s", dev,
+                    hipGetErrorString(slot.err));
+    *out = slot.ptr;
+    return GEMM_F32_OK;
+}
+
 }  // namespace
 
 hipError_t launch_zero_fill(float *C, int M, int N, int64_t ldc, int batch, int64_t sc,
@@ -524,70 +647,39 @@ int gemm_f32_splitk(int variant, int config_id, int64_t splits, int64_t M, int64
                     const float *A, int64_t lda, const float *B, int64_t ldb, float *C,
                     int64_t ldc, void *workspace, int64_t workspace_bytes, void *stream) {
     clear_error();
-    if (splits < 0 || splits > 0xffff)
-        return fail(GEMM_F32_EINVAL, "splits=%lld outside [0, 65535]", (long long)splits);
+    auto caller_buffer = [=](int64_t need, void *, float **W) {
+        float *w = static_cast<float *>(workspace);
+        if (w == nullptr || workspace_bytes < need)
+            return fail(GEMM_F32_EINVAL, "workspace of %lld bytes needed, %lld given",
+                        (long long)need, (long long)(w ? workspace_bytes : 0));
+        if (reinterpret_cast<uintptr_t>(w) % 4)
+            return fail(GEMM_F32_EINVAL, "workspace not 4-byte aligned");
+        *W = w;
+        return GEMM_F32_OK;
+    };
+    return splitk(variant, config_id, splits, M, N, K, A, lda, B, ldb, C, ldc, caller_buffer,
+                  stream);
+}
+
+int gemm_f32_splitk_noalloc(int variant, int config_id, int64_t splits, int64_t M, int64_t N,
+                            int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+                            float *C, int64_t ldc, void *stream) {
+    clear_error();
+    // library's choice of splits, capped so that the partials fit the scratch
     if (splits == 0 && M > 0 && N > 0 && K > 0 && M <= 0x7fffffff && N <= 0x7fffffff &&
-        K <= 0x7fffffff)
-        splits = auto_splits(M, N, K);
-    if (splits == 0) splits = 1;
-    if (variant < -1) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", variant);
-    int rc = validate_sizes(M, N, K, lda, ldb, ldc);
-    if (rc != GEMM_F32_OK) return rc;
-    int64_t used = 1;
-    const int len = K > 0 ? split_len(K, splits, &used) : 0;
-    if (used <= 1 || M == 0 || N == 0)  // one split: the plain product, no workspace
-        return run(variant, variant == -1 ? -1 : config_id, false, false, 1, M, N, K, A, lda, 0, B,
-                   ldb, 0, C, ldc, 0, stream);
-    rc = validate(false, false, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0);
-    if (rc != GEMM_F32_OK) return rc;
-    const int64_t need = used * M * N * static_cast<int64_t>(sizeof(float));
-    float *W = static_cast<float *>(workspace);
-    if (W == nullptr || workspace_bytes < need)
-        return fail(GEMM_F32_EINVAL, "workspace of %lld bytes needed, %lld given", (long long)need,
-                    (long long)(W ? workspace_bytes : 0));
-    if (reinterpret_cast<uintptr_t>(W) % 4) return fail(GEMM_F32_EINVAL, "workspace not 4-byte aligned");
-    const Span sw = {reinterpret_cast<uintptr_t>(W), reinterpret_cast<uintptr_t>(W) + need};
-    if (overlaps(sw, span_of(A, M, K, lda)) || overlaps(sw, span_of(B, K, N, ldb)) ||
-        overlaps(sw, span_of(C, M, N, ldc)))
-        return fail(GEMM_F32_EINVAL, "workspace overlaps A, B or C");
-    // partial products: a strided batch over the K splits into the workspace
-    int v = variant, c = config_id;
-    const bool aligned = direct_fast(
-        operands_aligned(A, lda, len, B, ldb, static_cast<int64_t>(len) * ldb), M, N, false, false);
-    if (v == -1) select_config(used, M, N, len, &v, &c, false, aligned);
-    int count = 0;
-    const ConfigEntry *cfgs = configs_of(v, &count);
-    if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", v);
-    if (c == -1) {
-        int vv = 0;
-        select_config(used, M, N, len, &vv, &c, false, aligned);
-        if (vv != v) c = 0;
+        K <= 0x7fffffff) {
+        const int64_t fit = kScratchBytes / (M * N * static_cast<int64_t>(sizeof(float)));
+        splits = std::max<int64_t>(1, std::min(auto_splits(M, N, K), fit));
     }
-    if (c < 0 || c >= count)
-        return fail(GEMM_F32_ENOKERNEL, "variant %d has no configuration %d", v, c);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const Problem p{static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), A, lda, B,
-                    ldb, W, N, static_cast<int>(used), len, static_cast<int64_t>(len) * ldb,
-                    M * N, false, false, len};
-    hipError_t err = cfgs[c].launch(p, st);
-    if (err == hipSuccess) {
-        const bool vec4 = (N % 4) == 0 && (ldc % 4) == 0 &&
-                          reinterpret_cast<uintptr_t>(C) % 16 == 0 &&
-                          reinterpret_cast<uintptr_t>(W) % 16 == 0;
-        const int64_t items = M * (vec4 ? N / 4 : N);
-        const unsigned grid = static_cast<unsigned>(std::min<int64_t>((items + 255) / 256, 8192));
-        if (vec4)
-            hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(grid), dim3(256), 0, st, W, M * N,
-                               static_cast<int>(used), static_cast<int>(M), static_cast<int>(N), C,
-                               ldc);
-        else
-            hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(grid), dim3(256), 0, st, W, M * N,
-                               static_cast<int>(used), static_cast<int>(M), static_cast<int>(N), C,
-                               ldc);
-        err = hipGetLastError();
-    }
-    if (err != hipSuccess) return fail(GEMM_F32_EHIP, "launch failed: %s", hipGetErrorString(err));
-    return GEMM_F32_OK;
+    auto library_scratch = [](int64_t need, void *s, float **W) {
+        if (need > kScratchBytes)
+            return fail(GEMM_F32_EINVAL,
+                        "split-K partials need %lld bytes, above the %lld-byte static scratch",
+                        (long long)need, (long long)kScratchBytes);
+        return scratch_address(s, W);
+    };
+    return splitk(variant, config_id, splits, M, N, K, A, lda, B, ldb, C, ldc, library_scratch,
+                  stream);
 }
 
 int gemm_f32_ex(int variant, int config_id, int opA, int opB, int64_t batch, int64_t M,
@@ -663,6 +755,6 @@ int gemm_f32_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int
     return GEMM_F32_OK;
 }
 
-int gemm_f32_abi_version(void) { return 2; }
+int gemm_f32_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -233,6 +233,36 @@ int gemm_f32_splitk(int variant, int config_id, int64_t splits,
                     void *workspace, int64_t workspace_bytes,
                     void *stream);
 
+/*
+ * gemm_f32_splitk_noalloc -- gemm_f32_splitk for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc): the partial products go to a scratch
+ * array the library holds in device memory instead of a workspace argument.
+ *
+ * The scratch is a static device array of GEMM_F32_SPLITK_SCRATCH_BYTES
+ * bytes; every GPU the library runs on holds its own copy until the process
+ * ends.  Its device address is looked up on the first call on each device
+ * (hipGetSymbolAddress, with that device current); the call itself performs
+ * no allocation and no hipMalloc / hipFree.  Every call on one GPU uses that
+ * GPU's one array, so calls that overlap in time on the same GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ *
+ * Arguments and results are those of gemm_f32_splitk without the
+ * workspace; splits = 0 takes the library's choice capped at the number of
+ * M x N slices that fit the scratch (at most one slice: the plain product).
+ * Returns GEMM_F32_EINVAL when the partial products need more
+ * than GEMM_F32_SPLITK_SCRATCH_BYTES (gemm_f32_splitk_workspace_size tells
+ * how much they need), and GEMM_F32_EHIP when the scratch address cannot be
+ * obtained.
+ */
+#define GEMM_F32_SPLITK_SCRATCH_BYTES 33554432 /* 32 MiB */
+int gemm_f32_splitk_noalloc(int variant, int config_id, int64_t splits,
+                            int64_t M, int64_t N, int64_t K,
+                            const float *A, int64_t lda,
+                            const float *B, int64_t ldb,
+                            float *C, int64_t ldc,
+                            void *stream);
+
 /* Bytes of workspace gemm_f32_splitk needs for these arguments, splits = 0
    meaning the library's choice (0 when it needs none, or for invalid
    sizes). */
@@ -285,7 +315,8 @@ int gemm_f32_plan(int64_t M, int64_t N, int64_t K,
                   int64_t lda, int64_t ldb, int64_t ldc,
                   int *parts, int *axis, int64_t *split, int *variant, int *config_id);
 
-/* ABI version of this header: 2 (2 added gemm_f32_plan). */
+/* ABI version of this header: 3 (2 added gemm_f32_plan, 3
+   gemm_f32_splitk_noalloc). */
 int gemm_f32_abi_version(void);
 
 #ifdef __cplusplus

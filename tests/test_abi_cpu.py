@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert b.gemm_f32_abi_version() == 2
+    assert b.gemm_f32_abi_version() == 3
 
 
 def test_strerror(lib):
@@ -273,6 +273,27 @@ def test_splitk_validation(lib):
                              None) == b.GEMM_F32_ENOKERNEL
     # empty products need nothing
     assert call(M=0) == b.GEMM_F32_OK
+
+
+def test_splitk_noalloc_validation(lib):
+    """The no-allocation split-K rejects, before any device call, invalid
+    arguments and partial products larger than the library's static
+    scratch."""
+    assert b.SPLITK_SCRATCH_BYTES == 32 << 20
+
+    def call(splits, M, N, K, lda=None):
+        return b.gemm_f32_splitk_noalloc(-1, -1, splits, M, N, K, 1 << 40, lda or K, 2 << 40,
+                                         N, 3 << 40, N, None)
+
+    assert call(-1, 100, 30, 1000) == b.GEMM_F32_EINVAL and "splits" in b.gemm_f32_last_error()
+    assert call(4, 100, 30, 1000, lda=999) == b.GEMM_F32_EINVAL
+    # 16 slices of 1024 x 1024 need 64 MiB: above the 32 MiB scratch
+    assert b.gemm_f32_splitk_workspace_size(1024, 1024, 65536, 16) > b.SPLITK_SCRATCH_BYTES
+    assert call(16, 1024, 1024, 65536) == b.GEMM_F32_EINVAL
+    assert "static scratch" in b.gemm_f32_last_error()
+    assert b.gemm_f32_splitk_noalloc(-2, 0, 4, 1, 1, 1, 0x1000, 1, 0x2000, 1, 0x3000, 1,
+                                     None) == b.GEMM_F32_ENOKERNEL
+    assert call(4, 0, 30, 1000) == b.GEMM_F32_OK  # empty: nothing to do
 
 
 C_CALLER = r"""
