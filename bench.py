@@ -36,7 +36,9 @@ if ROOT not in sys.path:
 PEAK_FP32_MATRIX_TFLOPS = 157.3  # MI355X: 256 CU x 4 SIMD x 64 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 METRIC = "FP32 GEMM TFLOP/s at M=N=K=8192 on 1 MI355X; % of FP32 matrix peak"
-KERNEL_SOURCES = ["dense_fp32_gemm_row_amd/csrc/mfma.hip",
+KERNEL_SOURCES = ["dense_fp32_gemm_row_amd/csrc/mfma_kernels.h",
+                  "dense_fp32_gemm_row_amd/csrc/mfma.hip",
+                  "dense_fp32_gemm_row_amd/csrc/mfma16.hip",
                   "dense_fp32_gemm_row_amd/csrc/gemm_internal.h"]
 
 

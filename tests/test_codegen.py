@@ -33,16 +33,60 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 @pytest.fixture(scope="module")
-def mfma_asm(tmp_path_factory):
+def mfma_build(tmp_path_factory):
+    """gfx950 assembly of the MFMA kernels, and the compiler's resource
+    remarks (registers, scratch) for every kernel."""
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "mfma.s"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "--cuda-device-only", "-S", os.path.join(CSRC, "mfma.hip"), "-o", str(out)]
-    res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
-    assert res.returncode == 0, res.stderr[-2000:]
-    return out.read_text()
+    from concurrent.futures import ThreadPoolExecutor
+
+    tmp = tmp_path_factory.mktemp("asm")
+
+    def compile_one(src):
+        out = tmp / (os.path.splitext(src)[0] + ".s")
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Rpass-analysis=kernel-resource-usage",
+               "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+        assert res.returncode == 0, res.stderr[-2000:]
+        return out.read_text(), res.stderr
+
+    with ThreadPoolExecutor(max_workers=2) as ex:
+        parts = list(ex.map(compile_one, ["mfma.hip", "mfma16.hip"]))
+    return "\n".join(p[0] for p in parts), "\n".join(p[1] for p in parts)
+
+
+@pytest.fixture(scope="module")
+def mfma_asm(mfma_build):
+    return mfma_build[0]
+
+
+def test_no_kernel_spills_registers(mfma_build):
+    """MFMA kernels keep their accumulators and fragments in registers: a
+    kernel that spills to scratch memory runs at a fraction of its rate (a
+    16-wavefront 256 x 256 tile of 16 x 16 blocks needs more than the 128
+    registers per lane that four wavefronts per SIMD leave, spilled, and ran
+    at 86 TFLOP/s at 8192^3).  Known exception: the register-staged variants
+    of the two-buffer 256 x 256 x 32 tiles (their float4 staging registers on
+    top of the fragments), which run only as the mfma2p stage configuration
+    and as the fallback of the direct-load tiles for operands whose rows are
+    not 16-byte aligned and that span more than 2^29 floats."""
+    remarks = mfma_build[1]
+    names = re.findall(r"Function Name: (\S+)", remarks)
+    scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", remarks)]
+    assert len(names) == len(scratch) and len(names) > 100, (len(names), len(scratch))
+    filt = shutil.which("c++filt") or shutil.which("llvm-cxxfilt")
+    spilled = [n for n, s in zip(names, scratch) if s]
+    dem = subprocess.run([filt], input="\n".join(spilled), capture_output=True,
+                         text=True).stdout.splitlines() if spilled else []
+    unexpected = []
+    for d in dem:
+        # <BM, BN, BK, WM, WN, PADA, PADB, STAGES, DIRECT, ...>
+        args = [a.strip() for a in d[d.index("<") + 1:d.index(">")].split(",")]
+        if not (args[:3] == ["256", "256", "32"] and args[7] == "2" and args[8] == "false"):
+            unexpected.append(d)
+    assert not unexpected, f"{len(unexpected)} kernels use scratch: {unexpected[:3]}"
 
 
 def loops(body: str) -> list[str]:

@@ -1,4 +1,4 @@
-"""Host-side models of the edge-tile load schemes in csrc/mfma.hip: the
+"""Host-side models of the edge-tile load schemes in csrc/mfma_kernels.h: the
 clamped register staging (OperandTile::init, init_clamp, load_clamped, and
 RingTile's split of K into whole K-steps plus a tail), then the 4-byte
 direct loads into LDS with range-checked zero fill (rows that are not
