@@ -27,6 +27,12 @@ at the same level.
 
     python -m dense_fp32_gemm_row_amd.tune.autotune --out tuned.json --calibrate
 
+Timing: every timed loop runs behind a long launch (two 8192^3 products),
+so that the host has enqueued all timed launches before the first one runs
+and the events around each launch time the GPU, not the host's launch cost
+(which exceeds the kernel on small products).  The launch floor subtracted
+above is then the GPU's own cost of a 1 x 1 x 1 launch of the candidate.
+
 Correctness of every configuration is established separately by the parity
 tests; this script only measures.
 """
@@ -75,7 +81,7 @@ CAL_UNALIGNED = [(1000, 1023, 7777), (2049, 2049, 2049), (3001, 3001, 3001), (40
 CAL_SHORTK = [(8192, 8192, 64), (8192, 8192, 128), (16384, 16384, 128), (16384, 16384, 256)]
 
 
-def calibrate_model(binding, model: dict, budget_ms: float) -> dict:
+def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dict:
     """Measured per-CU rates of the model's candidates (see the module doc)."""
     import math
     import statistics
@@ -95,7 +101,7 @@ def calibrate_model(binding, model: dict, budget_ms: float) -> dict:
             def call(cfg=cfg):
                 binding.gemm(dA, dB, dC, variant="mfma", config=cfg)
 
-            times[(cfg, M, N, K)] = time_fn(call, budget_ms)
+            times[(cfg, M, N, K)] = time_fn(call, budget_ms, blocker)
             print(json.dumps({"calibrate": cfg, "M": M, "N": N, "K": K,
                               "median_ms": round(times[(cfg, M, N, K)], 5)}), flush=True)
         del dA, dB, dC
@@ -143,26 +149,54 @@ def calibrate_model(binding, model: dict, budget_ms: float) -> dict:
     return out
 
 
-def time_config(binding, v, c, dA, dB, dC, reps, warmup):
+def make_blocker(binding):
+    """A launch of about 15 ms (two 8192^3 products).  Enqueued before a
+    timed loop, it keeps the GPU busy while the host enqueues every timed
+    launch, so that the events around each launch time the GPU's work (and
+    its gap between kernels) rather than the host's launch cost, which
+    exceeds the kernel time of small products."""
+    import torch
+
+    n = 8192
+    bA = torch.zeros((n, n), device="cuda")
+    bB = torch.zeros((n, n), device="cuda")
+    bC = torch.empty((n, n), device="cuda")
+    fn = binding.prepare(bA, bB, bC)
+
+    def block():
+        fn()
+        fn()
+
+    # prepare() keeps raw device addresses: the tensors must outlive every
+    # call of the blocker (freed, their memory could be reused or unmapped)
+    block.operands = (bA, bB, bC)
+    return block
+
+
+def time_config(binding, v, c, dA, dB, dC, reps, warmup, blocker=None):
     import torch
 
     stream = torch.cuda.current_stream()
+    launch = binding.prepare(dA, dB, dC, variant=v, config=c)
     for _ in range(warmup):
-        binding.gemm(dA, dB, dC, variant=v, config=c)
+        launch()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
+    if blocker is not None:
+        blocker()
     for s, e in ev:
         s.record(stream)
-        binding.gemm(dA, dB, dC, variant=v, config=c)
+        launch()
         e.record(stream)
     torch.cuda.synchronize()
     times = sorted(s.elapsed_time(e) for s, e in ev)
     return times[len(times) // 2]
 
 
-def time_fn(fn, budget_ms: float) -> float:
-    """Median milliseconds of fn() over enough launches to fill ~budget_ms."""
+def time_fn(fn, budget_ms: float, blocker=None) -> float:
+    """Median milliseconds of fn() over enough launches to fill ~budget_ms
+    (behind `blocker`, a long launch, when given: see make_blocker)."""
     import torch
 
     stream = torch.cuda.current_stream()
@@ -179,6 +213,8 @@ def time_fn(fn, budget_ms: float) -> float:
     reps = int(max(5, min(500, budget_ms / max(min(probe), 1e-3))))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
+    if blocker is not None:
+        blocker()
     for s, e in ev:
         s.record(stream)
         fn()
@@ -195,10 +231,19 @@ def main() -> int:
                     help="table whose defaults are kept")
     ap.add_argument("--variants", default="mfma")
     ap.add_argument("--shapes", default=",".join(s[0] for s in DEFAULT_SHAPES))
+    ap.add_argument("--extra", default="",
+                    help="comma-separated further shapes MxNxK to time (reported; written to "
+                         "the table only with --keep-extra)")
+    ap.add_argument("--keep-extra", action="store_true")
     ap.add_argument("--budget-ms", type=float, default=400.0,
                     help="approximate timed milliseconds per configuration")
     ap.add_argument("--calibrate", action="store_true",
                     help="also re-measure the cost model's per-CU rates (written to --out)")
+    ap.add_argument("--configs", default="",
+                    help="comma-separated configuration names to time (default: all)")
+    ap.add_argument("--no-queue-ahead", action="store_true",
+                    help="time launches without a long launch ahead of them (the events then "
+                         "include the host's launch cost on small products)")
     ap.add_argument("--splits", default="",
                     help="comma-separated split counts: also time gemm_f32_splitk with each "
                          "(reported, not written to the table)")
@@ -210,11 +255,18 @@ def main() -> int:
 
     binding.load()
     shapes = [s for s in DEFAULT_SHAPES if s[0] in args.shapes.split(",")]
+    extra = []
+    for x in (x for x in args.extra.split(",") if x):
+        M, N, K = (int(v) for v in x.split("x"))
+        extra.append((x, M, N, K))
+    shapes += extra
     variants = [binding.VARIANTS[v] for v in args.variants.split(",")]
     with open(args.base) as f:
         table = json.load(f)
     entries = {(e["M"], e["N"], e["K"]): e for e in table.get("entries", [])}
     report = []
+    blocker = None if args.no_queue_ahead else make_blocker(binding)
+    only = set(x for x in args.configs.split(",") if x)
     for name, M, N, K in shapes:
         g = torch.Generator(device="cuda").manual_seed(0)
         dA = torch.rand((M, K), device="cuda", generator=g) * 2 - 1
@@ -225,9 +277,11 @@ def main() -> int:
         for v in variants:
             for c in range(binding.gemm_f32_config_count(v)):
                 cname = binding.gemm_f32_config_name(v, c)
-                probe = time_config(binding, v, c, dA, dB, dC, reps=3, warmup=1)
+                if only and cname not in only:
+                    continue
+                probe = time_config(binding, v, c, dA, dB, dC, reps=3, warmup=1, blocker=blocker)
                 reps = int(max(5, min(500, args.budget_ms / max(probe, 1e-3))))
-                ms = time_config(binding, v, c, dA, dB, dC, reps=reps, warmup=2)
+                ms = time_config(binding, v, c, dA, dB, dC, reps=reps, warmup=2, blocker=blocker)
                 results.append((ms, cname))
                 print(json.dumps({"shape": name, "M": M, "N": N, "K": K, "config": cname,
                                   "median_ms": round(ms, 5),
@@ -248,15 +302,17 @@ def main() -> int:
                                       "tflops": round(flops / ms / 1e9, 3)}), flush=True)
         results.sort()
         best_ms, best = results[0]
-        entries[(M, N, K)] = {"M": M, "N": N, "K": K, "config": best, "shape": name,
-                              "median_ms": round(best_ms, 5),
-                              "tflops": round(flops / best_ms / 1e9, 3)}
-        report.append(entries[(M, N, K)])
+        best_entry = {"M": M, "N": N, "K": K, "config": best, "shape": name,
+                      "median_ms": round(best_ms, 5), "tflops": round(flops / best_ms / 1e9, 3)}
+        if (name, M, N, K) not in extra or args.keep_extra:
+            entries[(M, N, K)] = best_entry
+        report.append(best_entry)
         del dA, dB, dC
         torch.cuda.empty_cache()
     table["entries"] = sorted(entries.values(), key=lambda e: (e["M"], e["N"], e["K"]))
     if args.calibrate:
-        table["model"] = calibrate_model(binding, table["model"], min(args.budget_ms, 200.0))
+        table["model"] = calibrate_model(binding, table["model"], min(args.budget_ms, 200.0),
+                                         blocker)
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     with open(args.out, "w") as f:
         json.dump(table, f, indent=2)

@@ -157,9 +157,13 @@ def test_cost_model_choices(lib):
         v, c = b.gemm_f32_select(M, N, K, lda or K, ldb or N, N)
         return b.gemm_f32_config_name(v, c)
 
-    assert "64x64" in pick(512, 512, 512)
+    def tile(name):
+        bm, bn = (int(x) for x in name.split("_")[1].split("x")[:2])
+        return bm * bn
+
+    assert tile(pick(512, 512, 512)) <= 64 * 64      # 16 x 64 tiles (16x16x4 instructions)
     assert pick(8192, 8192, 8192 + 64) == "mfma2d_256x256x32_w4x4_swz_g4_il"
-    assert "64x64" in pick(3072, 3072, 3072)
+    assert tile(pick(3072, 3072, 3072)) <= 64 * 64
     # 256 tiles of 256 x 128 or 128 x 256: exactly one wave
     assert pick(8192, 1024, 4096) in {"mfma3d_256x128x32_w4x2_swz_il", "mfma3d_128x256x16_w2x4_swz_il"}
     # the same shape with rows that are not 16-byte aligned may choose differently,
