@@ -283,7 +283,8 @@ def prepare(A, B, out, *, variant: int | str | None = None, config: int | str = 
     or gemm_batched when ``batched``), with the operands checked and the C
     arguments built once: for launch loops, where the per-call checks of
     gemm would cost more host time than a small product takes on the GPU.
-    A, B and out must stay alive and unchanged in place while it is used."""
+    The callable holds references to A, B and out, so their memory stays
+    allocated while it exists; they must not be resized or re-strided."""
     name, args, _ = _marshal(A, B, out, variant, config, stream, batched)
     fn = getattr(load(), name)
 
@@ -292,6 +293,7 @@ def prepare(A, B, out, *, variant: int | str | None = None, config: int | str = 
         if rc != GEMM_F32_OK:
             raise GemmError(rc, gemm_f32_last_error())
 
+    launch.operands = (A, B, out)  # the raw addresses in args point into these
     return launch
 
 
