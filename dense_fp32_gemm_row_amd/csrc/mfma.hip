@@ -64,6 +64,9 @@ const ConfigEntry kMfmaConfigs[] = {
     {"mfma4d_64x64x64_w2x2_k4_swz", launch_mfma<64, 64, 64, 2, 2, -1, 0, 8, 4, true, true, false, 4>, kCapTransposed},
     {"mfma2_64x64x64_w2x2_k4_swz", launch_mfma<64, 64, 64, 2, 2, -1, 0, 8, 2, false, true, false, 4>, kCapTransposed},
     {"mfma3_256x256x16_w4x4_swz_g4_il", launch_mfma<256, 256, 16, 4, 4, -1, 0, 4, 3, false, true, true>, kCapTransposed},
+    // Register staging with two register sets (mfma2r): each K-step's loads
+    // are issued two steps ahead of their LDS store.
+    {"mfma2r_64x64x64_w2x2_k4_swz", launch_mfma<64, 64, 64, 2, 2, -1, 0, 8, 2, false, true, false, 4, 32, 2>, kCapTransposed},
 };
 
 }  // namespace

@@ -66,6 +66,8 @@
 
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_internal.h"
 
 namespace gemm_f32_impl {
@@ -372,7 +374,7 @@ struct OperandTile {
     int64_t ld;
     int r0, rlim;
     int ro[L], co[L], st[L];  // tile coordinates and LDS offset of each slot
-    float4 reg[L];
+    float4 reg[2][L];  // register staging: one or two sets of the tile in flight
     const float *src[J];
     int dst[J];
     __amdgpu_buffer_rsrc_t rsrc;  // DW: the operand as a buffer
@@ -464,20 +466,21 @@ struct OperandTile {
             }
         }
     }
+    template <int SET = 0>
     __device__ __forceinline__ void load_clamped(int k0) {
         const int64_t step = KMAJOR ? static_cast<int64_t>(k0) * ld : k0;
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const float *q = cp[i] + step;
-            if constexpr (VEC) reg[i] = *reinterpret_cast<const float4 *>(q);
-            else reg[i] = make_float4(q[0], q[1], q[2], q[3]);
+            if constexpr (VEC) reg[SET][i] = *reinterpret_cast<const float4 *>(q);
+            else reg[SET][i] = make_float4(q[0], q[1], q[2], q[3]);
         }
     }
 
     // Register staging of the tile of K-step starting at k0 (G: with zero
     // fill outside the operand; the direct-load kernels use it for a
     // partial last K-step).
-    template <bool G = GUARD>
+    template <bool G = GUARD, int SET = 0>
     __device__ __forceinline__ void load(int k0, int K) {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
@@ -485,17 +488,18 @@ struct OperandTile {
                 const int gk = k0 + ro[i];
                 const bool ok = !G || gk < K;
                 const float *row = X + static_cast<int64_t>(ok ? gk : 0) * ld + r0;
-                reg[i] = load_row4<G, VEC>(row, co[i], rlim - r0, ok);
+                reg[SET][i] = load_row4<G, VEC>(row, co[i], rlim - r0, ok);
             } else {
                 const bool ok = !G || r0 + ro[i] < rlim;
                 const float *row = X + static_cast<int64_t>(ok ? r0 + ro[i] : 0) * ld;
-                reg[i] = load_row4<G, VEC>(row, k0 + co[i], K, ok);
+                reg[SET][i] = load_row4<G, VEC>(row, k0 + co[i], K, ok);
             }
         }
     }
+    template <int SET = 0>
     __device__ __forceinline__ void store(float *buf) const {
 #pragma unroll
-        for (int i = 0; i < L; ++i) *reinterpret_cast<float4 *>(&buf[st[i]]) = reg[i];
+        for (int i = 0; i < L; ++i) *reinterpret_cast<float4 *>(&buf[st[i]]) = reg[SET][i];
     }
 
     // Direct loads of the tile of K-step k0 into `buf`: one instruction moves
@@ -648,11 +652,16 @@ struct OperandTile {
 // the tile at (m0, n0), with the LDS buffers of the workgroup.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
           bool GUARD, bool VEC, bool TA, bool TB, bool IL, int KG = 1, bool CL = false,
-          int MS = 32>
+          int MS = 32, int RSETS = 1>
 struct RingTile {
     // CL: register staging of an edge launch with clamped loads over the
     // whole K-steps and the partial last K-step as a zero-filled tail.
     static_assert(!CL || (GUARD && !DIRECT), "clamped loads: register staging with edges");
+    // RSETS = 2: register staging with two register sets, so that the loads
+    // of a K-step are issued two steps before their LDS store (two LDS
+    // buffers): twice the time for them to land.
+    static_assert(RSETS == 1 || (RSETS == 2 && STAGES == 2 && !DIRECT),
+                  "two register sets: register staging with two LDS buffers");
     static constexpr bool TAIL = (DIRECT && VEC) || CL;  // a partial last K-step runs after the loop
     static constexpr int NWG = WM * WN;  // wavefronts per k-group
     static constexpr int NW = NWG * KG, NT = 64 * NW;
@@ -723,6 +732,23 @@ struct RingTile {
                 tb.store(sB[buf]);
             }
         };
+        // register staging into (from) register set SET_C::value
+        auto load_set = [&](int k0, auto set_c) {
+            constexpr int SET = decltype(set_c)::value;
+            if constexpr (CL) {
+                ta.template load_clamped<SET>(k0);
+                tb.template load_clamped<SET>(k0);
+            } else {
+                ta.template load<GUARD, SET>(k0, K);
+                tb.template load<GUARD, SET>(k0, K);
+            }
+        };
+        auto store_set = [&](int buf, auto set_c) {
+            constexpr int SET = decltype(set_c)::value;
+            ta.template store<SET>(sA[buf]);
+            tb.template store<SET>(sB[buf]);
+        };
+        (void)load_set, (void)store_set;
 
         const int half = lane / MS;  // lane group along k
         const int l32 = lane % MS;   // row (column) of the lane in its block
@@ -763,6 +789,71 @@ struct RingTile {
         // With clamped loads the K-step that holds the last k always goes to
         // the tail, whole or partial.
         const int nk = CL ? (K - 1) / BK : (K + BK - 1) / BK - (TAIL && (K % BK) ? 1 : 0);
+        auto issue_pairs = [&] {
+            // Issue order for the scheduler: the reads of the next chunk go
+            // out one per MFMA at the start of this chunk, so their latency
+            // hides behind the remaining MFMAs and the matrix pipe never
+            // waits for a burst of reads.
+#pragma unroll
+            for (int r = 0; r < kPairs; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            }
+            if constexpr (kReadsPerChunk > kPairs)
+                __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerChunk - kPairs, 0);
+            if constexpr (kMfmaPerChunk > kPairs)
+                __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk - kPairs, 0);
+        };
+        if constexpr (RSETS == 2) {
+            // Two register sets: step t reads LDS buffer t % 2.  At its top
+            // it loads step t + 2 into register set t % 2 (stored to LDS at
+            // the end of step t - 1), and before its barrier it stores set
+            // (t + 1) % 2 (step t + 1, loaded at the top of step t - 1) into
+            // buffer (t + 1) % 2 (last read in step t - 1).  The loop runs
+            // steps in pairs, so buffer and set indices are constants.
+            using S0 = std::integral_constant<int, 0>;
+            using S1 = std::integral_constant<int, 1>;
+            if (0 < nk) {
+                load_set(0, S0{});
+                store_set(0, S0{});
+            }
+            if (1 < nk) load_set(BK, S1{});
+            __syncthreads();
+            read_frag(0, 0, 0);
+            // The loads are unconditional (the last two steps load the last
+            // whole step again, in bounds, and their stores are never read):
+            // behind a branch the compiler could not tell whether they had
+            // been issued, and waited for them before the store of step t + 1.
+            auto kstep = [&](int t, auto set_c) {
+                constexpr int CUR = decltype(set_c)::value, NXT = 1 - CUR;
+                load_set(min(t + 2, nk - 1) * BK, set_c);
+                __builtin_amdgcn_sched_barrier(0);  // the loads go out first
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const int set = kc & 1;
+                    if (kc == KC - 1) {
+                        // stale but in-bounds in the last step
+                        store_set(NXT, std::integral_constant<int, NXT>{});
+                        __builtin_amdgcn_sched_barrier(0);
+                        __syncthreads();
+                        read_frag(set ^ 1, NXT, 0);
+                    } else {
+                        read_frag(set ^ 1, CUR, kc + 1);
+                    }
+                    mfma_chunk(set);
+                    issue_pairs();
+                }
+            };
+            // Whole pairs in the loop, an odd last step after it: with the
+            // second step of a pair behind a branch, the compiler moved the
+            // loads of set 0 into that branch, next to their store.
+            int t = 0;
+            for (; t + 1 < nk; t += 2) {
+                kstep(t, S0{});
+                kstep(t + 1, S1{});
+            }
+            if (t < nk) kstep(t, S0{});
+        } else {
 #pragma unroll
         for (int st = 0; st < STAGES - 1; ++st) {
             if (st < nk) {
@@ -842,6 +933,7 @@ struct RingTile {
                 if (t + 1 < nk) __syncthreads();
             }
             cur = nxt;
+        }
         }
 
         // Tail of the direct-load and clamped kernels: the partial last
@@ -968,7 +1060,7 @@ struct RingTile {
 };
 
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int STAGES, bool DIRECT,
-          bool GUARD, bool VEC, bool TA, bool TB, bool IL, int KG, bool CL, int MS>
+          bool GUARD, bool VEC, bool TA, bool TB, bool IL, int KG, bool CL, int MS, int RSETS>
 __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_mfma_ring_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
     const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
@@ -976,7 +1068,7 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_mfma_ring_kernel(
     // DIRECT and GUARD together: direct loads clamped at the M and N edges
     // (see OperandTile) and guarded stores; K is whole K-steps.
     using Full = RingTile<BM, BN, BK, WM, WN, PADA, PADB, STAGES, DIRECT, GUARD, VEC, TA, TB, IL, KG,
-                          CL, MS>;
+                          CL, MS, RSETS>;
 
     __shared__ __align__(16) float sA[STAGES][Full::TileA::SIZE];
     __shared__ __align__(16) float sB[STAGES][Full::TileB::SIZE];
@@ -998,13 +1090,17 @@ __global__ __launch_bounds__(64 * WM * WN * KG) void gemm_mfma_ring_kernel(
 // KG: k-groups of WM x WN wavefronts (pipelined kernel only).
 // MS: 32 (v_mfma_f32_32x32x2_f32) or 16 (v_mfma_f32_16x16x4_f32) blocks
 // (16: pipelined kernel only).
+// RSETS: 2 for two register sets in the register-staged kernels of a
+// two-buffer configuration (RingTile); direct loads are unaffected.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int GROUP_M, int PIPE,
-          bool DIRECT = false, bool TRANS = false, bool IL = false, int KG = 1, int MS = 32>
+          bool DIRECT = false, bool TRANS = false, bool IL = false, int KG = 1, int MS = 32,
+          int RSETS = 1>
 hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
     static_assert(!TRANS || PIPE > 0, "transposed operands need the pipelined kernel");
     static_assert(!IL || PIPE > 0, "interleaved blocks need the pipelined kernel");
     static_assert(KG == 1 || PIPE > 0, "k-groups need the pipelined kernel");
     static_assert(MS == 32 || PIPE > 0, "16 x 16 blocks need the pipelined kernel");
+    static_assert(RSETS == 1 || PIPE == 2, "two register sets: two LDS buffers");
     constexpr int NT = 64 * WM * WN * KG;
     if ((p.ta || p.tb) && !TRANS) return hipErrorNotSupported;
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
@@ -1019,7 +1115,7 @@ hipError_t launch_mfma(const Problem &p, hipStream_t stream) {
 #define GEMM_RING(D, G, V, TA, TB, CL_)                                                        \
     hipLaunchKernelGGL(                                                                         \
         (gemm_mfma_ring_kernel<BM, BN, BK, WM, WN, PADA, PADB, ((D) || PIPE < 4 ? PIPE : 3), D, G, \
-                               V, TA, TB, IL, KG, CL_, MS>),                                         \
+                               V, TA, TB, IL, KG, CL_, MS, ((D) ? 1 : RSETS)>),                      \
         g, b, 0,                                                                                \
         stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, GROUP_M,   \
         batch_of(p))
