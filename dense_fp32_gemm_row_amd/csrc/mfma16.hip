@@ -27,9 +27,12 @@ const ConfigEntry kMfma16Configs[] = {
     {"mfma2d_128x128x32_w4x2_m16_il", launch_mfma<128, 128, 32, 4, 2, -1, 0, 8, 2, true, true, true, 1, 16>, kCapTransposed},
     // register staging with two register sets (loads two K-steps ahead)
     {"mfma2r_64x64x64_w4x1_k2_m16_il", launch_mfma<64, 64, 64, 4, 1, -1, 0, 8, 2, false, true, true, 2, 16, 2>, kCapTransposed},
-    {"mfma2r_64x64x128_w4x1_k4_m16_il", launch_mfma<64, 64, 128, 4, 1, -1, 0, 8, 2, false, true, true, 4, 16, 2>, kCapTransposed},
     // small tiles for products with few output tiles (256^3: 64 or 32 tiles)
     {"mfma2d_16x64x128_w1x1_k4_m16_il", launch_mfma<16, 64, 128, 1, 1, -1, 0, 8, 2, true, true, true, 4, 16>, kCapTransposed},
+    // one K-step of 256: a short K runs as a single step after one load
+    {"mfma2d_16x16x256_w1x1_k4_m16", launch_mfma<16, 16, 256, 1, 1, -1, 0, 8, 2, true, true, false, 4, 16>, kCapTransposed},
+    {"mfma2d_16x32x256_w1x1_k4_m16_il", launch_mfma<16, 32, 256, 1, 1, -1, 0, 8, 2, true, true, true, 4, 16>, kCapTransposed},
+    {"mfma2d_16x64x256_w1x1_k4_m16_il", launch_mfma<16, 64, 256, 1, 1, -1, 0, 8, 2, true, true, true, 4, 16>, kCapTransposed},
     {"mfma2d_32x64x64_w2x1_k2_m16_il", launch_mfma<32, 64, 64, 2, 1, -1, 0, 8, 2, true, true, true, 2, 16>, kCapTransposed},
 };
 

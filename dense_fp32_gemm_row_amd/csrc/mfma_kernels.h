@@ -374,7 +374,12 @@ struct OperandTile {
     int64_t ld;
     int r0, rlim;
     int ro[L], co[L], st[L];  // tile coordinates and LDS offset of each slot
-    float4 reg[2][L];  // register staging: one or two sets of the tile in flight
+    // Register staging: one or two sets of the tile in flight, and the tail
+    // step loaded early (two register sets).  Native vectors: with HIP's
+    // float4 struct the copies became memcpys, and with the tail set live
+    // across the loop the compiler kept them in scratch memory.
+    floatx4 reg[2][L];
+    floatx4 treg[L];
     const float *src[J];
     int dst[J];
     __amdgpu_buffer_rsrc_t rsrc;  // DW: the operand as a buffer
@@ -472,15 +477,23 @@ struct OperandTile {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const float *q = cp[i] + step;
-            if constexpr (VEC) reg[SET][i] = *reinterpret_cast<const float4 *>(q);
-            else reg[SET][i] = make_float4(q[0], q[1], q[2], q[3]);
+            if constexpr (VEC) reg[SET][i] = *reinterpret_cast<const floatx4 *>(q);
+            else reg[SET][i] = floatx4{q[0], q[1], q[2], q[3]};
         }
     }
 
     // Register staging of the tile of K-step starting at k0 (G: with zero
     // fill outside the operand; the direct-load kernels use it for a
     // partial last K-step).
-    template <bool G = GUARD, int SET = 0>
+    template <int SET>
+    __device__ __forceinline__ void set_reg(int i, float4 v) {
+        const floatx4 x = {v.x, v.y, v.z, v.w};
+        if constexpr (SET == 2) treg[i] = x;
+        else reg[SET][i] = x;
+    }
+    // (V16 = false: four 4-byte loads that the compiler merges where all four
+    // are in range, also for aligned rows)
+    template <bool G = GUARD, int SET = 0, bool V16 = VEC>
     __device__ __forceinline__ void load(int k0, int K) {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
@@ -488,18 +501,19 @@ struct OperandTile {
                 const int gk = k0 + ro[i];
                 const bool ok = !G || gk < K;
                 const float *row = X + static_cast<int64_t>(ok ? gk : 0) * ld + r0;
-                reg[SET][i] = load_row4<G, VEC>(row, co[i], rlim - r0, ok);
+                set_reg<SET>(i, load_row4<G, V16>(row, co[i], rlim - r0, ok));
             } else {
                 const bool ok = !G || r0 + ro[i] < rlim;
                 const float *row = X + static_cast<int64_t>(ok ? r0 + ro[i] : 0) * ld;
-                reg[SET][i] = load_row4<G, VEC>(row, k0 + co[i], K, ok);
+                set_reg<SET>(i, load_row4<G, V16>(row, k0 + co[i], K, ok));
             }
         }
     }
     template <int SET = 0>
     __device__ __forceinline__ void store(float *buf) const {
 #pragma unroll
-        for (int i = 0; i < L; ++i) *reinterpret_cast<float4 *>(&buf[st[i]]) = reg[SET][i];
+        for (int i = 0; i < L; ++i)
+            *reinterpret_cast<floatx4 *>(&buf[st[i]]) = SET == 2 ? treg[i] : reg[SET & 1][i];
     }
 
     // Direct loads of the tile of K-step k0 into `buf`: one instruction moves
@@ -804,6 +818,17 @@ struct RingTile {
             if constexpr (kMfmaPerChunk > kPairs)
                 __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerChunk - kPairs, 0);
         };
+        // With two register sets, the tail's zero-filled loads (set 2) go out
+        // before the loop: their latency is then off the critical path.  (As
+        // 4-byte loads: the aligned 16-byte form, held across the loop, made
+        // the compiler keep it in scratch memory.)
+        constexpr bool EARLY_TAIL = RSETS == 2 && TAIL;
+        if constexpr (EARLY_TAIL) {
+            if (CL || K % BK) {
+                ta.template load<true, 2, false>(nk * BK, K);
+                tb.template load<true, 2, false>(nk * BK, K);
+            }
+        }
         if constexpr (RSETS == 2) {
             // Two register sets: step t reads LDS buffer t % 2.  At its top
             // it loads step t + 2 into register set t % 2 (stored to LDS at
@@ -939,20 +964,29 @@ struct RingTile {
         // Tail of the direct-load and clamped kernels: the partial last
         // K-step, staged through registers with zero fill past K (and past
         // the M / N edges), once all waves are done with the loop's buffers.
-        // One exposed global-load latency per tile; its registers are not
-        // live in the loop.
+        // One exposed global-load latency per tile (none with two register
+        // sets, which load it before the loop); its registers are not live in
+        // the loop otherwise.  A wavefront whose share of the step lies
+        // wholly past K skips it: it holds only zeros.
         if constexpr (TAIL) {
             if (CL || K % BK) {
-                ta.template load<true>(nk * BK, K);
-                tb.template load<true>(nk * BK, K);
+                if constexpr (!EARLY_TAIL) {
+                    ta.template load<true>(nk * BK, K);
+                    tb.template load<true>(nk * BK, K);
+                }
+                constexpr int TS = EARLY_TAIL ? 2 : 0;
                 __syncthreads();
-                ta.store(sA[0]);
-                tb.store(sB[0]);
+                ta.template store<TS>(sA[0]);
+                tb.template store<TS>(sB[0]);
                 __syncthreads();
+                // (one test per wavefront: a test per chunk made the compiler
+                // keep the fragments in scratch memory)
+                if (nk * BK + kg * KC * CK < K) {
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    read_frag(0, 0, kc);
-                    mfma_chunk(0);
+                    for (int kc = 0; kc < KC; ++kc) {
+                        read_frag(0, 0, kc);
+                        mfma_chunk(0);
+                    }
                 }
             }
         }
