@@ -7,8 +7,10 @@ default workload is M = N = K = 8192 with uniform[-1, 1) inputs from seed 0.
 
 Prints ONE JSON line with the throughput (TFLOP/s = 2 M N K / time), the
 dominant kernel's roofline position (measured live with HIP events on the
-stream the kernel runs on), the oracle timed on the host's cores on a bounded
-sample of the same workload, and a parity check of the timed output.
+stream the kernel runs on), the oracle timed on the host's cores, and a parity
+check of the timed output against that oracle run: every row of the product
+when the oracle finishes it within --full-oracle-seconds, else a bounded
+sample of rows plus a Freivalds projection.
 Each step is its own launch with an event pair around it; with --graph the
 steps are captured into one HIP graph and timed as one replay, which removes
 the host's cost per launch (it bounds the small workloads).
