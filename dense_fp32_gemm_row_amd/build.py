@@ -30,7 +30,7 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-SOURCES = ["mfma.hip", "mfma16.hip", "api.hip", "naive.hip", "lds_tiled.hip", "regblock.hip"]
+SOURCES = ["mfma.hip", "mfma16.hip", "mfma_regs.hip", "api.hip", "naive.hip", "lds_tiled.hip", "regblock.hip"]
 
 
 def _compile(src: str, extra: list[str]) -> str:

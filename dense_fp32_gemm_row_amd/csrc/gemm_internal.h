@@ -60,6 +60,7 @@ const ConfigEntry *lds_configs(int *count);
 const ConfigEntry *regblock_configs(int *count);
 const ConfigEntry *mfma_configs(int *count);    // all MFMA configurations
 const ConfigEntry *mfma16_configs(int *count);  // those with 16x16x4 instructions
+const ConfigEntry *mfma_regs_configs(int *count);  // operands loaded straight into registers
 
 // Sets the C region to zero (the K == 0 case).  A fill kernel rather than a
 // memset so that a captured graph replays it faithfully and ldc padding is

@@ -1,6 +1,6 @@
 // Tile configurations of the MFMA kernels (csrc/mfma_kernels.h) with
 // 32 x 32 x 2 instructions, and the registry of every MFMA configuration
-// (these, then those of csrc/mfma16.hip).
+// (these, then those of csrc/mfma16.hip and csrc/mfma_regs.hip).
 
 #include <vector>
 
@@ -77,6 +77,9 @@ const ConfigEntry *mfma_configs(int *count) {
         int n16 = 0;
         const ConfigEntry *c16 = mfma16_configs(&n16);
         v.insert(v.end(), c16, c16 + n16);
+        int nr = 0;
+        const ConfigEntry *cr = mfma_regs_configs(&nr);
+        v.insert(v.end(), cr, cr + nr);
         return v;
     }();
     *count = static_cast<int>(all.size());

@@ -1,0 +1,376 @@
+// MFMA tiles whose operands go from global memory straight into registers.
+//
+// For products with about one output tile per CU and a moderate K (the
+// ragged 1000 x 1023 x 777 shape: 256 tiles of 64 x 64, 13 K-steps of 64)
+// the LDS-staged kernels spend a sixth of every K-step on the LDS round trip
+// and the barrier that ends it, with only eight matrix instructions per
+// wavefront between two barriers.  Here each wavefront loads the MFMA
+// operands it needs itself, in the register layout the instruction takes,
+// a few chunks of 16 k ahead: no LDS stores, no LDS reads and no barrier in
+// the K loop.  Wavefronts that read the same rows of A or columns of B share
+// them through the L1 cache instead of LDS.  LDS serves only the sum of the
+// k-groups' partial tiles at the end.
+//
+// Blocking ("Tiled GEMM: Matrix Multiplication in CUDA", section 2): a
+// workgroup owns a BM x BN tile of C; KG k-groups of WM x WN wavefronts split
+// K between them in chunks of 16 (chunk c goes to group c mod KG), and each
+// wavefront of a group accumulates a (BM / WM) x (BN / WN) slice for its
+// chunks in 16 x 16 blocks of v_mfma_f32_16x16x4_f32 (FM x FN blocks).  The
+// partial tiles are then added in LDS in group order, a fixed order, and
+// group 0 stores the tile ("Tiled Matrix Multiplication in CUDA", section
+// 5: one final write per output element).
+//
+// Operand layout of one chunk of 16 k.  Lane l = 16 g + i supplies, to
+// instruction s (s = 0..3), A[row][4 g + s] and B[4 g + s][col]: a fixed
+// permutation of the chunk applied to A and B alike, so lane l's four A
+// values of a row block are A[row][4 g .. 4 g + 3], one 16-byte load.  Block
+// f of A holds rows 16 f + i of the slice; column block j of B holds column
+// FN i + j (interleaved), so a lane's FN values of B in one k row are
+// adjacent, one load of 4 FN bytes.  Per chunk a lane issues FM + 4 loads for
+// 4 FM FN instructions.
+//
+// Edges ("Tiled GEMM: Matrix Multiplication in CUDA", section 7.1).  The K
+// loop runs the chunks that hold neither a k past K nor the last k of the
+// operand, with clamped addresses and no per-element checks: a row of A past
+// M loads row M - 1, a group of FN columns of B that starts past N loads the
+// group that holds column N - 1, and a group that starts inside the row
+// loads as it is (its floats past N come from the row's padding or the next
+// k row, which exists inside the loop).  Those values only feed outputs that
+// are never stored.  The chunk that holds the last k, whole or partial, is a
+// tail with zero fill past K and N, loaded before the loop.  Shapes where a
+// group can reach past the operand's storage even so (N < FN - 1) run a
+// variant that checks every element.  Stores are guarded.
+//
+// Roofline: MFMA bound per K-step (4 FM FN instructions of 32 cycles per
+// FM + 4 loads); the tile's fixed cost (first loads, the k-group sum, the
+// stores) is what a short K exposes.
+
+#include "mfma_kernels.h"
+
+namespace gemm_f32_impl {
+namespace {
+
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// N consecutive floats at q (4-byte alignment): one load of 4 N bytes per
+// 16-byte piece, which global memory accepts at any 4-byte alignment.
+template <int N>
+__device__ __forceinline__ void load_run(const float *q, float (&v)[N]) {
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int p = 0; p < N; p += 4) {
+            const floatx4 t = floatx4{q[p], q[p + 1], q[p + 2], q[p + 3]};
+            v[p] = t[0], v[p + 1] = t[1], v[p + 2] = t[2], v[p + 3] = t[3];
+        }
+    } else if constexpr (N == 2) {
+        const floatx2 t = floatx2{q[0], q[1]};
+        v[0] = t[0], v[1] = t[1];
+    } else {
+        v[0] = q[0];
+    }
+}
+template <int N>
+__device__ __forceinline__ void store_run(float *q, const float (&v)[N]) {
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int p = 0; p < N; p += 4)
+            *reinterpret_cast<floatx4 *>(q + p) = floatx4{v[p], v[p + 1], v[p + 2], v[p + 3]};
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<floatx2 *>(q) = floatx2{v[0], v[1]};
+    } else {
+        q[0] = v[0];
+    }
+}
+
+// Rows (f, r) of a wavefront's slice that one pass of the k-group sum
+// handles: a multiple of KG that divides FM x 4, as many as LDS holds.
+constexpr int regs_pass_rows(int FM, int FN, int KG, int NWG) {
+    int best = 0;
+    for (int rp = KG; rp <= FM * 4; rp += KG)
+        if ((FM * 4) % rp == 0 && KG * NWG * rp * 64 * FN * 4 <= kLdsBytes) best = rp;
+    return best;
+}
+
+// EDGE: 0 = whole tiles and whole chunks (no checks), 1 = clamped loop and a
+// zero-filled tail, 2 = every load checked (tiny N).
+// OCC: wavefronts per SIMD at most (one workgroup per CU with OCC = 1: two
+// 64 x 64 tiles that share a CU thrash its L1 and ran at half the rate).
+// ET: the tail's loads go out before the loop, into registers of their own.
+template <int BM, int BN, int WM, int WN, int KG, int D, int OCC, bool ET, int EDGE>
+__global__ __launch_bounds__(64 * WM * WN * KG) __attribute__((amdgpu_waves_per_eu(1, OCC)))
+void gemm_mfma_regs_kernel(
+    int M, int N, int K, const float *__restrict__ A, int64_t lda,
+    const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
+    int tiles_m, int tiles_n, int group_m, BatchArgs bt) {
+    constexpr int NWG = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int CK = 16;  // k per chunk: four 16x16x4 instructions per block
+    static_assert(WTM % 16 == 0 && (FN == 1 || FN == 2 || FN % 4 == 0), "16 x 16 blocks");
+    static_assert(D >= 2, "at least two chunks in flight");
+    constexpr int RP = KG > 1 ? regs_pass_rows(FM, FN, KG, NWG) : 1;
+    static_assert(KG == 1 || RP > 0, "LDS room for the k-group sum");
+    constexpr int RED = KG > 1 ? KG * NWG * RP * 64 * FN : 1;  // floats
+    __shared__ __align__(16) float red[RED];
+
+    int tm, tn;
+    const int tile = batch_select(xcd_remap(blockIdx.x, tiles_m * tiles_n * bt.count),
+                                  tiles_m * tiles_n, bt, A, B, C, K);
+    grouped_tile(tile, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave / NWG, wg = wave % NWG;
+    const int wm = wg / WN, wn = wg % WN;
+    const int g = lane / 16, i = lane % 16;
+
+    // The lane's rows of A (one per row block) and first column of B.
+    const float *pa[FM];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+        const int row = m0 + wm * WTM + 16 * f + i;
+        const int r = EDGE && row > M - 1 ? M - 1 : row;
+        pa[f] = A + static_cast<int64_t>(r) * lda + 4 * g;
+    }
+    const int bcol = n0 + wn * WTN + FN * i;
+    const int bcol_c = EDGE && bcol > N - 1 ? ((N - 1) / FN) * FN : bcol;
+    const float *pb = B + static_cast<int64_t>(4 * g) * ldb + bcol_c;
+
+    // Chunks of the loop (clamped addresses) and the tail chunk, if any.
+    const int nloop = EDGE == 0 ? K / CK : EDGE == 1 ? (K - 1) / CK : 0;
+    const int nchunks = EDGE == 0 ? nloop : (K + CK - 1) / CK;  // with the tail (or all, checked)
+    // this group's chunks of the loop: kg, kg + KG, ...
+    const int ng = nloop > kg ? (nloop - kg + KG - 1) / KG : 0;
+
+    float ra[D][FM][4];
+    float rb[D][4][FN];
+    auto load = [&](float (&xa)[FM][4], float (&xb)[4][FN], int c) {  // chunk c, clamped
+        const int k0 = c * CK;
+        const int64_t boff = static_cast<int64_t>(k0) * ldb;
+#pragma unroll
+        for (int f = 0; f < FM; ++f) load_run<4>(pa[f] + k0, xa[f]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) load_run<FN>(pb + boff + s * ldb, xb[s]);
+    };
+    // Zero-filled load of chunk c past K and N (rows of A are clamped):
+    // vector loads where all of a lane's values are in range, single floats
+    // where they straddle K or N.
+    auto load_checked = [&](float (&xa)[FM][4], float (&xb)[4][FN], int c) {
+        const int k0 = c * CK + 4 * g;
+#pragma unroll
+        for (int f = 0; f < FM; ++f) {
+            const float *q = pa[f] + c * CK;
+            if (k0 + 3 < K) {
+                load_run<4>(q, xa[f]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xa[f][e] = k0 + e < K ? q[e] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const bool ok = k0 + s < K;
+            const float *q = B + static_cast<int64_t>(ok ? k0 + s : 0) * ldb + bcol;
+            if (ok && bcol + FN - 1 < N) {
+                load_run<FN>(q, xb[s]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < FN; ++e) xb[s][e] = ok && bcol + e < N ? q[e] : 0.0f;
+            }
+        }
+    };
+
+    floatx4 acc[FM][FN];
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[f][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // instructions s0, s0 + SS, ... of a chunk
+    auto mma = [&](const float (&xa)[FM][4], const float (&xb)[4][FN], int s0 = 0, int ss = 1) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < s0 || (s - s0) % ss) continue;
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[f][s], xb[s][j], acc[f][j], 0, 0, 0);
+        }
+    };
+
+    // The tail chunk (the one that holds the last k) is shared by the
+    // groups: instruction s of it goes to group s mod KG.
+    constexpr int TS = KG < 4 ? KG : 4;  // groups with a share of the tail
+    const bool tail_mine = EDGE == 1 && nchunks > nloop && kg < TS;
+    float ta[ET ? FM : 1][4];
+    float tb[ET ? 4 : 1][FN];
+    if constexpr (EDGE == 1 && ET) {
+        if (tail_mine) load_checked(ta, tb, nloop);
+    }
+
+    if constexpr (EDGE == 2) {
+        // every chunk checked (shapes too narrow for the clamped loads)
+        for (int c = kg; c < nchunks; c += KG) {
+            load_checked(ra[0], rb[0], c);
+            mma(ra[0], rb[0]);
+        }
+    } else if (ng > 0) {
+        // Set u holds the group's chunk t with t mod D = u; after the
+        // instructions of chunk t, the same set loads chunk t + D (the last
+        // chunk again past the end: in bounds, never used).
+#pragma unroll
+        for (int u = 0; u < D; ++u) load(ra[u], rb[u], kg + KG * min(u, ng - 1));
+        int t = 0;
+        for (; t + D <= ng; t += D) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) {
+                mma(ra[u], rb[u]);
+                __builtin_amdgcn_sched_barrier(0);
+                load(ra[u], rb[u], kg + KG * min(t + u + D, ng - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < D - 1; ++u)
+            if (t + u < ng) mma(ra[u], rb[u]);
+    }
+    if constexpr (EDGE == 1) {
+        if (tail_mine) {
+            if constexpr (ET) {
+                mma(ta, tb, kg, TS);
+            } else {
+                load_checked(ra[0], rb[0], nloop);
+                mma(ra[0], rb[0], kg, TS);
+            }
+        }
+    }
+
+    // Register r of block (f, j): row 16 f + 4 g + r of the slice, column
+    // FN i + j.  With k-groups every wavefront leaves its partial slice in
+    // LDS, RP rows (f, r) per pass, and the KG wavefronts that share a slice
+    // each add up a KG-th of the pass's rows over the groups in group order
+    // (a fixed order) and store them.
+    const bool vec_c = (EDGE == 0 || (m0 + BM <= M && n0 + BN <= N)) &&
+                       ((reinterpret_cast<uintptr_t>(C) | static_cast<uintptr_t>(ldc * 4)) &
+                        (4 * (FN < 4 ? FN : 4) - 1)) == 0;
+    const int crow0 = m0 + wm * WTM + 4 * g;
+    auto store_row = [&](int fr, const float (&v)[FN]) {
+        const int gm = crow0 + 16 * (fr / 4) + fr % 4;
+        float *row = C + static_cast<int64_t>(gm) * ldc + bcol;
+        if (vec_c) {
+            store_run<FN>(row, v);
+        } else {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                if (gm < M && bcol + j < N) row[j] = v[j];
+        }
+    };
+    if constexpr (KG > 1) {
+        // red[group][wave of group][row of the pass][lane][j]: a lane's FN
+        // values of one row are adjacent
+        auto part = [&](int h, int q) { return red + ((h * NWG + wg) * RP + q) * 64 * FN + lane * FN; };
+#pragma unroll
+        for (int pass = 0; pass < FM * 4 / RP; ++pass) {
+            if (pass > 0) __syncthreads();  // the previous pass's reads are done
+#pragma unroll
+            for (int q = 0; q < RP; ++q) {
+                const int fr = pass * RP + q;
+                float v[FN];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) v[j] = acc[fr / 4][j][fr % 4];
+                store_run<FN>(part(kg, q), v);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int qq = 0; qq < RP / KG; ++qq) {
+                const int q = kg + qq * KG;
+                float v[FN];
+#pragma unroll
+                for (int h = 0; h < KG; ++h) {
+                    float x[FN];
+                    const float *src = part(h, q);
+                    if constexpr (FN >= 4) {
+#pragma unroll
+                        for (int p = 0; p < FN; p += 4) {
+                            const floatx4 t4 = *reinterpret_cast<const floatx4 *>(src + p);
+                            x[p] = t4[0], x[p + 1] = t4[1], x[p + 2] = t4[2], x[p + 3] = t4[3];
+                        }
+                    } else if constexpr (FN == 2) {
+                        const floatx2 t2 = *reinterpret_cast<const floatx2 *>(src);
+                        x[0] = t2[0], x[1] = t2[1];
+                    } else {
+                        x[0] = src[0];
+                    }
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) v[j] = h == 0 ? x[j] : v[j] + x[j];
+                }
+                store_row(pass * RP + q, v);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int fr = 0; fr < FM * 4; ++fr) {
+            float v[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) v[j] = acc[fr / 4][j][fr % 4];
+            store_row(fr, v);
+        }
+    }
+}
+
+// Launch of one configuration: row-major operands only.
+// WHOLE: compile the unchecked kernel for whole tiles and chunks (the
+// 128 x 128 tiles spill registers in it and run the clamped one instead,
+// whose last chunk is then a tail).
+template <int BM, int BN, int WM, int WN, int KG, int D, int OCC, bool ET, bool WHOLE, int GROUP_M>
+hipError_t launch_regs(const Problem &p, hipStream_t stream) {
+    constexpr int NT = 64 * WM * WN * KG;
+    constexpr int FN = BN / WN / 16;
+    if (p.ta || p.tb) return hipErrorNotSupported;
+    const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
+    const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * p.batch;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool whole = p.M % BM == 0 && p.N % BN == 0 && p.K % 16 == 0 &&
+                       (p.ksplit == 0 || p.ksplit % 16 == 0);
+    const dim3 gd(static_cast<unsigned>(grid)), bd(NT);
+#define GEMM_REGS(E)                                                                              \
+    hipLaunchKernelGGL((gemm_mfma_regs_kernel<BM, BN, WM, WN, KG, D, OCC, ET, E>), gd, bd, 0, stream, p.M, \
+                       p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, GROUP_M,  \
+                       batch_of(p))
+    if (whole && WHOLE) {
+        if constexpr (WHOLE) GEMM_REGS(0);
+    } else if (p.N >= FN - 1) {
+        GEMM_REGS(1);
+    }
+    else {
+        GEMM_REGS(2);
+    }
+#undef GEMM_REGS
+    return hipGetLastError();
+}
+
+const ConfigEntry kRegsConfigs[] = {
+    // operands straight from global memory into registers (mfmag): four
+    // k-groups of one wavefront that each own the whole tile (no operand
+    // loaded twice), D chunks in flight per wavefront, one wavefront per
+    // SIMD.  (The K-step in the name is KG chunks of 16.)  Measured and not
+    // kept: four wavefronts per group (w4x1, w2x2: each operand loaded by two
+    // or four wavefronts; ragged 1000 x 1023 x 777 32 against 21 us), eight
+    // groups of one wavefront (two per SIMD), 32 x 64 and 128 x 64 tiles,
+    // and D from 2 to 6 (within 2%).
+    {"mfmag_64x64x64_w1x1_k4_d3", launch_regs<64, 64, 1, 1, 4, 3, 1, true, true, 8>, 0},
+    // 128 x 128: 256 accumulator floats per lane
+    {"mfmag_128x128x64_w1x1_k4_d2", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8>, 0},
+};
+
+}  // namespace
+
+const ConfigEntry *mfma_regs_configs(int *count) {
+    *count = static_cast<int>(sizeof(kRegsConfigs) / sizeof(kRegsConfigs[0]));
+    return kRegsConfigs;
+}
+
+}  // namespace gemm_f32_impl

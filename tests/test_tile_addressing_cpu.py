@@ -311,3 +311,130 @@ def test_splitk_model_sees_the_unchecked_overrun():
     reads = slice_reads(K, length, used, BK, K % BK != 0)
     assert reads[0][1] > reads[0][2]
     assert reads[-1][1] > K
+
+
+# --------------------------------------------------------------------------
+# Operands loaded straight into registers (csrc/mfma_regs.hip): every lane
+# loads, per chunk of 16 k, A[row][16 c + 4 g .. + 3] for each of its row
+# blocks and B[16 c + 4 g + s][col .. col + FN - 1] for s = 0..3, with rows
+# past M clamped to M - 1 and column groups that start past N clamped to the
+# group holding column N - 1.  The loop runs chunks 0 .. (K - 1) / 16 - 1
+# (whole chunks only, with edges), the chunk of the last k is a checked tail,
+# and shapes with N < FN - 1 check every element.
+# --------------------------------------------------------------------------
+
+# (BM, BN, WM, WN, KG, whole): the register-direct configurations and other
+# splits of the same kernel template; whole = False: whole shapes also run the
+# clamped kernel (its last chunk a tail)
+REGS_TILES = [(64, 64, 1, 1, 4, True), (128, 128, 1, 1, 4, False), (128, 64, 1, 1, 4, True),
+              (64, 64, 4, 1, 4, True), (64, 64, 2, 2, 4, True), (32, 64, 1, 1, 8, True),
+              (64, 64, 1, 1, 2, True), (64, 64, 1, 1, 1, True)]
+REGS_SHAPES = [  # M, N, K, lda pad, ldb pad
+    (257, 259, 97, 0, 0), (64, 64, 64, 0, 0), (128, 64, 48, 0, 0), (65, 67, 17, 0, 0),
+    (1, 1, 1, 0, 0), (3, 2, 5, 0, 0), (70, 3, 33, 2, 0), (5, 2, 100, 0, 0), (64, 1, 16, 0, 0),
+    (33, 7, 16, 0, 0), (130, 129, 31, 1, 3), (1, 4, 32, 0, 0), (17, 5, 15, 0, 0), (40, 6, 50, 0, 0),
+    (129, 8, 20, 0, 0), (256, 256, 64, 0, 0)]
+
+
+def regs_model(BM, BN, WM, WN, KG, M, N, K, lda, ldb, whole_ok=True):
+    """Every load of the register-direct kernel as (first float, length), the
+    element each in-range operand position receives, and the k values each
+    tile's k-groups cover, restated from the kernel."""
+    WTM, WTN = BM // WM, BN // WN
+    FM, FN = WTM // 16, WTN // 16
+    whole = M % BM == 0 and N % BN == 0 and K % 16 == 0 and whole_ok
+    edge = 0 if whole else (1 if N >= FN - 1 else 2)
+    nloop = K // 16 if edge == 0 else ((K - 1) // 16 if edge == 1 else 0)
+    nchunks = nloop if edge == 0 else (K + 15) // 16
+    loads = {"A": [], "B": []}
+    wrong = []
+    covered = {}
+    for m0 in range(0, M, BM):
+        for n0 in range(0, N, BN):
+            ks = []
+            for kg in range(KG):
+                mine = [(c, False) for c in range(nloop) if c % KG == kg]
+                ks += [16 * c + q for c, _ in mine for q in range(16)]
+                if edge == 2:
+                    mine = [(c, True) for c in range(nchunks) if c % KG == kg]
+                    ks += [16 * c + q for c, _ in mine for q in range(16) if 16 * c + q < K]
+                elif nchunks > nloop and kg < min(KG, 4):
+                    # the tail: instruction s (k = 16 c + 4 g + s) goes to group s mod min(KG, 4)
+                    ts = min(KG, 4)
+                    mine.append((nloop, True))
+                    ks += [16 * nloop + 4 * gg + s for gg in range(4) for s in range(4)
+                           if s % ts == kg and 16 * nloop + 4 * gg + s < K]
+                for wm in range(WM):
+                    for wn in range(WN):
+                        for g in range(4):
+                            for i in range(16):
+                                for c, checked in mine:
+                                    for f in range(FM):
+                                        r = m0 + wm * WTM + 16 * f + i
+                                        rc = min(r, M - 1) if edge else r
+                                        for e in range(4):
+                                            k = 16 * c + 4 * g + e
+                                            if checked and k >= K:
+                                                continue  # zero fill
+                                            addr = rc * lda + k
+                                            if r < M and addr != r * lda + k:
+                                                wrong.append(("A", r, k, addr))
+                                        if checked:
+                                            loads["A"] += [(rc * lda + 16 * c + 4 * g + e, 1) for e in range(4)
+                                                           if 16 * c + 4 * g + e < K]
+                                        else:
+                                            loads["A"].append((rc * lda + 16 * c + 4 * g, 4))
+                                    bcol = n0 + wn * WTN + FN * i
+                                    bcol_c = ((N - 1) // FN) * FN if edge and bcol > N - 1 else bcol
+                                    for s in range(4):
+                                        k = 16 * c + 4 * g + s
+                                        if checked:
+                                            for j in range(FN):
+                                                if k < K and bcol + j < N:
+                                                    loads["B"].append((k * ldb + bcol + j, 1))
+                                            continue
+                                        loads["B"].append((k * ldb + bcol_c, FN))
+                                        for j in range(FN):
+                                            if bcol + j < N and k * ldb + bcol_c + j != k * ldb + bcol + j:
+                                                wrong.append(("B", k, bcol + j))
+            covered[(m0, n0)] = sorted(ks)
+    return loads, wrong, covered
+
+
+@pytest.mark.parametrize("tile", REGS_TILES, ids=lambda t: "x".join(map(str, t)))
+def test_register_direct_loads_inside_and_complete(tile):
+    """Every load of the register-direct kernel lies inside the operands'
+    storage ((rows - 1) ld + cols floats), every position that feeds a
+    stored output receives its own element, and each tile's k-groups cover
+    every k < K exactly once (the tail's positions past K are zero on both
+    sides)."""
+    BM, BN, WM, WN, KG, whole_ok = tile
+    for M, N, K, pa, pb in REGS_SHAPES:
+        lda, ldb = K + pa, N + pb
+        loads, wrong, covered = regs_model(BM, BN, WM, WN, KG, M, N, K, lda, ldb, whole_ok)
+        ends = {"A": (M - 1) * lda + K, "B": (K - 1) * ldb + N}
+        for op in "AB":
+            for first, length in loads[op]:
+                assert 0 <= first and first + length <= ends[op], (op, tile, (M, N, K), first, length)
+        assert not wrong, (tile, (M, N, K), wrong[:3])
+        for key, ks in covered.items():
+            assert ks == list(range(K)), (tile, (M, N, K), key)
+
+
+def test_register_direct_model_sees_a_loop_over_the_last_chunk():
+    """The check above fails if the loop also ran the chunk of the last k
+    with clamped loads (no tail): a group of columns that straddles N then
+    reads past the end of B in the last k row."""
+    BM, BN, WM, WN, KG, _ = REGS_TILES[0]
+    M, N, K = 65, 67, 32  # K whole chunks, N not a multiple of 4
+    lda, ldb = K, N
+    WTN, FN = BN // WN, BN // WN // 16
+    b_end = (K - 1) * ldb + N
+    overrun = False
+    for n0 in range(0, N, BN):
+        for i in range(16):
+            bcol = n0 + FN * i
+            bcol_c = ((N - 1) // FN) * FN if bcol > N - 1 else bcol
+            k = K - 1  # the last k row, loaded unchecked
+            overrun |= k * ldb + bcol_c + FN > b_end
+    assert overrun
