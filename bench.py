@@ -41,6 +41,7 @@ METRIC = "FP32 GEMM TFLOP/s at M=N=K=8192 on 1 MI355X; % of FP32 matrix peak"
 KERNEL_SOURCES = ["dense_fp32_gemm_row_amd/csrc/mfma_kernels.h",
                   "dense_fp32_gemm_row_amd/csrc/mfma.hip",
                   "dense_fp32_gemm_row_amd/csrc/mfma16.hip",
+                  "dense_fp32_gemm_row_amd/csrc/mfma_regs.hip",
                   "dense_fp32_gemm_row_amd/csrc/gemm_internal.h"]
 
 
