@@ -468,7 +468,8 @@ BATCH_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4"), (1, 1, "lds_t32"),
         "mfma2p_256x256x32_w4x4_swz_pb0", "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz_g4",
         "mfma2d_256x256x32_w2x4_swz_g4_il", "mfma2d_256x256x32_w4x4_swz_g4_il",
         "mfma2d_64x64x128_w2x2_k4_swz", "mfma2d_64x64x64_w2x2_k4_swz",
-        "mfma3_256x256x16_w4x4_swz_g4_il", "mfma2_64x64x64_w2x2_k4_swz")]
+        "mfma3_256x256x16_w4x4_swz_g4_il", "mfma2_64x64x64_w2x2_k4_swz",
+        "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2")]
 
 
 def _run_batched(A3, B3, M, N, K, nb, sa, sb, sc, lda, ldb, ldc, kernel):
@@ -643,7 +644,7 @@ SPLITK_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4"), (1, 1, "lds_t32"),
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in (
         "mfma_64x64x32_w2x2_pa4_pb0", "mfma3_64x64x16_w2x2_swz_pb0", "mfma3_128x128x16_w2x2_swz_pb0",
         "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz", "mfma2d_64x64x64_w2x2_k4_swz",
-        "mfma2d_64x64x128_w2x2_k4_swz")]
+        "mfma2d_64x64x128_w2x2_k4_swz", "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2")]
 
 
 @pytest.mark.parametrize("kernel", SPLITK_KERNELS, ids=[k[2] for k in SPLITK_KERNELS])
@@ -685,7 +686,8 @@ def test_splitk_full_tiles(kernel):
 SPLITK_WHOLE_K = [(None, -1, "select")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in (
         "mfma2_64x64x64_w2x2_k4_swz", "mfma2d_64x64x64_w2x2_k4_swz", "mfma2d_64x64x128_w2x2_k4_swz",
-        "mfma4d_64x64x64_w2x2_k4_swz", "mfma2d_256x256x32_w4x4_swz_g4_il")]
+        "mfma4d_64x64x64_w2x2_k4_swz", "mfma2d_256x256x32_w4x4_swz_g4_il",
+        "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2")]
 
 
 @pytest.mark.parametrize("kernel", SPLITK_WHOLE_K, ids=[k[2] for k in SPLITK_WHOLE_K])
