@@ -220,11 +220,12 @@ int validate(bool ta, bool tb, int64_t batch, int64_t M, int64_t N, int64_t K, c
 
 // Predicted microseconds of one candidate on a (batch of) M x N x K.
 double model_us(const ModelCandidate &m, int64_t batch, int64_t M, int64_t N, int64_t K,
-                bool aligned) {
+                bool aligned, bool trans) {
     const int64_t tiles = ((M + m.bm - 1) / m.bm) * ((N + m.bn - 1) / m.bn) * batch;
     const int64_t n = (tiles + kModelCUs - 1) / kModelCUs;
     const int level = static_cast<int>(n < m.nrates ? n : m.nrates);
-    const double rate = m.gflops_per_cu[level > 0 ? level - 1 : 0] * (aligned ? 1.0 : m.unaligned);
+    const double rate = m.gflops_per_cu[level > 0 ? level - 1 : 0] * (aligned ? 1.0 : m.unaligned) *
+                        (trans ? m.trans : 1.0);
     return static_cast<double>(n) * 2.0 * m.bm * m.bn * (static_cast<double>(K) + m.k0) /
            (rate * 1e3);
 }
@@ -261,7 +262,7 @@ double best_candidate(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans
     *config = -1;
     for (int i = 0; i < kModelSize; ++i) {
         if (!usable(i, trans)) continue;
-        const double t = model_us(kModel[i], batch, M, N, K, aligned);
+        const double t = model_us(kModel[i], batch, M, N, K, aligned, trans);
         if (*config < 0 || t < best_t) *config = model_ids().id[i], best_t = t;
     }
     if (*config < 0) *config = 0;
@@ -340,7 +341,7 @@ Plan search_plan(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans, boo
                 const int64_t m1 = axis == 0 ? first : M, n1 = axis == 0 ? N : first;
                 const int64_t m2 = axis == 0 ? M - first : M, n2 = axis == 0 ? N : N - first;
                 int c2 = -1;
-                const double t = model_us(m, batch, m1, n1, K, aligned) +
+                const double t = model_us(m, batch, m1, n1, K, aligned, trans) +
                                  best_candidate(batch, m2, n2, K, trans, aligned, &c2) + kLaunchUs;
                 // one configuration in two launches only looks faster: each
                 // launch would count at the one-tile-per-CU rate, but the

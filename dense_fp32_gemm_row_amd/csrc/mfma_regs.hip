@@ -91,12 +91,104 @@ constexpr int regs_pass_rows(int FM, int FN, int KG, int NWG) {
     return best;
 }
 
+// One operand of a wavefront's slice: F blocks of 16 rows (of op(A)) or
+// columns (of op(B)), for lane i of lane group g; x[f][s] is the value the
+// lane feeds to instruction s of a chunk for block f, at k = k0 + 4 g + s.
+//  * Row flavour (KMAJOR = false): element (r, k) at X[r ld + k], k
+//    contiguous (A as stored, B transposed).  A chunk's 4 values of block f
+//    are one 16-byte load.
+//  * K-major flavour (KMAJOR = true): element (r, k) at X[k ld + r], r
+//    contiguous (B as stored, A transposed).  With interleaved blocks a
+//    lane's F values of one k row are adjacent: one load of 4 F bytes per s.
+// Block f holds rows base + F i + f (IL, interleaved) or base + 16 f + i.
+// CLAMP: rows past R (row flavour) load row R - 1, a k-major group that
+// starts past R loads the group that holds row R - 1 (their values feed
+// outputs that are never stored).
+template <bool KMAJOR, int F, bool IL>
+struct RegOperand {
+    static_assert(!KMAJOR || IL, "k-major operands are interleaved");
+    const float *X;
+    int64_t ld;
+    int r0, R;                 // first row of the lane's group (or block 0), rows of the operand
+    const float *p[KMAJOR ? 1 : F];
+
+    __device__ __forceinline__ int row(int base, int i, int f) const {
+        return IL ? base + F * i + f : base + 16 * f + i;
+    }
+    __device__ __forceinline__ void init(const float *X_, int64_t ld_, int R_, int base, int g, int i,
+                                         bool clamp) {
+        X = X_, ld = ld_, R = R_;
+        r0 = row(base, i, 0);
+        if constexpr (KMAJOR) {
+            const int r = clamp && r0 > R - 1 ? ((R - 1) / F) * F : r0;
+            p[0] = X + static_cast<int64_t>(4 * g) * ld + r;
+        } else {
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+                const int rr = row(base, i, f);
+                const int r = clamp && rr > R - 1 ? R - 1 : rr;
+                p[f] = X + static_cast<int64_t>(r) * ld + 4 * g;
+            }
+        }
+    }
+    // chunk c, clamped addresses
+    __device__ __forceinline__ void load(float (&x)[F][4], int c) const {
+        const int k0 = c * 16;
+        if constexpr (KMAJOR) {
+            const float *q = p[0] + static_cast<int64_t>(k0) * ld;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                float v[F];
+                load_run<F>(q + s * ld, v);
+#pragma unroll
+                for (int f = 0; f < F; ++f) x[f][s] = v[f];
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < F; ++f) load_run<4>(p[f] + k0, x[f]);
+        }
+    }
+    // chunk c with zero fill past K and R: vector loads where all of a
+    // lane's values are in range, single floats where they straddle K or R
+    __device__ __forceinline__ void load_checked(float (&x)[F][4], int c, int g, int K) const {
+        const int k0 = c * 16 + 4 * g;
+        if constexpr (KMAJOR) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bool ok = k0 + s < K;
+                const float *q = X + static_cast<int64_t>(ok ? k0 + s : 0) * ld + r0;
+                float v[F];
+                if (ok && r0 + F - 1 < R) {
+                    load_run<F>(q, v);
+                } else {
+#pragma unroll
+                    for (int f = 0; f < F; ++f) v[f] = ok && r0 + f < R ? q[f] : 0.0f;
+                }
+#pragma unroll
+                for (int f = 0; f < F; ++f) x[f][s] = v[f];
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+                const float *q = p[f] + c * 16;  // row clamped: only unstored outputs see it
+                if (k0 + 3 < K) {
+                    load_run<4>(q, x[f]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[f][e] = k0 + e < K ? q[e] : 0.0f;
+                }
+            }
+        }
+    }
+};
+
 // EDGE: 0 = whole tiles and whole chunks (no checks), 1 = clamped loop and a
 // zero-filled tail, 2 = every load checked (tiny N).
 // OCC: wavefronts per SIMD at most (one workgroup per CU with OCC = 1: two
 // 64 x 64 tiles that share a CU thrash its L1 and ran at half the rate).
 // ET: the tail's loads go out before the loop, into registers of their own.
-template <int BM, int BN, int WM, int WN, int KG, int D, int OCC, bool ET, int EDGE>
+// TA / TB: op(A) = A^T (A stored K x M) / op(B) = B^T (B stored N x K).
+template <int BM, int BN, int WM, int WN, int KG, int D, int OCC, bool ET, bool TA, bool TB, int EDGE>
 __global__ __launch_bounds__(64 * WM * WN * KG) __attribute__((amdgpu_waves_per_eu(1, OCC)))
 void gemm_mfma_regs_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
@@ -126,17 +218,13 @@ void gemm_mfma_regs_kernel(
     const int wm = wg / WN, wn = wg % WN;
     const int g = lane / 16, i = lane % 16;
 
-    // The lane's rows of A (one per row block) and first column of B.
-    const float *pa[FM];
-#pragma unroll
-    for (int f = 0; f < FM; ++f) {
-        const int row = m0 + wm * WTM + 16 * f + i;
-        const int r = EDGE && row > M - 1 ? M - 1 : row;
-        pa[f] = A + static_cast<int64_t>(r) * lda + 4 * g;
-    }
-    const int bcol = n0 + wn * WTN + FN * i;
-    const int bcol_c = EDGE && bcol > N - 1 ? ((N - 1) / FN) * FN : bcol;
-    const float *pb = B + static_cast<int64_t>(4 * g) * ldb + bcol_c;
+    // A's blocks: rows 16 f + i of the slice (as stored) or FM i + f
+    // (transposed, k-major); B's blocks: columns FN i + j either way.
+    RegOperand<TA, FM, TA> opa;
+    RegOperand<!TB, FN, true> opb;
+    const int arow0 = m0 + wm * WTM, bcol = n0 + wn * WTN + FN * i;
+    opa.init(A, lda, M, arow0, g, i, EDGE != 0);
+    opb.init(B, ldb, N, n0 + wn * WTN, g, i, EDGE != 0);
 
     // Chunks of the loop (clamped addresses) and the tail chunk, if any.
     const int nloop = EDGE == 0 ? K / CK : EDGE == 1 ? (K - 1) / CK : 0;
@@ -145,41 +233,14 @@ void gemm_mfma_regs_kernel(
     const int ng = nloop > kg ? (nloop - kg + KG - 1) / KG : 0;
 
     float ra[D][FM][4];
-    float rb[D][4][FN];
-    auto load = [&](float (&xa)[FM][4], float (&xb)[4][FN], int c) {  // chunk c, clamped
-        const int k0 = c * CK;
-        const int64_t boff = static_cast<int64_t>(k0) * ldb;
-#pragma unroll
-        for (int f = 0; f < FM; ++f) load_run<4>(pa[f] + k0, xa[f]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) load_run<FN>(pb + boff + s * ldb, xb[s]);
+    float rb[D][FN][4];
+    auto load = [&](float (&xa)[FM][4], float (&xb)[FN][4], int c) {
+        opa.load(xa, c);
+        opb.load(xb, c);
     };
-    // Zero-filled load of chunk c past K and N (rows of A are clamped):
-    // vector loads where all of a lane's values are in range, single floats
-    // where they straddle K or N.
-    auto load_checked = [&](float (&xa)[FM][4], float (&xb)[4][FN], int c) {
-        const int k0 = c * CK + 4 * g;
-#pragma unroll
-        for (int f = 0; f < FM; ++f) {
-            const float *q = pa[f] + c * CK;
-            if (k0 + 3 < K) {
-                load_run<4>(q, xa[f]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xa[f][e] = k0 + e < K ? q[e] : 0.0f;
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const bool ok = k0 + s < K;
-            const float *q = B + static_cast<int64_t>(ok ? k0 + s : 0) * ldb + bcol;
-            if (ok && bcol + FN - 1 < N) {
-                load_run<FN>(q, xb[s]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < FN; ++e) xb[s][e] = ok && bcol + e < N ? q[e] : 0.0f;
-            }
-        }
+    auto load_checked = [&](float (&xa)[FM][4], float (&xb)[FN][4], int c) {
+        opa.load_checked(xa, c, g, K);
+        opb.load_checked(xb, c, g, K);
     };
 
     floatx4 acc[FM][FN];
@@ -189,7 +250,7 @@ void gemm_mfma_regs_kernel(
         for (int j = 0; j < FN; ++j) acc[f][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // instructions s0, s0 + SS, ... of a chunk
-    auto mma = [&](const float (&xa)[FM][4], const float (&xb)[4][FN], int s0 = 0, int ss = 1) {
+    auto mma = [&](const float (&xa)[FM][4], const float (&xb)[FN][4], int s0 = 0, int ss = 1) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             if (s < s0 || (s - s0) % ss) continue;
@@ -197,7 +258,7 @@ void gemm_mfma_regs_kernel(
             for (int f = 0; f < FM; ++f)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[f][s], xb[s][j], acc[f][j], 0, 0, 0);
+                    acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[f][s], xb[j][s], acc[f][j], 0, 0, 0);
         }
     };
 
@@ -206,7 +267,7 @@ void gemm_mfma_regs_kernel(
     constexpr int TS = KG < 4 ? KG : 4;  // groups with a share of the tail
     const bool tail_mine = EDGE == 1 && nchunks > nloop && kg < TS;
     float ta[ET ? FM : 1][4];
-    float tb[ET ? 4 : 1][FN];
+    float tb[ET ? FN : 1][4];
     if constexpr (EDGE == 1 && ET) {
         if (tail_mine) load_checked(ta, tb, nloop);
     }
@@ -248,17 +309,17 @@ void gemm_mfma_regs_kernel(
         }
     }
 
-    // Register r of block (f, j): row 16 f + 4 g + r of the slice, column
-    // FN i + j.  With k-groups every wavefront leaves its partial slice in
+    // Register r of block (f, j): row 16 f + 4 g + r of the slice (A
+    // transposed: FM (4 g + r) + f), column FN i + j.  With k-groups every wavefront leaves its partial slice in
     // LDS, RP rows (f, r) per pass, and the KG wavefronts that share a slice
     // each add up a KG-th of the pass's rows over the groups in group order
     // (a fixed order) and store them.
     const bool vec_c = (EDGE == 0 || (m0 + BM <= M && n0 + BN <= N)) &&
                        ((reinterpret_cast<uintptr_t>(C) | static_cast<uintptr_t>(ldc * 4)) &
                         (4 * (FN < 4 ? FN : 4) - 1)) == 0;
-    const int crow0 = m0 + wm * WTM + 4 * g;
     auto store_row = [&](int fr, const float (&v)[FN]) {
-        const int gm = crow0 + 16 * (fr / 4) + fr % 4;
+        const int f = fr / 4, r = fr % 4;
+        const int gm = arow0 + (TA ? FM * (4 * g + r) + f : 16 * f + 4 * g + r);
         float *row = C + static_cast<int64_t>(gm) * ldc + bcol;
         if (vec_c) {
             store_run<FN>(row, v);
@@ -321,33 +382,39 @@ void gemm_mfma_regs_kernel(
     }
 }
 
-// Launch of one configuration: row-major operands only.
+// Launch of one configuration.
 // WHOLE: compile the unchecked kernel for whole tiles and chunks (the
 // 128 x 128 tiles spill registers in it and run the clamped one instead,
 // whose last chunk is then a tail).
 template <int BM, int BN, int WM, int WN, int KG, int D, int OCC, bool ET, bool WHOLE, int GROUP_M>
 hipError_t launch_regs(const Problem &p, hipStream_t stream) {
     constexpr int NT = 64 * WM * WN * KG;
-    constexpr int FN = BN / WN / 16;
-    if (p.ta || p.tb) return hipErrorNotSupported;
+    constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
     const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * p.batch;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool whole = p.M % BM == 0 && p.N % BN == 0 && p.K % 16 == 0 &&
                        (p.ksplit == 0 || p.ksplit % 16 == 0);
+    // clamped k-major groups stay inside the operand when its rows are at
+    // least one group less one long
+    const bool clamp_ok = (!p.ta || p.M >= FM - 1) && (p.tb || p.N >= FN - 1);
+    const int edge = whole && WHOLE ? 0 : clamp_ok ? 1 : 2;
     const dim3 gd(static_cast<unsigned>(grid)), bd(NT);
-#define GEMM_REGS(E)                                                                              \
-    hipLaunchKernelGGL((gemm_mfma_regs_kernel<BM, BN, WM, WN, KG, D, OCC, ET, E>), gd, bd, 0, stream, p.M, \
-                       p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n, GROUP_M,  \
-                       batch_of(p))
-    if (whole && WHOLE) {
-        if constexpr (WHOLE) GEMM_REGS(0);
-    } else if (p.N >= FN - 1) {
-        GEMM_REGS(1);
-    }
-    else {
-        GEMM_REGS(2);
-    }
+#define GEMM_REGS(TA_, TB_, E)                                                                      \
+    hipLaunchKernelGGL((gemm_mfma_regs_kernel<BM, BN, WM, WN, KG, D, OCC, ET, TA_, TB_, E>), gd, bd, \
+                       0, stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m,       \
+                       tiles_n, GROUP_M, batch_of(p))
+#define GEMM_REGS_E(TA_, TB_)                       \
+    do {                                            \
+        if (edge == 1) GEMM_REGS(TA_, TB_, 1);      \
+        else if (edge == 2) GEMM_REGS(TA_, TB_, 2); \
+        else if constexpr (WHOLE) GEMM_REGS(TA_, TB_, 0); \
+    } while (0)
+    if (p.ta && p.tb) GEMM_REGS_E(true, true);
+    else if (p.ta) GEMM_REGS_E(true, false);
+    else if (p.tb) GEMM_REGS_E(false, true);
+    else GEMM_REGS_E(false, false);
+#undef GEMM_REGS_E
 #undef GEMM_REGS
     return hipGetLastError();
 }
@@ -362,9 +429,9 @@ const ConfigEntry kRegsConfigs[] = {
     // groups of one wavefront (two per SIMD), 32 x 64 and 128 x 64 tiles,
     // D from 2 to 6 (within 2%), and loads spread between the MFMAs into a
     // third register set (2 to 3% slower).
-    {"mfmag_64x64x64_w1x1_k4_d3", launch_regs<64, 64, 1, 1, 4, 3, 1, true, true, 8>, 0},
+    {"mfmag_64x64x64_w1x1_k4_d3", launch_regs<64, 64, 1, 1, 4, 3, 1, true, true, 8>, kCapTransposed},
     // 128 x 128: 256 accumulator floats per lane
-    {"mfmag_128x128x64_w1x1_k4_d2", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8>, 0},
+    {"mfmag_128x128x64_w1x1_k4_d2", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8>, kCapTransposed},
 };
 
 }  // namespace

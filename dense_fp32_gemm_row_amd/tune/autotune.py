@@ -23,7 +23,8 @@ levels per candidate is set in the table (at least its occupancy, and two
 for a candidate that fits one tile per CU, since one tile per CU runs
 faster per CU than several in turn).  `unaligned` is the median ratio of
 the rate on shapes whose rows are not 16-byte aligned to the aligned rate
-at the same level.
+at the same level, and `trans` the same ratio for operands stored transposed
+(A as K x M and / or B as N x K) on a few squares.
 
     python -m dense_fp32_gemm_row_amd.tune.autotune --out tuned.json --calibrate
 
@@ -79,6 +80,10 @@ CAL_UNALIGNED = [(1000, 1023, 7777), (2049, 2049, 2049), (3001, 3001, 3001), (40
 # short K and many output tiles: where a tile's fixed cost (its prologue, and
 # the stores of C that no other workgroup's math hides) shows
 CAL_SHORTK = [(8192, 8192, 64), (8192, 8192, 128), (16384, 16384, 128), (16384, 16384, 256)]
+# transposed operands (A stored K x M and/or B stored N x K) on shapes of
+# CAL_SHAPES, for the candidates that take them
+CAL_TRANS = [(2048, 2048, 8192), (4096, 4096, 4096), (6144, 6144, 6144), (8192, 8192, 8192)]
+TRANS_OPS = ("NT", "TN", "TT")
 
 
 def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dict:
@@ -105,6 +110,29 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
             print(json.dumps({"calibrate": cfg, "M": M, "N": N, "K": K,
                               "median_ms": round(times[(cfg, M, N, K)], 5)}), flush=True)
         del dA, dB, dC
+        torch.cuda.empty_cache()
+    for M, N, K in CAL_TRANS:
+        g = torch.Generator(device="cuda").manual_seed(0)
+        for ops in TRANS_OPS:
+            dA = (torch.rand((K, M), device="cuda", generator=g).t() if ops[0] == "T"
+                  else torch.rand((M, K), device="cuda", generator=g))
+            dB = (torch.rand((N, K), device="cuda", generator=g).t() if ops[1] == "T"
+                  else torch.rand((K, N), device="cuda", generator=g))
+            dC = torch.empty((M, N), device="cuda")
+            for cand in model["candidates"]:
+                cfg = cand["config"]
+
+                def call(cfg=cfg):
+                    binding.gemm(dA, dB, dC, variant="mfma", config=cfg)
+
+                try:
+                    call()
+                except binding.GemmError:  # the configuration takes row-major operands only
+                    continue
+                times[(cfg, ops, M, N, K)] = time_fn(call, budget_ms, blocker)
+                print(json.dumps({"calibrate": cfg, "ops": ops, "M": M, "N": N, "K": K,
+                                  "median_ms": round(times[(cfg, ops, M, N, K)], 5)}), flush=True)
+            del dA, dB, dC
         torch.cuda.empty_cache()
     out = {"cus": cus, "candidates": []}
     for cand in model["candidates"]:
@@ -143,9 +171,19 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
             n, level = share(M, N)
             ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
             ratios.append(2.0 * bm * bn * (K + k0) * n / (ms * 1e-3) / 1e9 / rates[level - 1])
+        # transposed operands: the median ratio of the rate to the row-major
+        # rate at the same level (1 for candidates that do not take them)
+        tratios = []
+        for M, N, K in CAL_TRANS:
+            n, level = share(M, N)
+            for ops in TRANS_OPS:
+                if (cfg, ops, M, N, K) in times:
+                    ms = max(times[(cfg, ops, M, N, K)] - floor, 1e-6)
+                    tratios.append(2.0 * bm * bn * (K + k0) * n / (ms * 1e-3) / 1e9 / rates[level - 1])
         out["candidates"].append({**cand, "gflops_per_cu": [round(r, 1) for r in rates],
                                   "k0": round(k0, 1),
-                                  "unaligned": round(min(1.0, statistics.median(ratios)), 3)})
+                                  "unaligned": round(min(1.0, statistics.median(ratios)), 3),
+                                  "trans": round(statistics.median(tratios), 3) if tratios else 1.0})
     return out
 
 

@@ -51,6 +51,7 @@ def render(table: dict) -> str:
         "    float gflops_per_cu[4];",
         "    float unaligned;",
         "    float k0;",
+        "    float trans;  // rate factor with a transposed operand",
         "};",
         f'constexpr int kModelCUs = {int(table["model"]["cus"])};',
         "constexpr ModelCandidate kModel[] = {",
@@ -61,7 +62,8 @@ def render(table: dict) -> str:
             raise ValueError(f"{c['config']}: 1 to 4 rates")
         padded = ", ".join(f"{x:.1f}f" for x in rates + [rates[-1]] * (4 - len(rates)))
         lines.append(f'    {{"{c["config"]}", {int(c["bm"])}, {int(c["bn"])}, {len(rates)}, '
-                     f'{{{padded}}}, {float(c["unaligned"]):.3f}f, {float(c.get("k0", 0.0)):.1f}f}},')
+                     f'{{{padded}}}, {float(c["unaligned"]):.3f}f, {float(c.get("k0", 0.0)):.1f}f, '
+                     f'{float(c.get("trans", 1.0)):.3f}f}},')
     lines += [
         "};",
         "}  // namespace gemm_f32_impl",

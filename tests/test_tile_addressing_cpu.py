@@ -314,13 +314,17 @@ def test_splitk_model_sees_the_unchecked_overrun():
 
 
 # --------------------------------------------------------------------------
-# Operands loaded straight into registers (csrc/mfma_regs.hip): every lane
-# loads, per chunk of 16 k, A[row][16 c + 4 g .. + 3] for each of its row
-# blocks and B[16 c + 4 g + s][col .. col + FN - 1] for s = 0..3, with rows
-# past M clamped to M - 1 and column groups that start past N clamped to the
-# group holding column N - 1.  The loop runs chunks 0 .. (K - 1) / 16 - 1
-# (whole chunks only, with edges), the chunk of the last k is a checked tail,
-# and shapes with N < FN - 1 check every element.
+# Operands loaded straight into registers (csrc/mfma_regs.hip).  Per chunk c
+# of 16 k, lane (g, i) feeds instruction s with k = 16 c + 4 g + s.  Row
+# flavour (A as stored, B transposed): block f of the operand is row r_f and
+# the lane loads its 4 values of k as one run.  K-major flavour (B as stored,
+# A transposed): the lane's F blocks are the F adjacent rows starting at
+# base + F i and it loads them as one run per k row.  Rows past the extent
+# load the last row (row flavour); a k-major group that starts past it loads
+# the group holding the last row.  The loop runs chunks 0 .. (K - 1) / 16 - 1
+# (with edges), the chunk of the last k is a checked tail split over the
+# groups by instruction, and shapes where a k-major group could pass the
+# operand's storage (extent < F - 1) check every element.
 # --------------------------------------------------------------------------
 
 # (BM, BN, WM, WN, KG, whole): the register-direct configurations and other
@@ -329,23 +333,37 @@ def test_splitk_model_sees_the_unchecked_overrun():
 REGS_TILES = [(64, 64, 1, 1, 4, True), (128, 128, 1, 1, 4, False), (128, 64, 1, 1, 4, True),
               (64, 64, 4, 1, 4, True), (64, 64, 2, 2, 4, True), (32, 64, 1, 1, 8, True),
               (64, 64, 1, 1, 2, True), (64, 64, 1, 1, 1, True)]
-REGS_SHAPES = [  # M, N, K, lda pad, ldb pad
+REGS_SHAPES = [  # M, N, K, ld pad of A, ld pad of B
     (257, 259, 97, 0, 0), (64, 64, 64, 0, 0), (128, 64, 48, 0, 0), (65, 67, 17, 0, 0),
     (1, 1, 1, 0, 0), (3, 2, 5, 0, 0), (70, 3, 33, 2, 0), (5, 2, 100, 0, 0), (64, 1, 16, 0, 0),
     (33, 7, 16, 0, 0), (130, 129, 31, 1, 3), (1, 4, 32, 0, 0), (17, 5, 15, 0, 0), (40, 6, 50, 0, 0),
-    (129, 8, 20, 0, 0), (256, 256, 64, 0, 0)]
+    (129, 8, 20, 0, 0), (256, 256, 64, 0, 0), (6, 130, 40, 0, 1)]
 
 
-def regs_model(BM, BN, WM, WN, KG, M, N, K, lda, ldb, whole_ok=True):
+def regs_operand(kmajor, F, il, base, i, R, clamp):
+    """Rows of the lane's F blocks, and the rows its loads use (clamped)."""
+    rows = [base + F * i + f if il else base + 16 * f + i for f in range(F)]
+    if kmajor:
+        r0 = rows[0]
+        rc0 = ((R - 1) // F) * F if clamp and r0 > R - 1 else r0
+        return rows, [rc0 + f for f in range(F)]
+    return rows, [min(r, R - 1) if clamp else r for r in rows]
+
+
+def regs_model(BM, BN, WM, WN, KG, M, N, K, lda, ldb, whole_ok=True, ta=False, tb=False):
     """Every load of the register-direct kernel as (first float, length), the
-    element each in-range operand position receives, and the k values each
-    tile's k-groups cover, restated from the kernel."""
+    positions that would receive another element than their own, and the k
+    values each tile's k-groups cover, restated from the kernel."""
     WTM, WTN = BM // WM, BN // WN
     FM, FN = WTM // 16, WTN // 16
     whole = M % BM == 0 and N % BN == 0 and K % 16 == 0 and whole_ok
-    edge = 0 if whole else (1 if N >= FN - 1 else 2)
+    clamp_ok = (not ta or M >= FM - 1) and (tb or N >= FN - 1)
+    edge = 0 if whole else (1 if clamp_ok else 2)
     nloop = K // 16 if edge == 0 else ((K - 1) // 16 if edge == 1 else 0)
     nchunks = nloop if edge == 0 else (K + 15) // 16
+    # operand: (kmajor, F, interleaved, extent, ld, element address of (row, k))
+    opa = (ta, FM, ta, M, lda, (lambda r, k: k * lda + r) if ta else (lambda r, k: r * lda + k))
+    opb = (not tb, FN, True, N, ldb, (lambda r, k: r * ldb + k) if tb else (lambda r, k: k * ldb + r))
     loads = {"A": [], "B": []}
     wrong = []
     covered = {}
@@ -359,66 +377,58 @@ def regs_model(BM, BN, WM, WN, KG, M, N, K, lda, ldb, whole_ok=True):
                     mine = [(c, True) for c in range(nchunks) if c % KG == kg]
                     ks += [16 * c + q for c, _ in mine for q in range(16) if 16 * c + q < K]
                 elif nchunks > nloop and kg < min(KG, 4):
-                    # the tail: instruction s (k = 16 c + 4 g + s) goes to group s mod min(KG, 4)
                     ts = min(KG, 4)
                     mine.append((nloop, True))
                     ks += [16 * nloop + 4 * gg + s for gg in range(4) for s in range(4)
                            if s % ts == kg and 16 * nloop + 4 * gg + s < K]
                 for wm in range(WM):
                     for wn in range(WN):
-                        for g in range(4):
-                            for i in range(16):
-                                for c, checked in mine:
-                                    for f in range(FM):
-                                        r = m0 + wm * WTM + 16 * f + i
-                                        rc = min(r, M - 1) if edge else r
-                                        for e in range(4):
-                                            k = 16 * c + 4 * g + e
-                                            if checked and k >= K:
-                                                continue  # zero fill
-                                            addr = rc * lda + k
-                                            if r < M and addr != r * lda + k:
-                                                wrong.append(("A", r, k, addr))
-                                        if checked:
-                                            loads["A"] += [(rc * lda + 16 * c + 4 * g + e, 1) for e in range(4)
-                                                           if 16 * c + 4 * g + e < K]
-                                        else:
-                                            loads["A"].append((rc * lda + 16 * c + 4 * g, 4))
-                                    bcol = n0 + wn * WTN + FN * i
-                                    bcol_c = ((N - 1) // FN) * FN if edge and bcol > N - 1 else bcol
-                                    for s in range(4):
-                                        k = 16 * c + 4 * g + s
-                                        if checked:
-                                            for j in range(FN):
-                                                if k < K and bcol + j < N:
-                                                    loads["B"].append((k * ldb + bcol + j, 1))
-                                            continue
-                                        loads["B"].append((k * ldb + bcol_c, FN))
-                                        for j in range(FN):
-                                            if bcol + j < N and k * ldb + bcol_c + j != k * ldb + bcol + j:
-                                                wrong.append(("B", k, bcol + j))
+                        for name, (kmajor, F, il, R, ld, addr), base in (
+                                ("A", opa, m0 + wm * WTM), ("B", opb, n0 + wn * WTN)):
+                            for g in range(4):
+                                for i in range(16):
+                                    rows, used = regs_operand(kmajor, F, il, base, i, R, edge != 0)
+                                    for c, checked in mine:
+                                        for s in range(4):
+                                            k = 16 * c + 4 * g + s
+                                            for r, ru in zip(rows, used):
+                                                if checked:
+                                                    if k < K and r < R:
+                                                        loads[name].append((addr(r, k), 1))
+                                                    continue  # else zero
+                                                if r < R and addr(ru, k) != addr(r, k):
+                                                    wrong.append((name, r, k))
+                                            if not checked:
+                                                if kmajor:
+                                                    loads[name].append((addr(used[0], k), F))
+                                                elif s == 0:
+                                                    loads[name] += [(addr(ru, 16 * c + 4 * g), 4) for ru in used]
             covered[(m0, n0)] = sorted(ks)
-    return loads, wrong, covered
+    ends = {"A": (K - 1) * lda + M if ta else (M - 1) * lda + K,
+            "B": (N - 1) * ldb + K if tb else (K - 1) * ldb + N}
+    return loads, wrong, covered, ends
 
 
+@pytest.mark.parametrize("ops", ["NN", "NT", "TN", "TT"])
 @pytest.mark.parametrize("tile", REGS_TILES, ids=lambda t: "x".join(map(str, t)))
-def test_register_direct_loads_inside_and_complete(tile):
+def test_register_direct_loads_inside_and_complete(tile, ops):
     """Every load of the register-direct kernel lies inside the operands'
-    storage ((rows - 1) ld + cols floats), every position that feeds a
-    stored output receives its own element, and each tile's k-groups cover
-    every k < K exactly once (the tail's positions past K are zero on both
-    sides)."""
+    storage ((rows - 1) ld + cols floats, as stored), every position that
+    feeds a stored output receives its own element, and each tile's k-groups
+    cover every k < K exactly once (the tail's positions past K are zero)."""
     BM, BN, WM, WN, KG, whole_ok = tile
+    ta, tb = ops[0] == "T", ops[1] == "T"
     for M, N, K, pa, pb in REGS_SHAPES:
-        lda, ldb = K + pa, N + pb
-        loads, wrong, covered = regs_model(BM, BN, WM, WN, KG, M, N, K, lda, ldb, whole_ok)
-        ends = {"A": (M - 1) * lda + K, "B": (K - 1) * ldb + N}
+        lda = (M if ta else K) + pa
+        ldb = (K if tb else N) + pb
+        loads, wrong, covered, ends = regs_model(BM, BN, WM, WN, KG, M, N, K, lda, ldb, whole_ok,
+                                                 ta, tb)
         for op in "AB":
             for first, length in loads[op]:
-                assert 0 <= first and first + length <= ends[op], (op, tile, (M, N, K), first, length)
-        assert not wrong, (tile, (M, N, K), wrong[:3])
+                assert 0 <= first and first + length <= ends[op], (op, ops, tile, (M, N, K), first, length)
+        assert not wrong, (ops, tile, (M, N, K), wrong[:3])
         for key, ks in covered.items():
-            assert ks == list(range(K)), (tile, (M, N, K), key)
+            assert ks == list(range(K)), (ops, tile, (M, N, K), key)
 
 
 def test_register_direct_model_sees_a_loop_over_the_last_chunk():
