@@ -382,11 +382,193 @@ void gemm_mfma_regs_kernel(
     }
 }
 
+// Barrier between the LDS writes and reads of the k-group sum that leaves
+// global loads in flight: each wavefront waits for its own LDS accesses
+// only (a __syncthreads would also wait for every outstanding global load,
+// here the next tile's first chunks).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    // s_waitcnt: lgkmcnt 0; vmcnt 63 (bits 3:0 and 15:14) and expcnt 7 not waited on
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (3 << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Persistent form of the register-direct tile for whole tiles and K a
+// multiple of 16 KG D: one workgroup per CU walks the tiles blockIdx.x +
+// j gridDim.x (through the same XCD-aware, grouped order as the one-launch
+// grid), and the last D chunks of a tile load the next tile's first D
+// chunks into their register sets.  The next tile's loads are thus in
+// flight during this tile's k-group sum and stores, and no workgroup start
+// or first-load latency sits between two tiles of a CU.
+template <int BM, int BN, int KG, int D, bool TA, bool TB>
+__global__ __launch_bounds__(64 * KG) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_mfma_regs_persistent_kernel(
+    int M, int N, int K, const float *__restrict__ A, int64_t lda,
+    const float *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc,
+    int tiles_m, int tiles_n, int group_m, BatchArgs bt) {
+    constexpr int FM = BM / 16, FN = BN / 16;
+    constexpr int CK = 16;
+    static_assert(BM % 16 == 0 && (FN == 1 || FN == 2 || FN % 4 == 0), "16 x 16 blocks");
+    static_assert(KG > 1 && D >= 2, "k-groups and chunks in flight");
+    constexpr int RP = regs_pass_rows(FM, FN, KG, 1);
+    static_assert(RP > 0, "LDS room for the k-group sum");
+    __shared__ __align__(16) float red[KG * RP * 64 * FN];
+    using OpA = RegOperand<TA, FM, TA>;
+    using OpB = RegOperand<!TB, FN, true>;
+
+    const int total = tiles_m * tiles_n * bt.count;
+    const int G = static_cast<int>(gridDim.x);
+    const int lane = threadIdx.x & 63;
+    const int kg = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int g = lane / 16, i = lane % 16;
+    const int ng = K / CK / KG;  // chunks of each group: kg, kg + KG, ...
+    auto chunk_of = [&](int t) { return kg + KG * t; };
+
+    // operands, C and origin of logical tile `logical`
+    auto tile_at = [&](int logical, OpA &oa, OpB &ob, float *&c, int &m0, int &n0) {
+        const float *a = A, *b = B;
+        c = C;
+        int k = K;
+        const int t = batch_select(logical, tiles_m * tiles_n, bt, a, b, c, k);
+        int tm, tn;
+        grouped_tile(t, tiles_m, tiles_n, group_m, tm, tn);
+        m0 = tm * BM, n0 = tn * BN;
+        oa.init(a, lda, M, m0, g, i, false);
+        ob.init(b, ldb, N, n0, g, i, false);
+    };
+
+    int logical = xcd_remap(static_cast<int>(blockIdx.x), G);
+    if (logical >= total) return;
+    OpA oa, oa_n;
+    OpB ob, ob_n;
+    float *c, *c_n;
+    int m0, n0, m0_n, n0_n;
+    tile_at(logical, oa, ob, c, m0, n0);
+
+    float ra[D][FM][4];
+    float rb[D][FN][4];
+    floatx4 acc[FM][FN];
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[f][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    auto mma = [&](const float (&xa)[FM][4], const float (&xb)[FN][4]) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[f][s], xb[j][s], acc[f][j], 0, 0, 0);
+    };
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+        oa.load(ra[u], chunk_of(u));
+        ob.load(rb[u], chunk_of(u));
+    }
+    const bool vec_c = ((reinterpret_cast<uintptr_t>(C) | static_cast<uintptr_t>(ldc * 4)) &
+                        (4 * (FN < 4 ? FN : 4) - 1)) == 0;
+    auto part = [&](int h, int q) { return red + (h * RP + q) * 64 * FN + lane * FN; };
+
+    for (;;) {
+        const int next = logical + G;
+        const bool has_next = next < total;
+        int t = 0;
+        for (; t + D < ng; t += D) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) {
+                mma(ra[u], rb[u]);
+                __builtin_amdgcn_sched_barrier(0);
+                oa.load(ra[u], chunk_of(t + u + D));
+                ob.load(rb[u], chunk_of(t + u + D));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // the last D chunks; their sets take the next tile's first D chunks
+        // (the last tile reloads its own, in bounds and never used)
+        if (has_next) {
+            tile_at(next, oa_n, ob_n, c_n, m0_n, n0_n);
+        } else {
+            oa_n = oa, ob_n = ob, c_n = c, m0_n = m0, n0_n = n0;
+        }
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            mma(ra[u], rb[u]);
+            __builtin_amdgcn_sched_barrier(0);
+            oa_n.load(ra[u], chunk_of(u));
+            ob_n.load(rb[u], chunk_of(u));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // the k-group sum in group order and the stores, as in the
+        // one-launch kernel (register r of block (f, j): row 16 f + 4 g + r,
+        // or FM (4 g + r) + f with A transposed; column FN i + j)
+        const int bcol = n0 + FN * i;
+#pragma unroll
+        for (int pass = 0; pass < FM * 4 / RP; ++pass) {
+            lds_barrier();  // the previous reads of the LDS slots are done
+#pragma unroll
+            for (int q = 0; q < RP; ++q) {
+                const int fr = pass * RP + q;
+                float v[FN];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) v[j] = acc[fr / 4][j][fr % 4];
+                store_run<FN>(part(kg, q), v);
+            }
+            lds_barrier();
+#pragma unroll
+            for (int qq = 0; qq < RP / KG; ++qq) {
+                const int q = kg + qq * KG;
+                const int fr = pass * RP + q, f = fr / 4, r = fr % 4;
+                float v[FN];
+#pragma unroll
+                for (int h = 0; h < KG; ++h) {
+                    float x[FN];
+                    const float *src = part(h, q);
+                    if constexpr (FN >= 4) {
+#pragma unroll
+                        for (int p = 0; p < FN; p += 4) {
+                            const floatx4 t4 = *reinterpret_cast<const floatx4 *>(src + p);
+                            x[p] = t4[0], x[p + 1] = t4[1], x[p + 2] = t4[2], x[p + 3] = t4[3];
+                        }
+                    } else if constexpr (FN == 2) {
+                        const floatx2 t2 = *reinterpret_cast<const floatx2 *>(src);
+                        x[0] = t2[0], x[1] = t2[1];
+                    } else {
+                        x[0] = src[0];
+                    }
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) v[j] = h == 0 ? x[j] : v[j] + x[j];
+                }
+                const int gm = m0 + (TA ? FM * (4 * g + r) + f : 16 * f + 4 * g + r);
+                float *row = c + static_cast<int64_t>(gm) * ldc + bcol;
+                if (vec_c) {
+                    store_run<FN>(row, v);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) row[j] = v[j];
+                }
+            }
+        }
+        if (!has_next) break;
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[f][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        logical = next;
+        oa = oa_n, ob = ob_n, c = c_n, m0 = m0_n, n0 = n0_n;
+    }
+}
+
 // Launch of one configuration.
 // WHOLE: compile the unchecked kernel for whole tiles and chunks (the
 // 128 x 128 tiles spill registers in it and run the clamped one instead,
 // whose last chunk is then a tail).
-template <int BM, int BN, int WM, int WN, int KG, int D, int OCC, bool ET, bool WHOLE, int GROUP_M>
+// PERSIST: the persistent kernel where the shape allows it (WM = WN = 1).
+template <int BM, int BN, int WM, int WN, int KG, int D, int OCC, bool ET, bool WHOLE, int GROUP_M,
+          bool PERSIST = false>
 hipError_t launch_regs(const Problem &p, hipStream_t stream) {
     constexpr int NT = 64 * WM * WN * KG;
     constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
@@ -400,6 +582,28 @@ hipError_t launch_regs(const Problem &p, hipStream_t stream) {
     const bool clamp_ok = (!p.ta || p.M >= FM - 1) && (p.tb || p.N >= FN - 1);
     const int edge = whole && WHOLE ? 0 : clamp_ok ? 1 : 2;
     const dim3 gd(static_cast<unsigned>(grid)), bd(NT);
+    if constexpr (PERSIST) {
+        // whole tiles, K whole rounds of D chunks per group, no split-K
+        // slices (every tile the same K), B as stored: one workgroup per CU
+        // walks the tiles.  (With B transposed the persistent kernel ran 6
+        // to 9% slower than one launch per tile at 8192^3, 4096^3 and the
+        // FFN shape, and 1% faster with B as stored.)
+        if (p.M % BM == 0 && p.N % BN == 0 && p.K % (16 * KG * D) == 0 && p.ksplit == 0 && !p.tb) {
+            int dev = 0, cus = 0;
+            hipError_t e = hipGetDevice(&dev);
+            if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess) return e;
+            const unsigned wgs = static_cast<unsigned>(grid < cus ? grid : cus);
+#define GEMM_REGS_P(TA_, TB_)                                                                        \
+    hipLaunchKernelGGL((gemm_mfma_regs_persistent_kernel<BM, BN, KG, D, TA_, TB_>), dim3(wgs), bd, 0, \
+                       stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,  \
+                       GROUP_M, batch_of(p))
+            if (p.ta) GEMM_REGS_P(true, false);
+            else GEMM_REGS_P(false, false);
+#undef GEMM_REGS_P
+            return hipGetLastError();
+        }
+    }
 #define GEMM_REGS(TA_, TB_, E)                                                                      \
     hipLaunchKernelGGL((gemm_mfma_regs_kernel<BM, BN, WM, WN, KG, D, OCC, ET, TA_, TB_, E>), gd, bd, \
                        0, stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m,       \
@@ -432,6 +636,9 @@ const ConfigEntry kRegsConfigs[] = {
     {"mfmag_64x64x64_w1x1_k4_d3", launch_regs<64, 64, 1, 1, 4, 3, 1, true, true, 8>, kCapTransposed},
     // 128 x 128: 256 accumulator floats per lane
     {"mfmag_128x128x64_w1x1_k4_d2", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8>, kCapTransposed},
+    // persistent where the shape allows (one workgroup per CU walks its
+    // tiles; for the 64 x 64 tile it gained nothing)
+    {"mfmag_128x128x64_w1x1_k4_d2_p", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8, true>, kCapTransposed},
 };
 
 }  // namespace

@@ -571,7 +571,8 @@ TRANS_CAPABLE = ["mfma2d_256x256x32_w4x4_swz", "mfma3d_256x128x32_w4x2_swz",
                  "mfma3d_64x64x64_w2x2_k4_swz", "mfma4d_64x64x64_w2x2_k4_swz",
                  "mfma3_256x256x16_w4x4_swz_g4_il", "mfma2_64x64x64_w2x2_k4_swz",
                  "mfma2d_128x128x32_w2x2_swz_il", "mfma2r_64x64x64_w2x2_k4_swz",
-                 "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2"] + [
+                 "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2",
+                 "mfmag_128x128x64_w1x1_k4_d2_p"] + [
     n for n in CONFIG_IDS if "_m16" in n]  # every 16x16x4 configuration takes them
 TRANS_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in TRANS_CAPABLE]
@@ -710,6 +711,47 @@ def test_splitk_slices_not_whole_k_steps(kernel, lda_pad):
     out = torch.full((M, N), float("nan"), device="cuda:0")
     b.gemm_splitk(dA, to_dev(B), 4, out, variant=v, config=c)
     assert_exact(to_host(out), oracle.gemm(A, B), f"{name} lda pad {lda_pad}")
+
+
+PERSISTENT = [(3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n.startswith("mfmag") and n.endswith("_p")]
+PERSISTENT_SHAPES = [(256, 256, 384), (2048, 2304, 384), (1280, 4096, 768)]
+
+
+@pytest.mark.parametrize("kernel", PERSISTENT, ids=[k[2] for k in PERSISTENT])
+@pytest.mark.parametrize("ops", OPS)
+def test_persistent_register_direct(kernel, ops):
+    """The persistent register-direct kernel runs whole tiles with K a
+    multiple of 128 (16 k x 4 groups x 2 chunks in flight) and B as stored:
+    one workgroup per CU walks one to five tiles, and the last chunks of each
+    tile load the next tile's first ones.  Fewer tiles than CUs, and rounds
+    with part of the workgroups idle; the forms with B transposed take the
+    one-launch kernel.  Exact on integers."""
+    import torch
+
+    v, c, name = kernel
+    for M, N, K in PERSISTENT_SHAPES:
+        log(f"persistent {ops} {M}x{N}x{K} on {name}")
+        A, B = make_inputs(M, N, K, "int4", seed=71)
+        out = torch.full((M, N), float("nan"), device="cuda:0")
+        b.gemm(_stored(A, ops[0]), _stored(B, ops[1]), out, variant=v, config=c)
+        assert_exact(to_host(out), oracle.gemm(A, B), f"{name} {ops} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("kernel", PERSISTENT, ids=[k[2] for k in PERSISTENT])
+def test_persistent_register_direct_batched(kernel):
+    """Three products of 512 x 640 x 384 in one persistent launch (tiles of
+    all products on one walk), C rows padded, B shared (stride 0)."""
+    M, N, K, nb = 512, 640, 384, 3
+    rng = np.random.default_rng(72)
+    lda, ldb, ldc = K, N, N + 3
+    sa, sb, sc = M * lda + 5, 0, M * ldc + 7
+    A3, As = _layout(rng, nb, M, K, lda, sa, "int4")
+    B3, Bs = _layout(rng, 1, K, N, ldb, 0, "int4")
+    log(f"persistent batched {nb} x {M}x{N}x{K} on {kernel[2]}")
+    Cflat = _run_batched(A3, B3, M, N, K, nb, sa, sb, sc, lda, ldb, ldc, kernel)
+    for q in range(nb):
+        got = np.lib.stride_tricks.as_strided(Cflat[q * sc:], shape=(M, N), strides=(4 * ldc, 4))
+        assert_exact(np.ascontiguousarray(got), oracle.gemm(As[q], Bs[0]), f"{kernel[2]} product {q}")
 
 
 def test_splitk_deep_k_full():

@@ -448,3 +448,28 @@ def test_register_direct_model_sees_a_loop_over_the_last_chunk():
             k = K - 1  # the last k row, loaded unchecked
             overrun |= k * ldb + bcol_c + FN > b_end
     assert overrun
+
+
+def xcd_remap(bid, n):
+    """Restated from csrc/gemm_internal.h: hardware workgroup id -> logical
+    id, consecutive logical ids on one XCD (workgroup b runs on XCD b % 8)."""
+    q, r = divmod(n, 8)
+    xcd, local = bid % 8, bid // 8
+    return xcd * (q + 1) + local if xcd < r else r * (q + 1) + (xcd - r) * q + local
+
+
+@pytest.mark.parametrize("grid", [1, 7, 8, 100, 255, 256])
+def test_persistent_walk_covers_every_tile_once(grid):
+    """The persistent register-direct kernel: workgroup b of `grid` takes
+    logical tiles xcd_remap(b, grid) + j * grid while they are below the
+    tile count; every tile is taken by exactly one workgroup, for tile counts
+    below, at and above the grid."""
+    for total in sorted({grid, max(1, grid - 3), grid + 1, 2 * grid, 5 * grid + 3}):
+        g = min(grid, total)  # the launcher never starts more workgroups than tiles
+        seen = []
+        for b in range(g):
+            logical = xcd_remap(b, g)
+            while logical < total:
+                seen.append(logical)
+                logical += g
+        assert sorted(seen) == list(range(total)), (grid, total)
