@@ -250,19 +250,30 @@ const ModelIds &model_ids() {
     }();
     return ids;
 }
-bool usable(int i, bool trans) {
+// What a product asks of a candidate besides its shape: a transposed
+// operand (the candidate must take them), B transposed, split-K slices.
+constexpr unsigned kOpsTrans = 1u, kOpsBTrans = 2u, kOpsSplitK = 4u;
+unsigned ops_of(bool ta, bool tb) { return (ta || tb ? kOpsTrans : 0u) | (tb ? kOpsBTrans : 0u); }
+
+// A candidate with whole_k > 0 (a persistent kernel) is rated only for the
+// products it runs in that form: whole tiles, K a multiple of whole_k, B as
+// stored, no split-K slices.
+bool usable(int i, unsigned ops, int64_t M, int64_t N, int64_t K) {
     const ModelIds &ids = model_ids();
-    return ids.id[i] >= 0 && (!trans || ids.trans[i]);
+    if (ids.id[i] < 0 || ((ops & kOpsTrans) && !ids.trans[i])) return false;
+    const ModelCandidate &m = kModel[i];
+    return m.whole_k == 0 || (!(ops & (kOpsBTrans | kOpsSplitK)) && M % m.bm == 0 &&
+                              N % m.bn == 0 && K % m.whole_k == 0);
 }
 
 // The model's fastest candidate; returns its predicted microseconds.
-double best_candidate(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans, bool aligned,
+double best_candidate(int64_t batch, int64_t M, int64_t N, int64_t K, unsigned ops, bool aligned,
                       int *config) {
     double best_t = 0.0;
     *config = -1;
     for (int i = 0; i < kModelSize; ++i) {
-        if (!usable(i, trans)) continue;
-        const double t = model_us(kModel[i], batch, M, N, K, aligned, trans);
+        if (!usable(i, ops, M, N, K)) continue;
+        const double t = model_us(kModel[i], batch, M, N, K, aligned, ops & kOpsTrans);
         if (*config < 0 || t < best_t) *config = model_ids().id[i], best_t = t;
     }
     if (*config < 0) *config = 0;
@@ -284,10 +295,11 @@ bool exact_entry(int64_t M, int64_t N, int64_t K, int *variant, int *config) {
 }
 
 void select_config(int64_t batch, int64_t M, int64_t N, int64_t K, int *variant, int *config,
-                   bool trans = false, bool aligned = true) {
-    if (batch == 1 && !trans && exact_entry(M, N, K, variant, config)) return;
+                   unsigned ops = 0, bool aligned = true) {
+    if (batch == 1 && !(ops & (kOpsTrans | kOpsSplitK)) && exact_entry(M, N, K, variant, config))
+        return;
     *variant = GEMM_F32_VARIANT_MFMA;
-    best_candidate(batch, M, N, K, trans, aligned, config);
+    best_candidate(batch, M, N, K, ops, aligned, config);
 }
 
 // How gemm_f32 runs one product, or every product of a strided batch alike:
@@ -313,20 +325,20 @@ constexpr double kSplitGain = 0.02;
 constexpr int64_t kSplitWaves = 16;
 constexpr double kSplitMinUs = 100.0;
 
-Plan search_plan(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
+Plan search_plan(int64_t batch, int64_t M, int64_t N, int64_t K, unsigned ops, bool aligned) {
     Plan plan{1, 0, 0, {GEMM_F32_VARIANT_MFMA, 0}, {0, 0}};
     if (M <= 0 || N <= 0 || K <= 0 || batch <= 0) {  // nothing to split
-        select_config(batch > 0 ? batch : 1, M, N, K, &plan.variant[0], &plan.config[0], trans,
+        select_config(batch > 0 ? batch : 1, M, N, K, &plan.variant[0], &plan.config[0], ops,
                       aligned);
         return plan;
     }
-    if (batch == 1 && !trans && exact_entry(M, N, K, &plan.variant[0], &plan.config[0]))
+    if (batch == 1 && !(ops & kOpsTrans) && exact_entry(M, N, K, &plan.variant[0], &plan.config[0]))
         return plan;
-    const double t1 = best_candidate(batch, M, N, K, trans, aligned, &plan.config[0]);
+    const double t1 = best_candidate(batch, M, N, K, ops, aligned, &plan.config[0]);
     if (t1 < kSplitMinUs) return plan;
     double best_t = t1 * (1.0 - kSplitGain);
     for (int i = 0; i < kModelSize; ++i) {
-        if (!usable(i, trans)) continue;
+        if (!usable(i, ops, 0, 0, 0)) continue;  // operand forms (the shape per part below)
         const ModelCandidate &m = kModel[i];
         const int id = model_ids().id[i];
         for (int axis = 0; axis < 2; ++axis) {
@@ -340,9 +352,10 @@ Plan search_plan(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans, boo
                 if (first >= along) break;
                 const int64_t m1 = axis == 0 ? first : M, n1 = axis == 0 ? N : first;
                 const int64_t m2 = axis == 0 ? M - first : M, n2 = axis == 0 ? N : N - first;
+                if (!usable(i, ops, m1, n1, K)) continue;
                 int c2 = -1;
-                const double t = model_us(m, batch, m1, n1, K, aligned, trans) +
-                                 best_candidate(batch, m2, n2, K, trans, aligned, &c2) + kLaunchUs;
+                const double t = model_us(m, batch, m1, n1, K, aligned, ops & kOpsTrans) +
+                                 best_candidate(batch, m2, n2, K, ops, aligned, &c2) + kLaunchUs;
                 // one configuration in two launches only looks faster: each
                 // launch would count at the one-tile-per-CU rate, but the
                 // second still waits for the first and starts from cold
@@ -360,18 +373,19 @@ Plan search_plan(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans, boo
 
 // search_plan with the last result of the calling thread kept: a loop over
 // one shape searches once.
-Plan plan_product(int64_t batch, int64_t M, int64_t N, int64_t K, bool trans, bool aligned) {
+Plan plan_product(int64_t batch, int64_t M, int64_t N, int64_t K, unsigned ops, bool aligned) {
     struct Key {
         int64_t batch, M, N, K;
-        bool trans, aligned;
+        unsigned ops;
+        bool aligned;
     };
-    thread_local Key last{-1, -1, -1, -1, false, false};
+    thread_local Key last{-1, -1, -1, -1, 0u, false};
     thread_local Plan last_plan{};
-    if (batch == last.batch && M == last.M && N == last.N && K == last.K && trans == last.trans &&
+    if (batch == last.batch && M == last.M && N == last.N && K == last.K && ops == last.ops &&
         aligned == last.aligned)
         return last_plan;
-    last_plan = search_plan(batch, M, N, K, trans, aligned);
-    last = Key{batch, M, N, K, trans, aligned};
+    last_plan = search_plan(batch, M, N, K, ops, aligned);
+    last = Key{batch, M, N, K, ops, aligned};
     return last_plan;
 }
 
@@ -400,7 +414,7 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
     if (variant == -1) {  // the library's choice: the products may be split in two launches
         int rc = validate_sizes(M, N, K, lda, ldb, ldc, ta, tb);
         if (rc != GEMM_F32_OK) return rc;
-        plan = plan_product(batch, M, N, K, ta || tb,
+        plan = plan_product(batch, M, N, K, ops_of(ta, tb),
                             direct_fast(operands_aligned(A, lda, sa, B, ldb, sb), M, N, ta, tb));
         variant = plan.variant[0];
         config_id = plan.config[0];
@@ -421,7 +435,7 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
     } else {
         if (config_id == -1) {
             int v = 0;
-            select_config(batch, M, N, K, &v, &config_id, ta || tb,
+            select_config(batch, M, N, K, &v, &config_id, ops_of(ta, tb),
                           direct_fast(operands_aligned(A, lda, sa, B, ldb, sb), M, N, ta, tb));
             if (v != variant) {  // first configuration of the asked variant that fits
                 config_id = 0;
@@ -495,13 +509,13 @@ int splitk(int variant, int config_id, int64_t splits, int64_t M, int64_t N, int
     int v = variant, c = config_id;
     const bool aligned = direct_fast(
         operands_aligned(A, lda, len, B, ldb, static_cast<int64_t>(len) * ldb), M, N, false, false);
-    if (v == -1) select_config(used, M, N, len, &v, &c, false, aligned);
+    if (v == -1) select_config(used, M, N, len, &v, &c, kOpsSplitK, aligned);
     int count = 0;
     const ConfigEntry *cfgs = configs_of(v, &count);
     if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", v);
     if (c == -1) {
         int vv = 0;
-        select_config(used, M, N, len, &vv, &c, false, aligned);
+        select_config(used, M, N, len, &vv, &c, kOpsSplitK, aligned);
         if (vv != v) c = 0;
     }
     if (c < 0 || c >= count)
@@ -731,7 +745,7 @@ int gemm_f32_select(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, i
     if (variant == nullptr || config_id == nullptr)
         return fail(GEMM_F32_EINVAL, "NULL output pointer");
     const bool fast = direct_fast(lda % 4 == 0 && ldb % 4 == 0, M, N, false, false);
-    const Plan plan = plan_product(1, M, N, K, false, fast);
+    const Plan plan = plan_product(1, M, N, K, 0u, fast);
     *variant = plan.variant[0];
     *config_id = plan.config[0];
     return GEMM_F32_OK;
@@ -745,7 +759,7 @@ int gemm_f32_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int
     if (!parts || !axis || !split || !variant || !config_id)
         return fail(GEMM_F32_EINVAL, "NULL output pointer");
     const bool fast = direct_fast(lda % 4 == 0 && ldb % 4 == 0, M, N, false, false);
-    const Plan plan = plan_product(1, M, N, K, false, fast);
+    const Plan plan = plan_product(1, M, N, K, 0u, fast);
     *parts = plan.parts;
     *axis = plan.parts == 2 ? plan.axis : 0;
     *split = plan.parts == 2 ? plan.split : (plan.axis == 0 ? M : N);

@@ -24,7 +24,9 @@ for a candidate that fits one tile per CU, since one tile per CU runs
 faster per CU than several in turn).  `unaligned` is the median ratio of
 the rate on shapes whose rows are not 16-byte aligned to the aligned rate
 at the same level, and `trans` the same ratio for operands stored transposed
-(A as K x M and / or B as N x K) on a few squares.
+(A as K x M and / or B as N x K) on a few squares.  A candidate with
+`whole_k` (a persistent kernel) is fitted only on the shapes it runs in that
+form: whole tiles, K a multiple of whole_k, B as stored.
 
     python -m dense_fp32_gemm_row_amd.tune.autotune --out tuned.json --calibrate
 
@@ -139,6 +141,12 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
         cfg, bm, bn = cand["config"], int(cand["bm"]), int(cand["bn"])
         levels = len(cand["gflops_per_cu"])
         floor = times[(cfg, 1, 1, 1)]
+        whole_k = int(cand.get("whole_k", 0))
+
+        def rated(M, N, K, ops="NN"):
+            """Shapes the model rates this candidate on: all, or for a
+            persistent candidate those it runs in that form."""
+            return whole_k == 0 or (M % bm == 0 and N % bn == 0 and K % whole_k == 0 and ops[1] == "N")
 
         def share(M, N):
             n = math.ceil(math.ceil(M / bm) * math.ceil(N / bn) / cus)
@@ -147,6 +155,8 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
         def fit_rates(k0):
             groups: dict[int, list[float]] = {}
             for M, N, K in CAL_SHAPES:
+                if not rated(M, N, K):
+                    continue
                 n, level = share(M, N)
                 ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
                 groups.setdefault(level, []).append(2.0 * bm * bn * (K + k0) * n / (ms * 1e-3) / 1e9)
@@ -158,6 +168,8 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
         def fit_k0(rates):
             extra = []
             for M, N, K in CAL_SHORTK:
+                if not rated(M, N, K):
+                    continue
                 n, level = share(M, N)
                 ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
                 extra.append(ms * 1e-3 * rates[level - 1] * 1e9 / (n * 2.0 * bm * bn) - K)
@@ -168,6 +180,8 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
         k0 = fit_k0(rates)
         ratios = []
         for M, N, K in CAL_UNALIGNED:
+            if not rated(M, N, K):
+                continue
             n, level = share(M, N)
             ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
             ratios.append(2.0 * bm * bn * (K + k0) * n / (ms * 1e-3) / 1e9 / rates[level - 1])
@@ -177,12 +191,12 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
         for M, N, K in CAL_TRANS:
             n, level = share(M, N)
             for ops in TRANS_OPS:
-                if (cfg, ops, M, N, K) in times:
+                if (cfg, ops, M, N, K) in times and rated(M, N, K, ops):
                     ms = max(times[(cfg, ops, M, N, K)] - floor, 1e-6)
                     tratios.append(2.0 * bm * bn * (K + k0) * n / (ms * 1e-3) / 1e9 / rates[level - 1])
         out["candidates"].append({**cand, "gflops_per_cu": [round(r, 1) for r in rates],
                                   "k0": round(k0, 1),
-                                  "unaligned": round(min(1.0, statistics.median(ratios)), 3),
+                                  "unaligned": round(min(1.0, statistics.median(ratios)), 3) if ratios else 1.0,
                                   "trans": round(statistics.median(tratios), 3) if tratios else 1.0})
     return out
 

@@ -52,6 +52,7 @@ def render(table: dict) -> str:
         "    float unaligned;",
         "    float k0;",
         "    float trans;  // rate factor with a transposed operand",
+        "    int whole_k;  // > 0: rated only for whole tiles, K a multiple of it, B as stored",
         "};",
         f'constexpr int kModelCUs = {int(table["model"]["cus"])};',
         "constexpr ModelCandidate kModel[] = {",
@@ -63,7 +64,7 @@ def render(table: dict) -> str:
         padded = ", ".join(f"{x:.1f}f" for x in rates + [rates[-1]] * (4 - len(rates)))
         lines.append(f'    {{"{c["config"]}", {int(c["bm"])}, {int(c["bn"])}, {len(rates)}, '
                      f'{{{padded}}}, {float(c["unaligned"]):.3f}f, {float(c.get("k0", 0.0)):.1f}f, '
-                     f'{float(c.get("trans", 1.0)):.3f}f}},')
+                     f'{float(c.get("trans", 1.0)):.3f}f, {int(c.get("whole_k", 0))}}},')
     lines += [
         "};",
         "}  // namespace gemm_f32_impl",
