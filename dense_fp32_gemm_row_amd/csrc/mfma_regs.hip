@@ -1,49 +1,53 @@
 // MFMA tiles whose operands go from global memory straight into registers.
 //
-// For products with about one output tile per CU and a moderate K (the
-// ragged 1000 x 1023 x 777 shape: 256 tiles of 64 x 64, 13 K-steps of 64)
-// the LDS-staged kernels spend a sixth of every K-step on the LDS round trip
-// and the barrier that ends it, with only eight matrix instructions per
-// wavefront between two barriers.  Here each wavefront loads the MFMA
-// operands it needs itself, in the register layout the instruction takes,
-// a few chunks of 16 k ahead: no LDS stores, no LDS reads and no barrier in
-// the K loop.  Wavefronts that read the same rows of A or columns of B share
-// them through the L1 cache instead of LDS.  LDS serves only the sum of the
-// k-groups' partial tiles at the end.
+// With about one output tile per CU the LDS-staged kernels spend a good
+// share of every K-step on the LDS round trip and the barrier that ends it
+// (a sixth for the 64 x 64 k-group tile of the ragged 1000 x 1023 x 777
+// shape).  Here each wavefront loads the MFMA operands it needs itself, in
+// the register layout the instruction takes, a few chunks of 16 k ahead: no
+// LDS stores, no LDS reads and no barrier in the K loop.  LDS serves only
+// the sum of the k-groups' partial tiles at the end.
 //
 // Blocking ("Tiled GEMM: Matrix Multiplication in CUDA", section 2): a
 // workgroup owns a BM x BN tile of C; KG k-groups of WM x WN wavefronts split
 // K between them in chunks of 16 (chunk c goes to group c mod KG), and each
 // wavefront of a group accumulates a (BM / WM) x (BN / WN) slice for its
 // chunks in 16 x 16 blocks of v_mfma_f32_16x16x4_f32 (FM x FN blocks).  The
-// partial tiles are then added in LDS in group order, a fixed order, and
-// group 0 stores the tile ("Tiled Matrix Multiplication in CUDA", section
+// configurations use one wavefront per group (WM = WN = 1), which owns the
+// whole tile, so no operand is loaded twice in a workgroup; one wavefront
+// per SIMD leaves 512 registers per lane (256 accumulator floats for
+// 128 x 128).  The partial tiles are then added in LDS in group order, a
+// fixed order, and stored ("Tiled Matrix Multiplication in CUDA", section
 // 5: one final write per output element).
 //
 // Operand layout of one chunk of 16 k.  Lane l = 16 g + i supplies, to
-// instruction s (s = 0..3), A[row][4 g + s] and B[4 g + s][col]: a fixed
-// permutation of the chunk applied to A and B alike, so lane l's four A
-// values of a row block are A[row][4 g .. 4 g + 3], one 16-byte load.  Block
-// f of A holds rows 16 f + i of the slice; column block j of B holds column
-// FN i + j (interleaved), so a lane's FN values of B in one k row are
-// adjacent, one load of 4 FN bytes.  Per chunk a lane issues FM + 4 loads for
-// 4 FM FN instructions.
+// instruction s (s = 0..3), op(A)[row][4 g + s] and op(B)[4 g + s][col]: a
+// fixed permutation of the chunk applied to A and B alike.  An operand
+// stored with k contiguous (A as stored, B transposed) gives a lane its 4
+// values of a block in one 16-byte load; one stored k-major (B as stored, A
+// transposed) gives it its F interleaved blocks' values of one k row in one
+// load of 4 F bytes (see RegOperand).
 //
 // Edges ("Tiled GEMM: Matrix Multiplication in CUDA", section 7.1).  The K
 // loop runs the chunks that hold neither a k past K nor the last k of the
-// operand, with clamped addresses and no per-element checks: a row of A past
-// M loads row M - 1, a group of FN columns of B that starts past N loads the
-// group that holds column N - 1, and a group that starts inside the row
-// loads as it is (its floats past N come from the row's padding or the next
-// k row, which exists inside the loop).  Those values only feed outputs that
-// are never stored.  The chunk that holds the last k, whole or partial, is a
-// tail with zero fill past K and N, loaded before the loop.  Shapes where a
-// group can reach past the operand's storage even so (N < FN - 1) run a
-// variant that checks every element.  Stores are guarded.
+// operand, with clamped addresses and no per-element checks: a row past M
+// or N loads the last row, a k-major group that starts past the extent
+// loads the group that holds the last row, and a group that starts inside
+// it loads as it is (its floats past the extent come from the row's padding
+// or the next k row, which exists inside the loop).  Those values only feed
+// outputs that are never stored.  The chunk that holds the last k, whole or
+// partial, is a tail with zero fill past K, M and N, loaded before the loop
+// and split over the groups by instruction.  Shapes where a k-major group
+// can reach past the operand's storage even so (an extent below F - 1) run
+// a variant that checks every element.  Stores are guarded.
 //
-// Roofline: MFMA bound per K-step (4 FM FN instructions of 32 cycles per
-// FM + 4 loads); the tile's fixed cost (first loads, the k-group sum, the
-// stores) is what a short K exposes.
+// A persistent form of the kernel (one workgroup per CU walking its tiles,
+// each tile's last chunks loading the next tile's first ones) serves whole
+// tiles with B as stored.
+//
+// Roofline: MFMA bound per chunk (4 FM FN instructions of 32 cycles per
+// FM + 4 loads, or fewer); the tile's fixed cost (first loads, the k-group
+// sum, the stores) is what a short K exposes.
 
 #include "mfma_kernels.h"
 
@@ -183,7 +187,7 @@ struct RegOperand {
 };
 
 // EDGE: 0 = whole tiles and whole chunks (no checks), 1 = clamped loop and a
-// zero-filled tail, 2 = every load checked (tiny N).
+// zero-filled tail, 2 = every load checked (an extent below F - 1).
 // OCC: wavefronts per SIMD at most (one workgroup per CU with OCC = 1: two
 // 64 x 64 tiles that share a CU thrash its L1 and ran at half the rate).
 // ET: the tail's loads go out before the loop, into registers of their own.
