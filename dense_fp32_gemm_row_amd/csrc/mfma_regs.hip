@@ -635,9 +635,12 @@ const ConfigEntry kRegsConfigs[] = {
     // kept: four wavefronts per group (w4x1, w2x2: each operand loaded by two
     // or four wavefronts; ragged 1000 x 1023 x 777 32 against 21 us), eight
     // groups of one wavefront (two per SIMD), 32 x 64 and 128 x 64 tiles,
-    // D from 2 to 6 (within 2%), and loads spread between the MFMAs, into a
-    // third register set (2 to 3% slower) or into the set the previous chunk
-    // freed (one chunk less lead: 0.5% slower at 128 x 128, 8% at 64 x 64).
+    // D from 2 to 6 (within 2%), and loads spread between the MFMAs: into a
+    // third register set (2 to 3% slower), into the set the previous chunk
+    // freed (one chunk less lead: 0.5% slower at 128 x 128, 8% at 64 x 64),
+    // or into the chunk's own set, each piece right after the last
+    // instruction that reads its registers (1 to 10% slower).  A burst of
+    // loads after the chunk's instructions was the fastest form measured.
     {"mfmag_64x64x64_w1x1_k4_d3", launch_regs<64, 64, 1, 1, 4, 3, 1, true, true, 8>, kCapTransposed},
     // 128 x 128: 256 accumulator floats per lane
     {"mfmag_128x128x64_w1x1_k4_d2", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8>, kCapTransposed},
