@@ -51,6 +51,12 @@
 
 #include "mfma_kernels.h"
 
+// Buffer load of 16 bytes: the resource's base plus a lane offset (bytes,
+// plus the instruction's constant offset) plus a scalar offset.
+__device__ gemm_f32_impl::floatx4 gemm_f32_buffer_load_x4(__amdgpu_buffer_rsrc_t rsrc, int voffset,
+                                                          int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.load.v4f32");
+
 namespace gemm_f32_impl {
 namespace {
 
@@ -185,6 +191,98 @@ struct RegOperand {
         }
     }
 };
+
+// An operand of the persistent kernel's whole tiles, loaded as a buffer:
+// the chunk's origin is a scalar resource, a lane's place in the chunk a
+// 32-bit byte offset fixed for the tile, and a k row's distance a scalar
+// offset, so a load takes no vector address arithmetic.  Same layout and
+// lane mapping as RegOperand; k-major operands take F >= 4 (16-byte loads).
+// Offsets stay below 2^31 bytes: the launcher checks (rows - 1) ld + 16
+// (row flavour) and 15 ld + rows (k-major) against 2^28 floats.
+template <bool KMAJOR, int F, bool IL>
+struct BufOperand {
+    static_assert(!KMAJOR || (IL && F % 4 == 0), "k-major operands: interleaved, 16-byte pieces");
+    static constexpr bool kKMajor = KMAJOR;
+    static constexpr int kPieces = KMAJOR ? 4 : F;
+    const float *X;  // the tile's origin: row r0 (row flavour) or column r0 (k-major), k = 0
+    int ld;
+    int voff[KMAJOR ? 1 : F];
+
+    __device__ __forceinline__ void init(const float *X_, int64_t ld_, int base, int g, int i) {
+        ld = static_cast<int>(ld_);
+        if constexpr (KMAJOR) {
+            X = X_ + base;
+            voff[0] = (4 * g * ld + F * i) * 4;
+        } else {
+            X = X_ + static_cast<int64_t>(base) * ld_;
+#pragma unroll
+            for (int f = 0; f < F; ++f) voff[f] = ((IL ? F * i + f : 16 * f + i) * ld + 4 * g) * 4;
+        }
+    }
+    // chunk c's origin: k = 16 c
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk(int c) const {
+        const float *o = KMAJOR ? X + static_cast<int64_t>(c * 16) * ld : X + c * 16;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(o), 0, 0x7fffffff, 0x00020000);
+    }
+    // piece q of chunk c: k row q of a k-major operand (x[.][q]), block q of
+    // a row operand (x[q][.])
+    __device__ __forceinline__ void load_piece(float (&x)[F][4], int c, int q) const {
+        const __amdgpu_buffer_rsrc_t rs = chunk(c);
+        if constexpr (KMAJOR) {
+#pragma unroll
+            for (int p = 0; p < F; p += 4) {
+                const floatx4 t = gemm_f32_buffer_load_x4(rs, voff[0] + 4 * p, q * ld * 4, 0);
+                x[p][q] = t[0], x[p + 1][q] = t[1], x[p + 2][q] = t[2], x[p + 3][q] = t[3];
+            }
+        } else {
+            const floatx4 t = gemm_f32_buffer_load_x4(rs, voff[q], 0, 0);
+            x[q][0] = t[0], x[q][1] = t[1], x[q][2] = t[2], x[q][3] = t[3];
+        }
+    }
+    __device__ __forceinline__ void load(float (&x)[F][4], int c) const {
+#pragma unroll
+        for (int q = 0; q < kPieces; ++q) load_piece(x, c, q);
+    }
+};
+
+// The 4 FM FN instructions of a chunk (sets xa, xb; s, then f, then j), then
+// chunk c's loads into the same sets, each piece issued right after the last
+// instruction that reads the registers it overwrites.
+template <int FM, int FN, class OA, class OB>
+__device__ __forceinline__ void mma_reload(floatx4 (&acc)[FM][FN], float (&xa)[FM][4], float (&xb)[FN][4],
+                                           const OA &la, const OB &lb, int c) {
+    constexpr bool rowA = !OA::kKMajor, rowB = !OB::kKMajor;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[f][s], xb[j][s], acc[f][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!rowA) la.load_piece(xa, c, s);
+        if constexpr (!rowB) lb.load_piece(xb, c, s);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[f][3], xb[j][3], acc[f][j], 0, 0, 0);
+        if constexpr (rowA) {
+            __builtin_amdgcn_sched_barrier(0);
+            la.load_piece(xa, c, f);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if constexpr (!rowA) la.load_piece(xa, c, 3);
+    if constexpr (rowB) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) lb.load_piece(xb, c, j);
+    } else {
+        lb.load_piece(xb, c, 3);
+    }
+}
 
 // EDGE: 0 = whole tiles and whole chunks (no checks), 1 = clamped loop and a
 // zero-filled tail, 2 = every load checked (an extent below F - 1).
@@ -405,7 +503,9 @@ __device__ __forceinline__ void lds_barrier() {
 // grid), and the last D chunks of a tile load the next tile's first D
 // chunks into their register sets.  The next tile's loads are thus in
 // flight during this tile's k-group sum and stores, and no workgroup start
-// or first-load latency sits between two tiles of a CU.
+// or first-load latency sits between two tiles of a CU.  Operands load as
+// buffers (no vector address arithmetic), each piece of a set's next chunk
+// right after the instructions that last read its registers (mma_reload).
 template <int BM, int BN, int KG, int D, bool TA, bool TB>
 __global__ __launch_bounds__(64 * KG) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mfma_regs_persistent_kernel(
@@ -419,8 +519,8 @@ void gemm_mfma_regs_persistent_kernel(
     constexpr int RP = regs_pass_rows(FM, FN, KG, 1);
     static_assert(RP > 0, "LDS room for the k-group sum");
     __shared__ __align__(16) float red[KG * RP * 64 * FN];
-    using OpA = RegOperand<TA, FM, TA>;
-    using OpB = RegOperand<!TB, FN, true>;
+    using OpA = BufOperand<TA, FM, TA>;
+    using OpB = BufOperand<!TB, FN, true>;
 
     const int total = tiles_m * tiles_n * bt.count;
     const int G = static_cast<int>(gridDim.x);
@@ -439,8 +539,8 @@ void gemm_mfma_regs_persistent_kernel(
         int tm, tn;
         grouped_tile(t, tiles_m, tiles_n, group_m, tm, tn);
         m0 = tm * BM, n0 = tn * BN;
-        oa.init(a, lda, M, m0, g, i, false);
-        ob.init(b, ldb, N, n0, g, i, false);
+        oa.init(a, lda, m0, g, i);
+        ob.init(b, ldb, n0, g, i);
     };
 
     int logical = xcd_remap(static_cast<int>(blockIdx.x), G);
@@ -455,19 +555,6 @@ void gemm_mfma_regs_persistent_kernel(
     float rb[D][FN][4];
     floatx4 acc[FM][FN];
 #pragma unroll
-    for (int f = 0; f < FM; ++f)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[f][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    auto mma = [&](const float (&xa)[FM][4], const float (&xb)[FN][4]) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int f = 0; f < FM; ++f)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[f][s], xb[j][s], acc[f][j], 0, 0, 0);
-    };
-#pragma unroll
     for (int u = 0; u < D; ++u) {
         oa.load(ra[u], chunk_of(u));
         ob.load(rb[u], chunk_of(u));
@@ -477,16 +564,18 @@ void gemm_mfma_regs_persistent_kernel(
     auto part = [&](int h, int q) { return red + (h * RP + q) * 64 * FN + lane * FN; };
 
     for (;;) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[f][j] = floatx4{0.f, 0.f, 0.f, 0.f};
         const int next = logical + G;
         const bool has_next = next < total;
         int t = 0;
         for (; t + D < ng; t += D) {
 #pragma unroll
             for (int u = 0; u < D; ++u) {
-                mma(ra[u], rb[u]);
                 __builtin_amdgcn_sched_barrier(0);
-                oa.load(ra[u], chunk_of(t + u + D));
-                ob.load(rb[u], chunk_of(t + u + D));
+                mma_reload(acc, ra[u], rb[u], oa, ob, chunk_of(t + u + D));
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -499,10 +588,8 @@ void gemm_mfma_regs_persistent_kernel(
         }
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            mma(ra[u], rb[u]);
             __builtin_amdgcn_sched_barrier(0);
-            oa_n.load(ra[u], chunk_of(u));
-            ob_n.load(rb[u], chunk_of(u));
+            mma_reload(acc, ra[u], rb[u], oa_n, ob_n, chunk_of(u));
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -557,10 +644,6 @@ void gemm_mfma_regs_persistent_kernel(
             }
         }
         if (!has_next) break;
-#pragma unroll
-        for (int f = 0; f < FM; ++f)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[f][j] = floatx4{0.f, 0.f, 0.f, 0.f};
         logical = next;
         oa = oa_n, ob = ob_n, c = c_n, m0 = m0_n, n0 = n0_n;
     }
@@ -588,11 +671,11 @@ hipError_t launch_regs(const Problem &p, hipStream_t stream) {
     const dim3 gd(static_cast<unsigned>(grid)), bd(NT);
     if constexpr (PERSIST) {
         // whole tiles, K whole rounds of D chunks per group, no split-K
-        // slices (every tile the same K), B as stored: one workgroup per CU
-        // walks the tiles.  (With B transposed the persistent kernel ran 6
-        // to 9% slower than one launch per tile at 8192^3, 4096^3 and the
-        // FFN shape, and 1% faster with B as stored.)
-        if (p.M % BM == 0 && p.N % BN == 0 && p.K % (16 * KG * D) == 0 && p.ksplit == 0 && !p.tb) {
+        // slices (every tile the same K), and a chunk's buffer offsets below
+        // 2^31 bytes: one workgroup per CU walks the tiles
+        const bool buf_ok = (p.ta ? 15 * p.lda + BM : (BM - 1) * p.lda + 16) < (int64_t{1} << 28) &&
+                            (p.tb ? (BN - 1) * p.ldb + 16 : 15 * p.ldb + BN) < (int64_t{1} << 28);
+        if (p.M % BM == 0 && p.N % BN == 0 && p.K % (16 * KG * D) == 0 && p.ksplit == 0 && buf_ok) {
             int dev = 0, cus = 0;
             hipError_t e = hipGetDevice(&dev);
             if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -602,7 +685,9 @@ hipError_t launch_regs(const Problem &p, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_mfma_regs_persistent_kernel<BM, BN, KG, D, TA_, TB_>), dim3(wgs), bd, 0, \
                        stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,  \
                        GROUP_M, batch_of(p))
-            if (p.ta) GEMM_REGS_P(true, false);
+            if (p.ta && p.tb) GEMM_REGS_P(true, true);
+            else if (p.tb) GEMM_REGS_P(false, true);
+            else if (p.ta) GEMM_REGS_P(true, false);
             else GEMM_REGS_P(false, false);
 #undef GEMM_REGS_P
             return hipGetLastError();

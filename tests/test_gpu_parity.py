@@ -721,11 +721,10 @@ PERSISTENT_SHAPES = [(256, 256, 384), (2048, 2304, 384), (1280, 4096, 768)]
 @pytest.mark.parametrize("ops", OPS)
 def test_persistent_register_direct(kernel, ops):
     """The persistent register-direct kernel runs whole tiles with K a
-    multiple of 128 (16 k x 4 groups x 2 chunks in flight) and B as stored:
-    one workgroup per CU walks one to five tiles, and the last chunks of each
-    tile load the next tile's first ones.  Fewer tiles than CUs, and rounds
-    with part of the workgroups idle; the forms with B transposed take the
-    one-launch kernel.  Exact on integers."""
+    multiple of 128 (16 k x 4 groups x 2 chunks in flight), every operand
+    form: one workgroup per CU walks one to five tiles, and the last chunks
+    of each tile load the next tile's first ones.  Fewer tiles than CUs, and
+    rounds with part of the workgroups idle.  Exact on integers."""
     import torch
 
     v, c, name = kernel
@@ -735,6 +734,41 @@ def test_persistent_register_direct(kernel, ops):
         out = torch.full((M, N), float("nan"), device="cuda:0")
         b.gemm(_stored(A, ops[0]), _stored(B, ops[1]), out, variant=v, config=c)
         assert_exact(to_host(out), oracle.gemm(A, B), f"{name} {ops} {M}x{N}x{K}")
+
+
+# (operand, leading dimension): just inside the buffer-offset limit of the
+# persistent kernel (a chunk's byte offsets below 2^31) and just past it,
+# where the launcher takes the one-launch kernel instead
+PERSISTENT_FAR = [("A", 1 << 21), ("A", (1 << 21) + (1 << 17)), ("AT", (1 << 24)),
+                  ("B", 1 << 24), ("B", (1 << 24) + (1 << 21)), ("BT", 1 << 21)]
+
+
+@pytest.mark.parametrize("kernel", PERSISTENT, ids=[k[2] for k in PERSISTENT])
+@pytest.mark.parametrize("operand,ld", PERSISTENT_FAR,
+                         ids=[f"{o}_ld{ld}" for o, ld in PERSISTENT_FAR])
+def test_persistent_register_direct_far_rows(kernel, operand, ld):
+    """Whole 128 x 128 x 256 products with one operand's rows (or k rows)
+    far apart: byte offsets within a chunk near 2^30 on the buffer-load
+    path, and past the limit on the fallback.  Exact on integers."""
+    import torch
+
+    v, c, name = kernel
+    M, N, K = 128, 128, 256
+    A, B = make_inputs(M, N, K, "int4", seed=73)
+    X = {"A": A, "AT": A.T, "B": B, "BT": B.T}[operand]
+    rows, cols = X.shape
+    log(f"persistent far rows {operand} ld {ld} on {name}")
+    buf = torch.empty((rows - 1) * ld + cols, dtype=torch.float32, device="cuda:0")
+    dX = buf.as_strided((rows, cols), (ld, 1))
+    dX.copy_(to_dev(np.ascontiguousarray(X)))
+    dA = dX if operand == "A" else dX.T if operand == "AT" else to_dev(A)
+    dB = dX if operand == "B" else dX.T if operand == "BT" else to_dev(B)
+    out = torch.full((M, N), float("nan"), device="cuda:0")
+    b.gemm(dA, dB, out, variant=v, config=c)
+    got = to_host(out)
+    del dX, buf, dA, dB
+    torch.cuda.empty_cache()
+    assert_exact(got, oracle.gemm(A, B), f"{name} {operand} ld {ld}")
 
 
 @pytest.mark.parametrize("kernel", PERSISTENT, ids=[k[2] for k in PERSISTENT])
