@@ -724,8 +724,9 @@ const ConfigEntry kRegsConfigs[] = {
     // third register set (2 to 3% slower), into the set the previous chunk
     // freed (one chunk less lead: 0.5% slower at 128 x 128, 8% at 64 x 64),
     // or into the chunk's own set, each piece right after the last
-    // instruction that reads its registers (1 to 10% slower).  A burst of
-    // loads after the chunk's instructions was the fastest form measured.
+    // instruction that reads its registers (1 to 10% slower with global
+    // loads; with buffer loads, as the persistent tile runs them, the 64 x 64
+    // tile gained nothing and the 128 x 128 one spilled registers).
     {"mfmag_64x64x64_w1x1_k4_d3", launch_regs<64, 64, 1, 1, 4, 3, 1, true, true, 8>, kCapTransposed},
     // 128 x 128: 256 accumulator floats per lane
     {"mfmag_128x128x64_w1x1_k4_d2", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8>, kCapTransposed},
