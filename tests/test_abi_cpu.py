@@ -3,6 +3,7 @@ and rejects invalid arguments before touching the device (no compute call
 reaches HIP here)."""
 
 import ctypes
+import json
 import os
 import re
 
@@ -358,7 +359,9 @@ def test_header_serves_a_c_caller(lib, tmp_path):
     assert res.returncode == 0, res.stderr
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
-    assert f"select mfma2d_256x256x32_w4x4_swz_g4_il {len(names)}" in run.stdout
+    with open(os.path.join(ROOT, "dense_fp32_gemm_row_amd", "tune", "table.json")) as f:
+        tuned = {(e["M"], e["N"], e["K"]): e["config"] for e in json.load(f)["entries"]}
+    assert f"select {tuned[(8192, 8192, 8192)]} {len(names)}" in run.stdout
 
 
 def test_split_plans(lib):
