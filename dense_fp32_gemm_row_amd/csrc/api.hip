@@ -251,19 +251,19 @@ const ModelIds &model_ids() {
     return ids;
 }
 // What a product asks of a candidate besides its shape: a transposed
-// operand (the candidate must take them), B transposed, split-K slices.
-constexpr unsigned kOpsTrans = 1u, kOpsBTrans = 2u, kOpsSplitK = 4u;
-unsigned ops_of(bool ta, bool tb) { return (ta || tb ? kOpsTrans : 0u) | (tb ? kOpsBTrans : 0u); }
+// operand (the candidate must take them), split-K slices.
+constexpr unsigned kOpsTrans = 1u, kOpsSplitK = 4u;
+unsigned ops_of(bool ta, bool tb) { return ta || tb ? kOpsTrans : 0u; }
 
 // A candidate with whole_k > 0 (a persistent kernel) is rated only for the
-// products it runs in that form: whole tiles, K a multiple of whole_k, B as
-// stored, no split-K slices.
+// products it runs in that form: whole tiles, K a multiple of whole_k, no
+// split-K slices.
 bool usable(int i, unsigned ops, int64_t M, int64_t N, int64_t K) {
     const ModelIds &ids = model_ids();
     if (ids.id[i] < 0 || ((ops & kOpsTrans) && !ids.trans[i])) return false;
     const ModelCandidate &m = kModel[i];
-    return m.whole_k == 0 || (!(ops & (kOpsBTrans | kOpsSplitK)) && M % m.bm == 0 &&
-                              N % m.bn == 0 && K % m.whole_k == 0);
+    return m.whole_k == 0 ||
+           (!(ops & kOpsSplitK) && M % m.bm == 0 && N % m.bn == 0 && K % m.whole_k == 0);
 }
 
 // The model's fastest candidate; returns its predicted microseconds.

@@ -26,7 +26,7 @@ the rate on shapes whose rows are not 16-byte aligned to the aligned rate
 at the same level, and `trans` the same ratio for operands stored transposed
 (A as K x M and / or B as N x K) on a few squares.  A candidate with
 `whole_k` (a persistent kernel) is fitted only on the shapes it runs in that
-form: whole tiles, K a multiple of whole_k, B as stored.
+form: whole tiles, K a multiple of whole_k.
 
     python -m dense_fp32_gemm_row_amd.tune.autotune --out tuned.json --calibrate
 
@@ -143,10 +143,10 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
         floor = times[(cfg, 1, 1, 1)]
         whole_k = int(cand.get("whole_k", 0))
 
-        def rated(M, N, K, ops="NN"):
+        def rated(M, N, K):
             """Shapes the model rates this candidate on: all, or for a
             persistent candidate those it runs in that form."""
-            return whole_k == 0 or (M % bm == 0 and N % bn == 0 and K % whole_k == 0 and ops[1] == "N")
+            return whole_k == 0 or (M % bm == 0 and N % bn == 0 and K % whole_k == 0)
 
         def share(M, N):
             n = math.ceil(math.ceil(M / bm) * math.ceil(N / bn) / cus)
@@ -191,7 +191,7 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
         for M, N, K in CAL_TRANS:
             n, level = share(M, N)
             for ops in TRANS_OPS:
-                if (cfg, ops, M, N, K) in times and rated(M, N, K, ops):
+                if (cfg, ops, M, N, K) in times and rated(M, N, K):
                     ms = max(times[(cfg, ops, M, N, K)] - floor, 1e-6)
                     tratios.append(2.0 * bm * bn * (K + k0) * n / (ms * 1e-3) / 1e9 / rates[level - 1])
         out["candidates"].append({**cand, "gflops_per_cu": [round(r, 1) for r in rates],

@@ -52,7 +52,7 @@ def render(table: dict) -> str:
         "    float unaligned;",
         "    float k0;",
         "    float trans;  // rate factor with a transposed operand",
-        "    int whole_k;  // > 0: rated only for whole tiles, K a multiple of it, B as stored",
+        "    int whole_k;  // > 0: rated only for whole tiles, K a multiple of it, no split-K",
         "};",
         f'constexpr int kModelCUs = {int(table["model"]["cus"])};',
         "constexpr ModelCandidate kModel[] = {",
