@@ -43,7 +43,10 @@
 //
 // A persistent form of the kernel (one workgroup per CU walking its tiles,
 // each tile's last chunks loading the next tile's first ones) serves whole
-// tiles with B as stored.
+// tiles with K a multiple of 16 KG D, in every operand form.  It loads the
+// operands as buffers (a scalar resource per chunk, a lane offset fixed per
+// tile, a scalar offset per k row: no vector address arithmetic), each piece
+// right after the last instruction that reads the registers it refills.
 //
 // Roofline: MFMA bound per chunk (4 FM FN instructions of 32 cycles per
 // FM + 4 loads, or fewer); the tile's fixed cost (first loads, the k-group
