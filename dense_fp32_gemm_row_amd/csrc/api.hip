@@ -224,8 +224,12 @@ double model_us(const ModelCandidate &m, int64_t batch, int64_t M, int64_t N, in
     const int64_t tiles = ((M + m.bm - 1) / m.bm) * ((N + m.bn - 1) / m.bn) * batch;
     const int64_t n = (tiles + kModelCUs - 1) / kModelCUs;
     const int level = static_cast<int>(n < m.nrates ? n : m.nrates);
+    // a persistent candidate runs K in whole rounds of whole_k, and its edge
+    // form (tiles past M or N, K past whole rounds) at its edge rate
+    const bool edge = m.whole_k > 0 && (M % m.bm || N % m.bn || K % m.whole_k);
+    if (m.whole_k > 0) K = (K + m.whole_k - 1) / m.whole_k * m.whole_k;
     const double rate = m.gflops_per_cu[level > 0 ? level - 1 : 0] * (aligned ? 1.0 : m.unaligned) *
-                        (trans ? m.trans : 1.0);
+                        (trans ? m.trans : 1.0) * (edge ? m.edge : 1.0);
     return static_cast<double>(n) * 2.0 * m.bm * m.bn * (static_cast<double>(K) + m.k0) /
            (rate * 1e3);
 }
@@ -251,19 +255,25 @@ const ModelIds &model_ids() {
     return ids;
 }
 // What a product asks of a candidate besides its shape: a transposed
-// operand (the candidate must take them), split-K slices.
-constexpr unsigned kOpsTrans = 1u, kOpsSplitK = 4u;
-unsigned ops_of(bool ta, bool tb) { return ta || tb ? kOpsTrans : 0u; }
+// operand (the candidate must take them; A, B transposed), split-K slices.
+constexpr unsigned kOpsTrans = 1u, kOpsTransA = 2u, kOpsSplitK = 4u, kOpsTransB = 8u;
+unsigned ops_of(bool ta, bool tb) {
+    return (ta || tb ? kOpsTrans : 0u) | (ta ? kOpsTransA : 0u) | (tb ? kOpsTransB : 0u);
+}
 
 // A candidate with whole_k > 0 (a persistent kernel) is rated only for the
-// products it runs in that form: whole tiles, K a multiple of whole_k, no
-// split-K slices.
+// products it runs in that form: no split-K slices, and whole tiles with K a
+// multiple of whole_k, or (its edge form) K and the row length of a k-major
+// operand (M for A transposed, N for B as stored) multiples of 4.
 bool usable(int i, unsigned ops, int64_t M, int64_t N, int64_t K) {
     const ModelIds &ids = model_ids();
     if (ids.id[i] < 0 || ((ops & kOpsTrans) && !ids.trans[i])) return false;
     const ModelCandidate &m = kModel[i];
-    return m.whole_k == 0 ||
-           (!(ops & kOpsSplitK) && M % m.bm == 0 && N % m.bn == 0 && K % m.whole_k == 0);
+    if (m.whole_k == 0) return true;
+    if ((ops & kOpsSplitK) || K <= 0) return false;
+    const bool whole = M % m.bm == 0 && N % m.bn == 0 && K % m.whole_k == 0;
+    const bool edge = K % 4 == 0 && (!(ops & kOpsTransA) || M % 4 == 0) && ((ops & kOpsTransB) || N % 4 == 0);
+    return whole || edge;
 }
 
 // The model's fastest candidate; returns its predicted microseconds.

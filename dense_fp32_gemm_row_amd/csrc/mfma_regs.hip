@@ -52,6 +52,8 @@
 // FM + 4 loads, or fewer); the tile's fixed cost (first loads, the k-group
 // sum, the stores) is what a short K exposes.
 
+#include <type_traits>
+
 #include "mfma_kernels.h"
 
 // Buffer load of 16 bytes: the resource's base plus a lane offset (bytes,
@@ -195,31 +197,48 @@ struct RegOperand {
     }
 };
 
-// An operand of the persistent kernel's whole tiles, loaded as a buffer:
-// the chunk's origin is a scalar resource, a lane's place in the chunk a
-// 32-bit byte offset fixed for the tile, and a k row's distance a scalar
-// offset, so a load takes no vector address arithmetic.  Same layout and
+// An operand of the persistent kernel, loaded as a buffer: the chunk's
+// origin is a scalar resource, a lane's place in the chunk a 32-bit byte
+// offset fixed for the tile, and a k row's distance a scalar offset, so a
+// load of a whole tile takes no vector address arithmetic.  Same layout and
 // lane mapping as RegOperand; k-major operands take F >= 4 (16-byte loads).
 // Offsets stay below 2^31 bytes: the launcher checks (rows - 1) ld + 16
 // (row flavour) and 15 ld + rows (k-major) against 2^28 floats.
-template <bool KMAJOR, int F, bool IL>
+// EDGE: rows past R and k past K read as zeros: their offset is 2^31, past
+// the resource's 2^31 - 1 bytes, and an out-of-range buffer load returns 0.
+// Whole rows (row flavour) or groups of 4 (k-major) are in or out: K, and
+// R of a k-major operand, are multiples of 4 (the launcher checks).
+template <bool KMAJOR, int F, bool IL, bool EDGE = false>
 struct BufOperand {
     static_assert(!KMAJOR || (IL && F % 4 == 0), "k-major operands: interleaved, 16-byte pieces");
     static constexpr bool kKMajor = KMAJOR;
     static constexpr int kPieces = KMAJOR ? 4 : F;
+    static constexpr int kOut = static_cast<int>(0x80000000u);  // an offset past the resource
     const float *X;  // the tile's origin: row r0 (row flavour) or column r0 (k-major), k = 0
     int ld;
-    int voff[KMAJOR ? 1 : F];
+    int voff[KMAJOR ? (EDGE ? F / 4 : 1) : F];
+    int klim;  // EDGE: K - 4 g, the lane's first k past the operand (relative to the chunk)
 
-    __device__ __forceinline__ void init(const float *X_, int64_t ld_, int base, int g, int i) {
+    __device__ __forceinline__ void init(const float *X_, int64_t ld_, int base, int g, int i, int R = 0,
+                                         int K = 0) {
         ld = static_cast<int>(ld_);
+        klim = K - 4 * g;
         if constexpr (KMAJOR) {
             X = X_ + base;
-            voff[0] = (4 * g * ld + F * i) * 4;
+            if constexpr (EDGE) {
+#pragma unroll
+                for (int p = 0; p < F; p += 4)
+                    voff[p / 4] = base + F * i + p < R ? (4 * g * ld + F * i + p) * 4 : kOut;
+            } else {
+                voff[0] = (4 * g * ld + F * i) * 4;
+            }
         } else {
             X = X_ + static_cast<int64_t>(base) * ld_;
 #pragma unroll
-            for (int f = 0; f < F; ++f) voff[f] = ((IL ? F * i + f : 16 * f + i) * ld + 4 * g) * 4;
+            for (int f = 0; f < F; ++f) {
+                const int r = IL ? F * i + f : 16 * f + i;
+                voff[f] = !EDGE || base + r < R ? (r * ld + 4 * g) * 4 : kOut;
+            }
         }
     }
     // chunk c's origin: k = 16 c
@@ -228,30 +247,37 @@ struct BufOperand {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(o), 0, 0x7fffffff, 0x00020000);
     }
     // piece q of chunk c: k row q of a k-major operand (x[.][q]), block q of
-    // a row operand (x[q][.])
+    // a row operand (x[q][.]); KCHK: the chunk may hold k past K (a per-lane
+    // check, otherwise none)
+    template <bool KCHK>
     __device__ __forceinline__ void load_piece(float (&x)[F][4], int c, int q) const {
+        constexpr bool kc = EDGE && KCHK;
         const __amdgpu_buffer_rsrc_t rs = chunk(c);
         if constexpr (KMAJOR) {
+            const bool kin = !kc || c * 16 + q < klim;
 #pragma unroll
             for (int p = 0; p < F; p += 4) {
-                const floatx4 t = gemm_f32_buffer_load_x4(rs, voff[0] + 4 * p, q * ld * 4, 0);
+                const int v = EDGE ? voff[p / 4] : voff[0] + 4 * p;
+                const floatx4 t = gemm_f32_buffer_load_x4(rs, kin ? v : kOut, q * ld * 4, 0);
                 x[p][q] = t[0], x[p + 1][q] = t[1], x[p + 2][q] = t[2], x[p + 3][q] = t[3];
             }
         } else {
-            const floatx4 t = gemm_f32_buffer_load_x4(rs, voff[q], 0, 0);
+            const int o = kc && c * 16 >= klim ? kOut : voff[q];
+            const floatx4 t = gemm_f32_buffer_load_x4(rs, o, 0, 0);
             x[q][0] = t[0], x[q][1] = t[1], x[q][2] = t[2], x[q][3] = t[3];
         }
     }
+    template <bool KCHK>
     __device__ __forceinline__ void load(float (&x)[F][4], int c) const {
 #pragma unroll
-        for (int q = 0; q < kPieces; ++q) load_piece(x, c, q);
+        for (int q = 0; q < kPieces; ++q) load_piece<KCHK>(x, c, q);
     }
 };
 
 // The 4 FM FN instructions of a chunk (sets xa, xb; s, then f, then j), then
 // chunk c's loads into the same sets, each piece issued right after the last
 // instruction that reads the registers it overwrites.
-template <int FM, int FN, class OA, class OB>
+template <bool KCHK, int FM, int FN, class OA, class OB>
 __device__ __forceinline__ void mma_reload(floatx4 (&acc)[FM][FN], float (&xa)[FM][4], float (&xb)[FN][4],
                                            const OA &la, const OB &lb, int c) {
     constexpr bool rowA = !OA::kKMajor, rowB = !OB::kKMajor;
@@ -263,8 +289,8 @@ __device__ __forceinline__ void mma_reload(floatx4 (&acc)[FM][FN], float (&xa)[F
             for (int j = 0; j < FN; ++j)
                 acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[f][s], xb[j][s], acc[f][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (!rowA) la.load_piece(xa, c, s);
-        if constexpr (!rowB) lb.load_piece(xb, c, s);
+        if constexpr (!rowA) la.template load_piece<KCHK>(xa, c, s);
+        if constexpr (!rowB) lb.template load_piece<KCHK>(xb, c, s);
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -274,16 +300,16 @@ __device__ __forceinline__ void mma_reload(floatx4 (&acc)[FM][FN], float (&xa)[F
             acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[f][3], xb[j][3], acc[f][j], 0, 0, 0);
         if constexpr (rowA) {
             __builtin_amdgcn_sched_barrier(0);
-            la.load_piece(xa, c, f);
+            la.template load_piece<KCHK>(xa, c, f);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    if constexpr (!rowA) la.load_piece(xa, c, 3);
+    if constexpr (!rowA) la.template load_piece<KCHK>(xa, c, 3);
     if constexpr (rowB) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) lb.load_piece(xb, c, j);
+        for (int j = 0; j < FN; ++j) lb.template load_piece<KCHK>(xb, c, j);
     } else {
-        lb.load_piece(xb, c, 3);
+        lb.template load_piece<KCHK>(xb, c, 3);
     }
 }
 
@@ -509,7 +535,10 @@ __device__ __forceinline__ void lds_barrier() {
 // or first-load latency sits between two tiles of a CU.  Operands load as
 // buffers (no vector address arithmetic), each piece of a set's next chunk
 // right after the instructions that last read its registers (mma_reload).
-template <int BM, int BN, int KG, int D, bool TA, bool TB>
+// EDGE: edge tiles and K not a multiple of 16 KG D: rows past M or N and k
+// past K load as zeros (BufOperand), each group runs K rounded up to whole
+// rounds of D chunks, and stores past M or N are skipped.
+template <int BM, int BN, int KG, int D, bool TA, bool TB, bool EDGE>
 __global__ __launch_bounds__(64 * KG) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mfma_regs_persistent_kernel(
     int M, int N, int K, const float *__restrict__ A, int64_t lda,
@@ -522,15 +551,17 @@ void gemm_mfma_regs_persistent_kernel(
     constexpr int RP = regs_pass_rows(FM, FN, KG, 1);
     static_assert(RP > 0, "LDS room for the k-group sum");
     __shared__ __align__(16) float red[KG * RP * 64 * FN];
-    using OpA = BufOperand<TA, FM, TA>;
-    using OpB = BufOperand<!TB, FN, true>;
+    using OpA = BufOperand<TA, FM, TA, EDGE>;
+    using OpB = BufOperand<!TB, FN, true, EDGE>;
 
     const int total = tiles_m * tiles_n * bt.count;
     const int G = static_cast<int>(gridDim.x);
     const int lane = threadIdx.x & 63;
     const int kg = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int g = lane / 16, i = lane % 16;
-    const int ng = K / CK / KG;  // chunks of each group: kg, kg + KG, ...
+    // chunks of each group: kg, kg + KG, ... (with EDGE, K rounded up to
+    // whole rounds of KG D chunks; the chunks past K load zeros)
+    const int ng = EDGE ? (K + CK * KG * D - 1) / (CK * KG * D) * D : K / CK / KG;
     auto chunk_of = [&](int t) { return kg + KG * t; };
 
     // operands, C and origin of logical tile `logical`
@@ -542,8 +573,8 @@ void gemm_mfma_regs_persistent_kernel(
         int tm, tn;
         grouped_tile(t, tiles_m, tiles_n, group_m, tm, tn);
         m0 = tm * BM, n0 = tn * BN;
-        oa.init(a, lda, m0, g, i);
-        ob.init(b, ldb, n0, g, i);
+        oa.init(a, lda, m0, g, i, M, K);
+        ob.init(b, ldb, n0, g, i, N, K);
     };
 
     int logical = xcd_remap(static_cast<int>(blockIdx.x), G);
@@ -557,10 +588,18 @@ void gemm_mfma_regs_persistent_kernel(
     float ra[D][FM][4];
     float rb[D][FN][4];
     floatx4 acc[FM][FN];
+    // EDGE: the loads of a tile's first D chunks check k (a few per tile),
+    // and so do those of the loop's rounds from t_chk on, the first round
+    // that loads a chunk holding k past K; the rounds before do not
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-        oa.load(ra[u], chunk_of(u));
-        ob.load(rb[u], chunk_of(u));
+        oa.template load<EDGE>(ra[u], chunk_of(u));
+        ob.template load<EDGE>(rb[u], chunk_of(u));
+    }
+    int t_chk = ng;
+    if constexpr (EDGE) {
+        t_chk = 0;
+        while (t_chk + D < ng && CK * chunk_of(t_chk + 2 * D - 1) + CK <= K) t_chk += D;
     }
     const bool vec_c = ((reinterpret_cast<uintptr_t>(C) | static_cast<uintptr_t>(ldc * 4)) &
                         (4 * (FN < 4 ? FN : 4) - 1)) == 0;
@@ -573,15 +612,18 @@ void gemm_mfma_regs_persistent_kernel(
             for (int j = 0; j < FN; ++j) acc[f][j] = floatx4{0.f, 0.f, 0.f, 0.f};
         const int next = logical + G;
         const bool has_next = next < total;
-        int t = 0;
-        for (; t + D < ng; t += D) {
+        auto round = [&](int t, auto kchk) {
 #pragma unroll
             for (int u = 0; u < D; ++u) {
                 __builtin_amdgcn_sched_barrier(0);
-                mma_reload(acc, ra[u], rb[u], oa, ob, chunk_of(t + u + D));
+                mma_reload<decltype(kchk)::value>(acc, ra[u], rb[u], oa, ob, chunk_of(t + u + D));
                 __builtin_amdgcn_sched_barrier(0);
             }
-        }
+        };
+        int t = 0;
+        for (; t + D < ng && t < t_chk; t += D) round(t, std::false_type{});
+        if constexpr (EDGE)
+            for (; t + D < ng; t += D) round(t, std::true_type{});
         // the last D chunks; their sets take the next tile's first D chunks
         // (the last tile reloads its own, in bounds and never used)
         if (has_next) {
@@ -592,7 +634,7 @@ void gemm_mfma_regs_persistent_kernel(
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             __builtin_amdgcn_sched_barrier(0);
-            mma_reload(acc, ra[u], rb[u], oa_n, ob_n, chunk_of(u));
+            mma_reload<EDGE>(acc, ra[u], rb[u], oa_n, ob_n, chunk_of(u));
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -638,11 +680,12 @@ void gemm_mfma_regs_persistent_kernel(
                 }
                 const int gm = m0 + (TA ? FM * (4 * g + r) + f : 16 * f + 4 * g + r);
                 float *row = c + static_cast<int64_t>(gm) * ldc + bcol;
-                if (vec_c) {
+                if (vec_c && (!EDGE || (m0 + BM <= M && n0 + BN <= N))) {
                     store_run<FN>(row, v);
                 } else {
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) row[j] = v[j];
+                    for (int j = 0; j < FN; ++j)
+                        if (!EDGE || (gm < M && bcol + j < N)) row[j] = v[j];
                 }
             }
         }
@@ -673,26 +716,35 @@ hipError_t launch_regs(const Problem &p, hipStream_t stream) {
     const int edge = whole && WHOLE ? 0 : clamp_ok ? 1 : 2;
     const dim3 gd(static_cast<unsigned>(grid)), bd(NT);
     if constexpr (PERSIST) {
-        // whole tiles, K whole rounds of D chunks per group, no split-K
-        // slices (every tile the same K), and a chunk's buffer offsets below
-        // 2^31 bytes: one workgroup per CU walks the tiles
+        // one workgroup per CU walks the tiles: no split-K slices (every
+        // tile the same K), a chunk's buffer offsets below 2^31 bytes, and
+        // whole tiles with K whole rounds of D chunks per group, or else
+        // (EDGE form) K and the rows of a k-major operand multiples of 4
         const bool buf_ok = (p.ta ? 15 * p.lda + BM : (BM - 1) * p.lda + 16) < (int64_t{1} << 28) &&
                             (p.tb ? (BN - 1) * p.ldb + 16 : 15 * p.ldb + BN) < (int64_t{1} << 28);
-        if (p.M % BM == 0 && p.N % BN == 0 && p.K % (16 * KG * D) == 0 && p.ksplit == 0 && buf_ok) {
+        const bool whole_p = p.M % BM == 0 && p.N % BN == 0 && p.K % (16 * KG * D) == 0;
+        const bool edge_p = p.K % 4 == 0 && (!p.ta || p.M % 4 == 0) && (p.tb || p.N % 4 == 0);
+        if (p.ksplit == 0 && buf_ok && p.K > 0 && (whole_p || edge_p)) {
             int dev = 0, cus = 0;
             hipError_t e = hipGetDevice(&dev);
             if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             if (e != hipSuccess) return e;
             const unsigned wgs = static_cast<unsigned>(grid < cus ? grid : cus);
-#define GEMM_REGS_P(TA_, TB_)                                                                        \
-    hipLaunchKernelGGL((gemm_mfma_regs_persistent_kernel<BM, BN, KG, D, TA_, TB_>), dim3(wgs), bd, 0, \
-                       stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,  \
+#define GEMM_REGS_P1(TA_, TB_, E)                                                                       \
+    hipLaunchKernelGGL((gemm_mfma_regs_persistent_kernel<BM, BN, KG, D, TA_, TB_, E>), dim3(wgs), bd, 0, \
+                       stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,     \
                        GROUP_M, batch_of(p))
+#define GEMM_REGS_P(TA_, TB_)                            \
+    do {                                                 \
+        if (whole_p) GEMM_REGS_P1(TA_, TB_, false);      \
+        else GEMM_REGS_P1(TA_, TB_, true);               \
+    } while (0)
             if (p.ta && p.tb) GEMM_REGS_P(true, true);
             else if (p.tb) GEMM_REGS_P(false, true);
             else if (p.ta) GEMM_REGS_P(true, false);
             else GEMM_REGS_P(false, false);
 #undef GEMM_REGS_P
+#undef GEMM_REGS_P1
             return hipGetLastError();
         }
     }

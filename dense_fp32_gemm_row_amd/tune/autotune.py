@@ -26,7 +26,9 @@ the rate on shapes whose rows are not 16-byte aligned to the aligned rate
 at the same level, and `trans` the same ratio for operands stored transposed
 (A as K x M and / or B as N x K) on a few squares.  A candidate with
 `whole_k` (a persistent kernel) is fitted only on the shapes it runs in that
-form: whole tiles, K a multiple of whole_k.
+form: whole tiles, K a multiple of whole_k; its `edge` factor is the median
+ratio of its rate on edge tiles and K past whole rounds (with K rounded up to
+whole rounds) to the rate at the same level.
 
     python -m dense_fp32_gemm_row_amd.tune.autotune --out tuned.json --calibrate
 
@@ -86,6 +88,9 @@ CAL_SHORTK = [(8192, 8192, 64), (8192, 8192, 128), (16384, 16384, 128), (16384, 
 # CAL_SHAPES, for the candidates that take them
 CAL_TRANS = [(2048, 2048, 8192), (4096, 4096, 4096), (6144, 6144, 6144), (8192, 8192, 8192)]
 TRANS_OPS = ("NT", "TN", "TT")
+# edge tiles and K past whole rounds, for persistent candidates (whole_k)
+CAL_EDGE = [(8000, 8000, 8000), (6000, 6000, 6000), (4000, 4000, 4000), (8192, 8192, 8100),
+            (2000, 2000, 6000)]
 
 
 def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dict:
@@ -135,6 +140,24 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
                 print(json.dumps({"calibrate": cfg, "ops": ops, "M": M, "N": N, "K": K,
                                   "median_ms": round(times[(cfg, ops, M, N, K)], 5)}), flush=True)
             del dA, dB, dC
+        torch.cuda.empty_cache()
+    for M, N, K in CAL_EDGE:
+        g = torch.Generator(device="cuda").manual_seed(0)
+        dA = torch.rand((M, K), device="cuda", generator=g)
+        dB = torch.rand((K, N), device="cuda", generator=g)
+        dC = torch.empty((M, N), device="cuda")
+        for cand in model["candidates"]:
+            if not int(cand.get("whole_k", 0)):
+                continue
+            cfg = cand["config"]
+
+            def call(cfg=cfg):
+                binding.gemm(dA, dB, dC, variant="mfma", config=cfg)
+
+            times[(cfg, "edge", M, N, K)] = time_fn(call, budget_ms, blocker)
+            print(json.dumps({"calibrate": cfg, "edge": True, "M": M, "N": N, "K": K,
+                              "median_ms": round(times[(cfg, "edge", M, N, K)], 5)}), flush=True)
+        del dA, dB, dC
         torch.cuda.empty_cache()
     out = {"cus": cus, "candidates": []}
     for cand in model["candidates"]:
@@ -194,10 +217,22 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
                 if (cfg, ops, M, N, K) in times and rated(M, N, K):
                     ms = max(times[(cfg, ops, M, N, K)] - floor, 1e-6)
                     tratios.append(2.0 * bm * bn * (K + k0) * n / (ms * 1e-3) / 1e9 / rates[level - 1])
-        out["candidates"].append({**cand, "gflops_per_cu": [round(r, 1) for r in rates],
-                                  "k0": round(k0, 1),
-                                  "unaligned": round(min(1.0, statistics.median(ratios)), 3) if ratios else 1.0,
-                                  "trans": round(statistics.median(tratios), 3) if tratios else 1.0})
+        # a persistent candidate's edge form (edge tiles, K rounded up to whole
+        # rounds of whole_k): the median ratio of its rate to the rate at the
+        # same level
+        eratios = []
+        for M, N, K in CAL_EDGE:
+            if (cfg, "edge", M, N, K) in times:
+                n, level = share(M, N)
+                kr = -(-K // whole_k) * whole_k
+                ms = max(times[(cfg, "edge", M, N, K)] - floor, 1e-6)
+                eratios.append(2.0 * bm * bn * (kr + k0) * n / (ms * 1e-3) / 1e9 / rates[level - 1])
+        entry = {**cand, "gflops_per_cu": [round(r, 1) for r in rates], "k0": round(k0, 1),
+                 "unaligned": round(min(1.0, statistics.median(ratios)), 3) if ratios else 1.0,
+                 "trans": round(statistics.median(tratios), 3) if tratios else 1.0}
+        if whole_k:
+            entry["edge"] = round(min(1.0, statistics.median(eratios)), 3) if eratios else 1.0
+        out["candidates"].append(entry)
     return out
 
 

@@ -52,7 +52,8 @@ def render(table: dict) -> str:
         "    float unaligned;",
         "    float k0;",
         "    float trans;  // rate factor with a transposed operand",
-        "    int whole_k;  // > 0: rated only for whole tiles, K a multiple of it, no split-K",
+        "    int whole_k;  // > 0: a persistent kernel, whose K runs in rounds of whole_k, no split-K",
+        "    float edge;   // its rate factor on edge tiles or K past whole rounds",
         "};",
         f'constexpr int kModelCUs = {int(table["model"]["cus"])};',
         "constexpr ModelCandidate kModel[] = {",
@@ -64,7 +65,8 @@ def render(table: dict) -> str:
         padded = ", ".join(f"{x:.1f}f" for x in rates + [rates[-1]] * (4 - len(rates)))
         lines.append(f'    {{"{c["config"]}", {int(c["bm"])}, {int(c["bn"])}, {len(rates)}, '
                      f'{{{padded}}}, {float(c["unaligned"]):.3f}f, {float(c.get("k0", 0.0)):.1f}f, '
-                     f'{float(c.get("trans", 1.0)):.3f}f, {int(c.get("whole_k", 0))}}},')
+                     f'{float(c.get("trans", 1.0)):.3f}f, {int(c.get("whole_k", 0))}, '
+                     f'{float(c.get("edge", 1.0)):.3f}f}},')
     lines += [
         "};",
         "}  // namespace gemm_f32_impl",

@@ -736,6 +736,37 @@ def test_persistent_register_direct(kernel, ops):
         assert_exact(to_host(out), oracle.gemm(A, B), f"{name} {ops} {M}x{N}x{K}")
 
 
+# edge tiles and K past whole rounds (K and k-major row lengths multiples of
+# 4; M odd where A is a row operand), K below one chunk, one tile
+PERSISTENT_EDGE_SHAPES = [(300, 260, 132), (301, 1020, 776), (2000, 2052, 388), (128, 132, 4),
+                          (4, 4, 1000), (1028, 128, 128)]
+
+
+@pytest.mark.parametrize("kernel", PERSISTENT, ids=[k[2] for k in PERSISTENT])
+@pytest.mark.parametrize("ops", OPS)
+def test_persistent_register_direct_edges(kernel, ops):
+    """The persistent kernel's edge form: rows past M or N and k past K load
+    as zeros (out-of-range buffer offsets), K rounds up to whole rounds of
+    chunks, stores past M or N are skipped.  Shapes whose transposed operand
+    has a row length that is not a multiple of 4 take the one-launch
+    kernel.  NaN fill around C checks the skipped stores.  Exact on
+    integers."""
+    import torch
+
+    v, c, name = kernel
+    for M, N, K in PERSISTENT_EDGE_SHAPES:
+        log(f"persistent edges {ops} {M}x{N}x{K} on {name}")
+        A, B = make_inputs(M, N, K, "int4", seed=74)
+        big = torch.full((M + 2, N + 3), float("nan"), device="cuda:0")
+        out = big[1:M + 1, 1:N + 1]
+        b.gemm(_stored(A, ops[0]), _stored(B, ops[1]), out, variant=v, config=c)
+        got = to_host(big)
+        assert_exact(np.ascontiguousarray(got[1:M + 1, 1:N + 1]), oracle.gemm(A, B), f"{name} {ops} {M}x{N}x{K}")
+        rest = got.copy()
+        rest[1:M + 1, 1:N + 1] = np.nan
+        assert np.isnan(rest).all(), f"{name} {ops} {M}x{N}x{K}: a store outside C"
+
+
 # (operand, leading dimension): just inside the buffer-offset limit of the
 # persistent kernel (a chunk's byte offsets below 2^31) and just past it,
 # where the launcher takes the one-launch kernel instead
