@@ -473,3 +473,126 @@ def test_persistent_walk_covers_every_tile_once(grid):
                 seen.append(logical)
                 logical += g
         assert sorted(seen) == list(range(total)), (grid, total)
+
+
+# --------------------------------------------------------------------------
+# the persistent register-direct tile's buffer loads (BufOperand), whole and
+# edge forms, restated with numpy over the 64 lanes
+# --------------------------------------------------------------------------
+
+OUT = 1 << 31  # a lane offset past the resource: the load returns zeros
+
+
+def buf_offsets(kmajor, F, il, base, R, ld, K, c, q, edge, kchk):
+    """Lane byte offsets (voffset + soffset) of piece q of chunk c, and for
+    each of the 4 floats of every lane's 16-byte load the operand element
+    (row, k) it stands for; (row-flavour piece q is block q, k-major piece q
+    is k row q, which loads F / 4 pieces)."""
+    lane = np.arange(64)
+    g, i = lane // 16, lane % 16
+    out = []
+    if kmajor:
+        for p in range(0, F, 4):
+            col = base + F * i + p
+            v = np.where(col < R, (4 * g * ld + F * i + p) * 4, OUT) if edge else (4 * g * ld + F * i + p) * 4
+            k = 16 * c + 4 * g + q
+            if edge and kchk:
+                v = np.where(k < K, v, OUT)
+            off = np.where(v >= OUT, OUT, v + q * ld * 4)
+            out.append((off, [(col + e, k) for e in range(4)]))
+    else:
+        r = base + (F * i + q if il else 16 * q + i)
+        v = np.where(r < R, ((r - base) * ld + 4 * g) * 4, OUT) if edge else ((r - base) * ld + 4 * g) * 4
+        if edge and kchk:
+            v = np.where(16 * c < K - 4 * g, v, OUT)
+        out.append((v, [(r, 16 * c + 4 * g + e) for e in range(4)]))
+    return out
+
+
+def persistent_model(M, N, K, lda, ldb, ta, tb, BM=128, BN=128, KG=4, D=2, no_kchk=False):
+    """Every load of the persistent kernel: checks that a load with a lane
+    offset inside the resource reads, for each of its floats, the element
+    its position stands for, inside the operand's storage; that positions
+    past M, N or K read zeros (offset past the resource) or, in the rounds
+    that do not check k, never occur; and that each tile's groups cover every
+    k < K once.  no_kchk: a planted mistake, no round checks k.  Returns
+    the number of loads checked."""
+    whole = M % BM == 0 and N % BN == 0 and K % (16 * KG * D) == 0
+    edge = not whole
+    assert not edge or (K % 4 == 0 and (not ta or M % 4 == 0) and (tb or N % 4 == 0))
+    FM, FN = BM // 16, BN // 16
+    ng = -(-(-(-K // 16)) // (KG * D)) * D if edge else K // 16 // KG
+    # operand: (kmajor, F, interleaved, extent, ld, element index of (row, k), storage floats)
+    opa = (ta, FM, ta, M, lda, (lambda r, k: k * lda + r) if ta else (lambda r, k: r * lda + k),
+           (K - 1) * lda + M if ta else (M - 1) * lda + K)
+    opb = (not tb, FN, True, N, ldb, (lambda r, k: r * ldb + k) if tb else (lambda r, k: k * ldb + r),
+           (N - 1) * ldb + K if tb else (K - 1) * ldb + N)
+    nloads = 0
+    for kg in range(KG):
+        chunk_of = lambda t: kg + KG * t  # noqa: E731
+        t_chk = ng
+        if edge:
+            t_chk = 0
+            while t_chk + D < ng and 16 * chunk_of(t_chk + 2 * D - 1) + 16 <= K:
+                t_chk += D
+        # (chunk, checked): the first D chunks (checked in the edge form), then
+        # round t's loads of chunks t + u + D
+        loads = [(chunk_of(u), edge) for u in range(D)]
+        for t in range(0, ng - D, D):
+            loads += [(chunk_of(t + u + D), edge and t >= t_chk) for u in range(D)]
+        for m0 in range(0, M, BM):
+            for n0 in range(0, N, BN):
+                for (kmajor, F, il, R, ld, index, size), base in ((opa, m0), (opb, n0)):
+                    origin = lambda c: base + 16 * c * ld if kmajor else base * ld + 16 * c  # noqa: E731
+                    for c, kchk in loads:
+                        for q in range(4 if kmajor else F):
+                            for off, elems in buf_offsets(kmajor, F, il, base, R, ld, K, c, q, edge,
+                                                          kchk and not no_kchk):
+                                nloads += 1
+                                for e, (r, k) in enumerate(elems):
+                                    inside = off < OUT
+                                    valid = (r < R) & (k < K)
+                                    # a position past M, N or K reads zeros
+                                    assert not np.any(inside & ~valid), (kmajor, c, q, e)
+                                    idx = origin(c) + off // 4 + e
+                                    want = index(r, k)
+                                    assert np.all(np.where(inside, idx == want, True)), (kmajor, c, q, e)
+                                    assert np.all(np.where(inside, (idx >= 0) & (idx < size), True))
+                                    assert np.all(np.where(inside, off + 4 * e < (1 << 31), True))
+                                    # a valid position is loaded (not zero-filled)
+                                    assert np.all(np.where(valid, inside, True)), (kmajor, c, q, e)
+    chunks = [kg + KG * t for kg in range(KG) for t in range(ng)]
+    assert sorted(16 * c + j for c in chunks for j in range(16) if 16 * c + j < K) == list(range(K))
+    return nloads
+
+
+PERSISTENT_BUF_SHAPES = [  # M, N, K, ld pads
+    (128, 128, 128, 0, 0), (256, 128, 384, 4, 8), (130, 132, 100, 0, 0), (300, 260, 388, 3, 0),
+    (4, 4, 20, 0, 0), (128, 132, 4, 0, 4), (129, 256, 256, 0, 0)]
+
+
+@pytest.mark.parametrize("ops", ["NN", "NT", "TN", "TT"])
+def test_persistent_buffer_loads(ops):
+    """The persistent tile's buffer loads, whole and edge forms: in-range
+    lanes read their own element inside the operand, positions past M, N or
+    K read zeros through an offset past the resource, and the groups cover
+    every k once.  Shapes the edge form does not take (K, or a k-major row
+    length, not a multiple of 4) are skipped, as the launcher skips them."""
+    ta, tb = ops[0] == "T", ops[1] == "T"
+    ran = 0
+    for M, N, K, pa, pb in PERSISTENT_BUF_SHAPES:
+        whole = M % 128 == 0 and N % 128 == 0 and K % 128 == 0
+        if not whole and not (K % 4 == 0 and (not ta or M % 4 == 0) and (tb or N % 4 == 0)):
+            continue
+        lda = (M if ta else K) + pa
+        ldb = (K if tb else N) + pb
+        ran += persistent_model(M, N, K, lda, ldb, ta, tb) > 0
+    assert ran >= 5
+
+
+def test_persistent_buffer_model_sees_an_unchecked_tail():
+    """The model fails if no round checked k: a K that is not whole rounds
+    then has loads of k past K from memory."""
+    persistent_model(128, 128, 100, 100, 128, False, False)
+    with pytest.raises(AssertionError):
+        persistent_model(128, 128, 100, 100, 128, False, False, no_kchk=True)
