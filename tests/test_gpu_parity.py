@@ -803,10 +803,12 @@ def test_persistent_register_direct_far_rows(kernel, operand, ld):
 
 
 @pytest.mark.parametrize("kernel", PERSISTENT, ids=[k[2] for k in PERSISTENT])
-def test_persistent_register_direct_batched(kernel):
-    """Three products of 512 x 640 x 384 in one persistent launch (tiles of
-    all products on one walk), C rows padded, B shared (stride 0)."""
-    M, N, K, nb = 512, 640, 384, 3
+@pytest.mark.parametrize("shape", [(512, 640, 384), (300, 260, 132)], ids=["whole", "edges"])
+def test_persistent_register_direct_batched(kernel, shape):
+    """Three products in one persistent launch (tiles of all products on one
+    walk), whole tiles or the edge form, C rows padded, B shared (stride
+    0)."""
+    (M, N, K), nb = shape, 3
     rng = np.random.default_rng(72)
     lda, ldb, ldc = K, N, N + 3
     sa, sb, sc = M * lda + 5, 0, M * ldc + 7
