@@ -526,8 +526,9 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Persistent form of the register-direct tile for whole tiles and K a
-// multiple of 16 KG D: one workgroup per CU walks the tiles blockIdx.x +
+// Persistent form of the register-direct tile (whole tiles and K a multiple
+// of 16 KG D; the EDGE form takes the rest): one workgroup per CU walks the
+// tiles blockIdx.x +
 // j gridDim.x (through the same XCD-aware, grouped order as the one-launch
 // grid), and the last D chunks of a tile load the next tile's first D
 // chunks into their register sets.  The next tile's loads are thus in
