@@ -706,6 +706,10 @@ template <int BM, int BN, int WM, int WN, int KG, int D, int OCC, bool ET, bool 
 hipError_t launch_regs(const Problem &p, hipStream_t stream) {
     constexpr int NT = 64 * WM * WN * KG;
     constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
+    // A transposed (k-major) needs loads of FM whole floats: FM of 1, 2 or a
+    // multiple of 4 (configurations with other FM take row-major A only)
+    constexpr bool kTransA = FM <= 2 || FM % 4 == 0;
+    if (p.ta && !kTransA) return hipErrorInvalidValue;
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
     const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * p.batch;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -740,10 +744,12 @@ hipError_t launch_regs(const Problem &p, hipStream_t stream) {
         if (whole_p) GEMM_REGS_P1(TA_, TB_, false);      \
         else GEMM_REGS_P1(TA_, TB_, true);               \
     } while (0)
-            if (p.ta && p.tb) GEMM_REGS_P(true, true);
-            else if (p.tb) GEMM_REGS_P(false, true);
-            else if (p.ta) GEMM_REGS_P(true, false);
-            else GEMM_REGS_P(false, false);
+            if constexpr (FM % 4 == 0) {
+                if (p.ta && p.tb) GEMM_REGS_P(true, true);
+                else if (p.ta) GEMM_REGS_P(true, false);
+            }
+            if (p.tb && !p.ta) GEMM_REGS_P(false, true);
+            else if (!p.ta) GEMM_REGS_P(false, false);
 #undef GEMM_REGS_P
 #undef GEMM_REGS_P1
             return hipGetLastError();
@@ -759,10 +765,12 @@ hipError_t launch_regs(const Problem &p, hipStream_t stream) {
         else if (edge == 2) GEMM_REGS(TA_, TB_, 2); \
         else if constexpr (WHOLE) GEMM_REGS(TA_, TB_, 0); \
     } while (0)
-    if (p.ta && p.tb) GEMM_REGS_E(true, true);
-    else if (p.ta) GEMM_REGS_E(true, false);
-    else if (p.tb) GEMM_REGS_E(false, true);
-    else GEMM_REGS_E(false, false);
+    if constexpr (kTransA) {
+        if (p.ta && p.tb) GEMM_REGS_E(true, true);
+        else if (p.ta) GEMM_REGS_E(true, false);
+    }
+    if (p.tb && !p.ta) GEMM_REGS_E(false, true);
+    else if (!p.ta) GEMM_REGS_E(false, false);
 #undef GEMM_REGS_E
 #undef GEMM_REGS
     return hipGetLastError();
@@ -789,6 +797,8 @@ const ConfigEntry kRegsConfigs[] = {
     // persistent where the shape allows (one workgroup per CU walks its
     // tiles; for the 64 x 64 tile it gained nothing)
     {"mfmag_128x128x64_w1x1_k4_d2_p", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8, true>, kCapTransposed},
+    // 96 x 128 (A row-major only): 768 tiles at 3072^3, three rounds of 256
+    {"mfmag_96x128x64_w1x1_k4_d2_p", launch_regs<96, 128, 1, 1, 4, 2, 1, true, false, 8, true>, 0},
 };
 
 }  // namespace

@@ -83,7 +83,8 @@ CAL_UNALIGNED = [(1000, 1023, 7777), (2049, 2049, 2049), (3001, 3001, 3001), (40
                  (8192, 8192, 2047)]
 # short K and many output tiles: where a tile's fixed cost (its prologue, and
 # the stores of C that no other workgroup's math hides) shows
-CAL_SHORTK = [(8192, 8192, 64), (8192, 8192, 128), (16384, 16384, 128), (16384, 16384, 256)]
+CAL_SHORTK = [(8192, 8192, 64), (8192, 8192, 128), (16384, 16384, 128), (16384, 16384, 256),
+              (6144, 8192, 128)]
 # transposed operands (A stored K x M and/or B stored N x K) on shapes of
 # CAL_SHAPES, for the candidates that take them
 CAL_TRANS = [(2048, 2048, 8192), (4096, 4096, 4096), (6144, 6144, 6144), (8192, 8192, 8192)]
@@ -196,7 +197,7 @@ def calibrate_model(binding, model: dict, budget_ms: float, blocker=None) -> dic
                 n, level = share(M, N)
                 ms = max(times[(cfg, M, N, K)] - floor, 1e-6)
                 extra.append(ms * 1e-3 * rates[level - 1] * 1e9 / (n * 2.0 * bm * bn) - K)
-            return max(0.0, statistics.median(extra))
+            return max(0.0, statistics.median(extra)) if extra else float(cand.get("k0", 0.0))
 
         k0 = fit_k0(fit_rates(0.0))
         rates = fit_rates(k0)

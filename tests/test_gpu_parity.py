@@ -714,11 +714,13 @@ def test_splitk_slices_not_whole_k_steps(kernel, lda_pad):
 
 
 PERSISTENT = [(3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n.startswith("mfmag") and n.endswith("_p")]
+# (kernel, operand forms): configurations without transposed operands run NN only
+PERSISTENT_OPS = [(k, ops) for k in PERSISTENT for ops in (OPS if k[2] in TRANS_CAPABLE else ["NN"])]
+PERSISTENT_OPS_IDS = [f"{k[2]}-{ops}" for k, ops in PERSISTENT_OPS]
 PERSISTENT_SHAPES = [(256, 256, 384), (2048, 2304, 384), (1280, 4096, 768)]
 
 
-@pytest.mark.parametrize("kernel", PERSISTENT, ids=[k[2] for k in PERSISTENT])
-@pytest.mark.parametrize("ops", OPS)
+@pytest.mark.parametrize("kernel,ops", PERSISTENT_OPS, ids=PERSISTENT_OPS_IDS)
 def test_persistent_register_direct(kernel, ops):
     """The persistent register-direct kernel runs whole tiles with K a
     multiple of 128 (16 k x 4 groups x 2 chunks in flight), every operand
@@ -742,8 +744,7 @@ PERSISTENT_EDGE_SHAPES = [(300, 260, 132), (301, 1020, 776), (2000, 2052, 388), 
                           (4, 4, 1000), (1028, 128, 128)]
 
 
-@pytest.mark.parametrize("kernel", PERSISTENT, ids=[k[2] for k in PERSISTENT])
-@pytest.mark.parametrize("ops", OPS)
+@pytest.mark.parametrize("kernel,ops", PERSISTENT_OPS, ids=PERSISTENT_OPS_IDS)
 def test_persistent_register_direct_edges(kernel, ops):
     """The persistent kernel's edge form: rows past M or N and k past K load
     as zeros (out-of-range buffer offsets), K rounds up to whole rounds of
@@ -774,9 +775,12 @@ PERSISTENT_FAR = [("A", 1 << 21), ("A", (1 << 21) + (1 << 17)), ("AT", (1 << 24)
                   ("B", 1 << 24), ("B", (1 << 24) + (1 << 21)), ("BT", 1 << 21)]
 
 
-@pytest.mark.parametrize("kernel", PERSISTENT, ids=[k[2] for k in PERSISTENT])
-@pytest.mark.parametrize("operand,ld", PERSISTENT_FAR,
-                         ids=[f"{o}_ld{ld}" for o, ld in PERSISTENT_FAR])
+PERSISTENT_FAR_CASES = [(k, o, ld) for k in PERSISTENT for o, ld in PERSISTENT_FAR
+                        if k[2] in TRANS_CAPABLE or o in ("A", "B")]
+
+
+@pytest.mark.parametrize("kernel,operand,ld", PERSISTENT_FAR_CASES,
+                         ids=[f"{k[2]}-{o}_ld{ld}" for k, o, ld in PERSISTENT_FAR_CASES])
 def test_persistent_register_direct_far_rows(kernel, operand, ld):
     """Whole 128 x 128 x 256 products with one operand's rows (or k rows)
     far apart: byte offsets within a chunk near 2^30 on the buffer-load
