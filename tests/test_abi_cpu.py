@@ -153,7 +153,8 @@ def test_cost_model_choices(lib):
     """The cost model's choice on shapes not in the table: small products
     get small tiles, a product that fills the chip many times over the
     largest tile, and wave quantisation is accounted for (3072^3: 144 tiles
-    of 256^2 would leave 112 CUs idle)."""
+    of 256^2 would leave 112 CUs idle, 576 of 128^2 a quarter-full round;
+    96 x 128 tiles make three whole rounds, 64^2 nine)."""
     def pick(M, N, K, lda=None, ldb=None):
         v, c = b.gemm_f32_select(M, N, K, lda or K, ldb or N, N)
         return b.gemm_f32_config_name(v, c)
@@ -168,7 +169,8 @@ def test_cost_model_choices(lib):
     # register-direct tile
     assert pick(8192, 8192, 8192 + 64) in {"mfma2d_256x256x32_w4x4_swz_g4_il",
                                            "mfmag_128x128x64_w1x1_k4_d2_p"}
-    assert tile(pick(3072, 3072, 3072)) <= 64 * 64
+    bm, bn = (int(x) for x in pick(3072, 3072, 3072).split("_")[1].split("x")[:2])
+    assert ((3072 // bm) * (3072 // bn)) % 256 == 0
     # 8192 x 1024: a tile that fills whole waves of the 256 CUs (256 tiles of
     # 256 x 128 or 128 x 256, or 512 of 128 x 128), none with a part-empty wave
     bm, bn = (int(x) for x in pick(8192, 1024, 4096).split("_")[1].split("x")[:2])
@@ -372,7 +374,7 @@ def test_split_plans(lib):
     def plan(M, N, K):
         return b.gemm_f32_plan(M, N, K, max(K, 1), N, N)
 
-    for M, N, K in [(3584, 3584, 3584), (4608, 4608, 4608), (3000, 3000, 1000), (2048, 5632, 8192)]:
+    for M, N, K in [(3584, 3584, 3584), (5120, 5120, 5120), (7168, 7168, 7168), (2048, 5632, 8192)]:
         p = plan(M, N, K)
         assert p["parts"] == 2, (M, N, K, p)
         name = b.gemm_f32_config_name(*p["configs"][0])
