@@ -957,7 +957,7 @@ def test_splitk_one_split_is_plain_product():
 # full-size workloads in the benchmark's launch configuration
 # --------------------------------------------------------------------------
 
-SPLIT_SHAPES = [(3584, 3584, 3584), (3000, 3000, 1000), (4607, 4609, 1001), (1800, 9000, 1024)]
+SPLIT_SHAPES = [(3584, 3584, 3584), (3300, 3300, 1000), (4607, 4609, 1001), (1800, 9000, 1024)]
 
 
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=["x".join(map(str, s)) for s in SPLIT_SHAPES])
