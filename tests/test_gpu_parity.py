@@ -861,21 +861,24 @@ def test_prepared_call_matches_gemm():
         assert np.array_equal(to_host(out).view(np.uint32), ref.view(np.uint32)), kw
 
 
-@pytest.mark.parametrize("case", ["select", "k4", "splitk"])
+@pytest.mark.parametrize("case", ["select", "k4", "splitk", "persistent", "persistent_edge"])
 def test_graph_capture_replays(case):
     """A library call captured in a HIP graph (torch.cuda.CUDAGraph on a side
     stream) replays correctly: three replays, with eager work between them
     that changes A in place, each checked bit for bit against an eager call
     on the same inputs, and the last against the oracle.  The shape has no
-    16-byte-aligned rows (4-byte direct loads) and ragged tiles."""
+    16-byte-aligned rows (4-byte direct loads) and ragged tiles; the
+    persistent register-direct tile runs whole tiles and its edge form."""
     import torch
 
-    M, N, K = 300, 277, 1029
+    M, N, K = {"persistent": (512, 640, 384), "persistent_edge": (300, 260, 132)}.get(case, (300, 277, 1029))
     A, B = make_inputs(M, N, K, "int4", seed=60)
     dA, dB = to_dev(A), to_dev(B)
     out = torch.full((M, N), float("nan"), device="cuda:0")
     ref = torch.empty((M, N), device="cuda:0")
     kw = {"variant": "mfma", "config": "mfma4d_64x64x64_w2x2_k4_swz"} if case == "k4" else {}
+    if case.startswith("persistent"):
+        kw = {"variant": "mfma", "config": "mfmag_128x128x64_w1x1_k4_d2_p"}
     if case == "splitk":
         need = b.gemm_f32_splitk_workspace_size(M, N, K, 3)
         work = torch.empty(need // 4, device="cuda:0")
