@@ -797,8 +797,10 @@ const ConfigEntry kRegsConfigs[] = {
     // persistent where the shape allows (one workgroup per CU walks its
     // tiles; for the 64 x 64 tile it gained nothing)
     {"mfmag_128x128x64_w1x1_k4_d2_p", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8, true>, kCapTransposed},
-    // 96 x 128 (A row-major only): 768 tiles at 3072^3, three rounds of 256
-    {"mfmag_96x128x64_w1x1_k4_d2_p", launch_regs<96, 128, 1, 1, 4, 2, 1, true, false, 8, true>, 0},
+    // 96 x 128 (A as stored, B as stored or transposed): 768 tiles at
+    // 3072^3, three rounds of 256
+    {"mfmag_96x128x64_w1x1_k4_d2_p", launch_regs<96, 128, 1, 1, 4, 2, 1, true, false, 8, true>,
+     kCapTransposedB},
 };
 
 }  // namespace
