@@ -239,8 +239,7 @@ double model_us(const ModelCandidate &m, int64_t batch, int64_t M, int64_t N, in
 constexpr int kModelSize = static_cast<int>(sizeof(kModel) / sizeof(kModel[0]));
 struct ModelIds {
     int id[kModelSize];
-    bool trans[kModelSize];   // transposed A and/or B
-    bool transb[kModelSize];  // transposed B
+    bool trans[kModelSize];
 };
 const ModelIds &model_ids() {
     static const ModelIds ids = [] {
@@ -250,7 +249,6 @@ const ModelIds &model_ids() {
         for (int i = 0; i < kModelSize; ++i) {
             r.id[i] = find_config(GEMM_F32_VARIANT_MFMA, kModel[i].config);
             r.trans[i] = r.id[i] >= 0 && (cfgs[r.id[i]].caps & kCapTransposed);
-            r.transb[i] = r.id[i] >= 0 && (cfgs[r.id[i]].caps & (kCapTransposed | kCapTransposedB));
         }
         return r;
     }();
@@ -266,16 +264,17 @@ unsigned ops_of(bool ta, bool tb) {
 // A candidate with whole_k > 0 (a persistent kernel) is rated only for the
 // products it runs in that form: no split-K slices, and whole tiles with K a
 // multiple of whole_k, or (its edge form) K and the row length of a k-major
-// operand (M for A transposed, N for B as stored) multiples of 4.
+// operand (M for A transposed, N for B as stored) multiples of 4, for tiles
+// whose k-major loads come in groups of 4 (bm, bn multiples of 64).
 bool usable(int i, unsigned ops, int64_t M, int64_t N, int64_t K) {
     const ModelIds &ids = model_ids();
-    if (ids.id[i] < 0 || ((ops & kOpsTransA) && !ids.trans[i]) || ((ops & kOpsTransB) && !ids.transb[i]))
-        return false;
+    if (ids.id[i] < 0 || ((ops & kOpsTrans) && !ids.trans[i])) return false;
     const ModelCandidate &m = kModel[i];
     if (m.whole_k == 0) return true;
     if ((ops & kOpsSplitK) || K <= 0) return false;
     const bool whole = M % m.bm == 0 && N % m.bn == 0 && K % m.whole_k == 0;
-    const bool edge = K % 4 == 0 && (!(ops & kOpsTransA) || M % 4 == 0) && ((ops & kOpsTransB) || N % 4 == 0);
+    const bool edge = K % 4 == 0 && (!(ops & kOpsTransA) || (M % 4 == 0 && m.bm % 64 == 0)) &&
+                      ((ops & kOpsTransB) || (N % 4 == 0 && m.bn % 64 == 0));
     return whole || edge;
 }
 
@@ -457,9 +456,8 @@ int run(int variant, int config_id, bool ta, bool tb, int64_t batch, int64_t M, 
                         ++config_id;
             }
         }
-        const unsigned caps = cfgs[config_id].caps;
-        if ((ta && !(caps & kCapTransposed)) || (tb && !(caps & (kCapTransposed | kCapTransposedB))))
-            return fail(GEMM_F32_ENOKERNEL, "configuration %s does not take these transposed operands",
+        if ((ta || tb) && !(cfgs[config_id].caps & kCapTransposed))
+            return fail(GEMM_F32_ENOKERNEL, "configuration %s does not take transposed operands",
                         cfgs[config_id].name);
         const Problem p{static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), A, lda, B,
                         ldb, C, ldc, static_cast<int>(batch), sa, sb, sc, ta, tb};

@@ -47,7 +47,6 @@ using LaunchFn = hipError_t (*)(const Problem &, hipStream_t);
 
 // Capabilities of a configuration beyond plain row-major operands.
 constexpr unsigned kCapTransposed = 1u;  // accepts transposed A and/or B
-constexpr unsigned kCapTransposedB = 2u;  // accepts a transposed B (A as stored)
 
 struct ConfigEntry {
     const char *name;  // stable, used by the tuning table and benchmarks

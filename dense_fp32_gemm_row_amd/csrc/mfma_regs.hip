@@ -56,11 +56,14 @@
 
 #include "mfma_kernels.h"
 
-// Buffer load of 16 bytes: the resource's base plus a lane offset (bytes,
-// plus the instruction's constant offset) plus a scalar offset.
+// Buffer loads of 16 and 8 bytes: the resource's base plus a lane offset
+// (bytes, plus the instruction's constant offset) plus a scalar offset.
 __device__ gemm_f32_impl::floatx4 gemm_f32_buffer_load_x4(__amdgpu_buffer_rsrc_t rsrc, int voffset,
                                                           int soffset, int aux)
     __asm("llvm.amdgcn.raw.ptr.buffer.load.v4f32");
+__device__ float __attribute__((ext_vector_type(2))) gemm_f32_buffer_load_x2(
+    __amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.load.v2f32");
 
 namespace gemm_f32_impl {
 namespace {
@@ -71,16 +74,16 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 // 16-byte piece, which global memory accepts at any 4-byte alignment.
 template <int N>
 __device__ __forceinline__ void load_run(const float *q, float (&v)[N]) {
-    if constexpr (N >= 4) {
+    static_assert(N == 1 || N % 2 == 0, "runs of 1 or an even number of floats");
 #pragma unroll
-        for (int p = 0; p < N; p += 4) {
-            const floatx4 t = floatx4{q[p], q[p + 1], q[p + 2], q[p + 3]};
-            v[p] = t[0], v[p + 1] = t[1], v[p + 2] = t[2], v[p + 3] = t[3];
-        }
-    } else if constexpr (N == 2) {
-        const floatx2 t = floatx2{q[0], q[1]};
-        v[0] = t[0], v[1] = t[1];
-    } else {
+    for (int p = 0; p + 4 <= N; p += 4) {
+        const floatx4 t = floatx4{q[p], q[p + 1], q[p + 2], q[p + 3]};
+        v[p] = t[0], v[p + 1] = t[1], v[p + 2] = t[2], v[p + 3] = t[3];
+    }
+    if constexpr (N % 4 == 2) {  // the last two: one 8-byte load
+        const floatx2 t = floatx2{q[N - 2], q[N - 1]};
+        v[N - 2] = t[0], v[N - 1] = t[1];
+    } else if constexpr (N == 1) {
         v[0] = q[0];
     }
 }
@@ -201,16 +204,19 @@ struct RegOperand {
 // origin is a scalar resource, a lane's place in the chunk a 32-bit byte
 // offset fixed for the tile, and a k row's distance a scalar offset, so a
 // load of a whole tile takes no vector address arithmetic.  Same layout and
-// lane mapping as RegOperand; k-major operands take F >= 4 (16-byte loads).
+// lane mapping as RegOperand; a k-major operand's F floats of one k row go
+// in 16-byte loads and, for F = 4 n + 2, one 8-byte load.
 // Offsets stay below 2^31 bytes: the launcher checks (rows - 1) ld + 16
 // (row flavour) and 15 ld + rows (k-major) against 2^28 floats.
 // EDGE: rows past R and k past K read as zeros: their offset is 2^31, past
 // the resource's 2^31 - 1 bytes, and an out-of-range buffer load returns 0.
 // Whole rows (row flavour) or groups of 4 (k-major) are in or out: K, and
-// R of a k-major operand, are multiples of 4 (the launcher checks).
+// R of a k-major operand, are multiples of 4, and F of a k-major operand
+// too (the launcher checks).
 template <bool KMAJOR, int F, bool IL, bool EDGE = false>
 struct BufOperand {
-    static_assert(!KMAJOR || (IL && F % 4 == 0), "k-major operands: interleaved, 16-byte pieces");
+    static_assert(!KMAJOR || (IL && F % 2 == 0), "k-major operands: interleaved, 16- and 8-byte pieces");
+    static_assert(!(KMAJOR && EDGE) || F % 4 == 0, "edge form: k-major groups of 4");
     static constexpr bool kKMajor = KMAJOR;
     static constexpr int kPieces = KMAJOR ? 4 : F;
     static constexpr int kOut = static_cast<int>(0x80000000u);  // an offset past the resource
@@ -256,10 +262,14 @@ struct BufOperand {
         if constexpr (KMAJOR) {
             const bool kin = !kc || c * 16 + q < klim;
 #pragma unroll
-            for (int p = 0; p < F; p += 4) {
+            for (int p = 0; p + 4 <= F; p += 4) {
                 const int v = EDGE ? voff[p / 4] : voff[0] + 4 * p;
                 const floatx4 t = gemm_f32_buffer_load_x4(rs, kin ? v : kOut, q * ld * 4, 0);
                 x[p][q] = t[0], x[p + 1][q] = t[1], x[p + 2][q] = t[2], x[p + 3][q] = t[3];
+            }
+            if constexpr (F % 4 == 2) {  // whole tiles only (no EDGE)
+                const auto t = gemm_f32_buffer_load_x2(rs, voff[0] + 4 * (F - 2), q * ld * 4, 0);
+                x[F - 2][q] = t[0], x[F - 1][q] = t[1];
             }
         } else {
             const int o = kc && c * 16 >= klim ? kOut : voff[q];
@@ -706,9 +716,9 @@ template <int BM, int BN, int WM, int WN, int KG, int D, int OCC, bool ET, bool 
 hipError_t launch_regs(const Problem &p, hipStream_t stream) {
     constexpr int NT = 64 * WM * WN * KG;
     constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
-    // A transposed (k-major) needs loads of FM whole floats: FM of 1, 2 or a
-    // multiple of 4 (configurations with other FM take row-major A only)
-    constexpr bool kTransA = FM <= 2 || FM % 4 == 0;
+    // A transposed (k-major) is loaded in runs of FM floats: FM of 1 or even
+    // (configurations with other FM take A as stored only)
+    constexpr bool kTransA = FM == 1 || FM % 2 == 0;
     if (p.ta && !kTransA) return hipErrorInvalidValue;
     const int tiles_m = ceil_div(p.M, BM), tiles_n = ceil_div(p.N, BN);
     const int64_t grid = static_cast<int64_t>(tiles_m) * tiles_n * p.batch;
@@ -728,7 +738,8 @@ hipError_t launch_regs(const Problem &p, hipStream_t stream) {
         const bool buf_ok = (p.ta ? 15 * p.lda + BM : (BM - 1) * p.lda + 16) < (int64_t{1} << 28) &&
                             (p.tb ? (BN - 1) * p.ldb + 16 : 15 * p.ldb + BN) < (int64_t{1} << 28);
         const bool whole_p = p.M % BM == 0 && p.N % BN == 0 && p.K % (16 * KG * D) == 0;
-        const bool edge_p = p.K % 4 == 0 && (!p.ta || p.M % 4 == 0) && (p.tb || p.N % 4 == 0);
+        const bool edge_p = p.K % 4 == 0 && (!p.ta || (p.M % 4 == 0 && FM % 4 == 0)) &&
+                            (p.tb || (p.N % 4 == 0 && FN % 4 == 0));
         if (p.ksplit == 0 && buf_ok && p.K > 0 && (whole_p || edge_p)) {
             int dev = 0, cus = 0;
             hipError_t e = hipGetDevice(&dev);
@@ -739,12 +750,13 @@ hipError_t launch_regs(const Problem &p, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_mfma_regs_persistent_kernel<BM, BN, KG, D, TA_, TB_, E>), dim3(wgs), bd, 0, \
                        stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,     \
                        GROUP_M, batch_of(p))
-#define GEMM_REGS_P(TA_, TB_)                            \
-    do {                                                 \
-        if (whole_p) GEMM_REGS_P1(TA_, TB_, false);      \
-        else GEMM_REGS_P1(TA_, TB_, true);               \
+#define GEMM_REGS_P(TA_, TB_)                                                          \
+    do {                                                                               \
+        if (whole_p) GEMM_REGS_P1(TA_, TB_, false);                                    \
+        else if constexpr ((!TA_ || FM % 4 == 0) && (TB_ || FN % 4 == 0))             \
+            GEMM_REGS_P1(TA_, TB_, true);                                              \
     } while (0)
-            if constexpr (FM % 4 == 0) {
+            if constexpr (kTransA) {
                 if (p.ta && p.tb) GEMM_REGS_P(true, true);
                 else if (p.ta) GEMM_REGS_P(true, false);
             }
@@ -797,10 +809,11 @@ const ConfigEntry kRegsConfigs[] = {
     // persistent where the shape allows (one workgroup per CU walks its
     // tiles; for the 64 x 64 tile it gained nothing)
     {"mfmag_128x128x64_w1x1_k4_d2_p", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8, true>, kCapTransposed},
-    // 96 x 128 (A as stored, B as stored or transposed): 768 tiles at
-    // 3072^3, three rounds of 256
+    // 96 x 128: 768 tiles at 3072^3, three rounds of 256 (its edge form
+    // takes A as stored; a transposed A runs whole tiles persistent, the
+    // rest one launch per tile)
     {"mfmag_96x128x64_w1x1_k4_d2_p", launch_regs<96, 128, 1, 1, 4, 2, 1, true, false, 8, true>,
-     kCapTransposedB},
+     kCapTransposed},
 };
 
 }  // namespace

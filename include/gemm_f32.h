@@ -182,8 +182,7 @@ int gemm_f32_strided_batched_variant(int variant, int config_id,
  *   variant, config_id   -1, -1 for the library's choice, else as in
  *                        gemm_f32_variant.  Transposed operands are taken by
  *                        the naive kernel and by the MFMA configurations
- *                        that list them (some take a transposed B only);
- *                        others return GEMM_F32_ENOKERNEL.
+ *                        that list them; others return GEMM_F32_ENOKERNEL.
  *   batch, strides       as in gemm_f32_strided_batched (batch 1, strides 0
  *                        for one product).
  *

@@ -572,10 +572,8 @@ TRANS_CAPABLE = ["mfma2d_256x256x32_w4x4_swz", "mfma3d_256x128x32_w4x2_swz",
                  "mfma3_256x256x16_w4x4_swz_g4_il", "mfma2_64x64x64_w2x2_k4_swz",
                  "mfma2d_128x128x32_w2x2_swz_il", "mfma2r_64x64x64_w2x2_k4_swz",
                  "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2",
-                 "mfmag_128x128x64_w1x1_k4_d2_p"] + [
+                 "mfmag_128x128x64_w1x1_k4_d2_p", "mfmag_96x128x64_w1x1_k4_d2_p"] + [
     n for n in CONFIG_IDS if "_m16" in n]  # every 16x16x4 configuration takes them
-# configurations that take a transposed B with A as stored only
-TRANSB_CAPABLE = ["mfmag_96x128x64_w1x1_k4_d2_p"]
 TRANS_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in TRANS_CAPABLE]
 OPS = ["NN", "NT", "TN", "TT"]
@@ -630,27 +628,16 @@ def test_transposed_batched(ops):
 
 def test_transposed_rejected_where_unsupported():
     """Configurations without transposed operands reject them with
-    ENOKERNEL; those that take a transposed B only reject a transposed A
-    and run a transposed B (exact on integers)."""
+    ENOKERNEL."""
     import torch
 
     A = torch.ones((64, 64), device="cuda:0")
     for v, c, name in ALL_CONFIGS:
         if v in (1, 2) or (v == 3 and name not in TRANS_CAPABLE):
-            with pytest.raises(b.GemmError) as e:
-                b.gemm(A.T, A, variant=v, config=c)
-            assert e.value.code == b.GEMM_F32_ENOKERNEL, name
-        if v in (1, 2) or (v == 3 and name not in TRANS_CAPABLE + TRANSB_CAPABLE):
-            with pytest.raises(b.GemmError) as e:
-                b.gemm(A, A.T, variant=v, config=c)
-            assert e.value.code == b.GEMM_F32_ENOKERNEL, name
-    for v, c, name in ALL_CONFIGS:
-        if name in TRANSB_CAPABLE:
-            for M, N, K in [(300, 277, 129), (384, 512, 256)]:
-                X, Y = make_inputs(M, N, K, "int4", seed=75)
-                out = torch.full((M, N), float("nan"), device="cuda:0")
-                b.gemm(to_dev(X), _stored(Y, "T"), out, variant=v, config=c)
-                assert_exact(to_host(out), oracle.gemm(X, Y), f"{name} NT {M}x{N}x{K}")
+            for X, Y in ((A.T, A), (A, A.T)):
+                with pytest.raises(b.GemmError) as e:
+                    b.gemm(X, Y, variant=v, config=c)
+                assert e.value.code == b.GEMM_F32_ENOKERNEL, name
 
 
 # --------------------------------------------------------------------------
@@ -731,9 +718,7 @@ def test_splitk_slices_not_whole_k_steps(kernel, lda_pad):
 
 PERSISTENT = [(3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n.startswith("mfmag") and n.endswith("_p")]
 # (kernel, operand forms): configurations without transposed operands run NN only
-PERSISTENT_OPS = [(k, ops) for k in PERSISTENT
-                  for ops in (OPS if k[2] in TRANS_CAPABLE else ["NN", "NT"] if k[2] in TRANSB_CAPABLE
-                              else ["NN"])]
+PERSISTENT_OPS = [(k, ops) for k in PERSISTENT for ops in (OPS if k[2] in TRANS_CAPABLE else ["NN"])]
 PERSISTENT_OPS_IDS = [f"{k[2]}-{ops}" for k, ops in PERSISTENT_OPS]
 PERSISTENT_SHAPES = [(256, 256, 384), (2048, 2304, 384), (1280, 4096, 768)]
 
@@ -794,7 +779,7 @@ PERSISTENT_FAR = [("A", 1 << 21), ("A", (1 << 21) + (1 << 17)), ("AT", (1 << 24)
 
 
 PERSISTENT_FAR_CASES = [(k, o, ld) for k in PERSISTENT for o, ld in PERSISTENT_FAR
-                        if k[2] in TRANS_CAPABLE or o in ("A", "B") or (o == "BT" and k[2] in TRANSB_CAPABLE)]
+                        if k[2] in TRANS_CAPABLE or o in ("A", "B")]
 
 
 @pytest.mark.parametrize("kernel,operand,ld", PERSISTENT_FAR_CASES,
