@@ -43,10 +43,13 @@
 //
 // A persistent form of the kernel (one workgroup per CU walking its tiles,
 // each tile's last chunks loading the next tile's first ones) serves whole
-// tiles with K a multiple of 16 KG D, in every operand form.  It loads the
-// operands as buffers (a scalar resource per chunk, a lane offset fixed per
-// tile, a scalar offset per k row: no vector address arithmetic), each piece
-// right after the last instruction that reads the registers it refills.
+// tiles with K a multiple of 16 KG D, in every operand form, and in an edge
+// form the other shapes whose K and k-major row lengths are multiples of 4
+// (positions past M, N or K read zeros: their buffer offset lies past the
+// resource).  It loads the operands as buffers (a scalar resource per chunk,
+// a lane offset fixed per tile, a scalar offset per k row: no vector address
+// arithmetic), each piece right after the last instruction that reads the
+// registers it refills.
 //
 // Roofline: MFMA bound per chunk (4 FM FN instructions of 32 cycles per
 // FM + 4 loads, or fewer); the tile's fixed cost (first loads, the k-group
