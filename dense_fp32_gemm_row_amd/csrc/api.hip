@@ -86,11 +86,12 @@ int split_len(int64_t K, int64_t want, int64_t *used) {
     return static_cast<int>(len);
 }
 
-// Library choice of the number of K splits: enough 256 x 256 tiles to give
+// Library choice of the number of K splits: enough 128 x 128 tiles (the
+// persistent register-direct tile that takes slices of equal length) to give
 // every CU one, with at least 1024 k per split.
 int64_t auto_splits(int64_t M, int64_t N, int64_t K) {
     constexpr int64_t kCUs = 256;
-    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     int64_t s = (kCUs + tiles - 1) / tiles;
     const int64_t by_k = K / 1024;
     if (s > by_k) s = by_k;
@@ -521,13 +522,16 @@ int splitk(int variant, int config_id, int64_t splits, int64_t M, int64_t N, int
     int v = variant, c = config_id;
     const bool aligned = direct_fast(
         operands_aligned(A, lda, len, B, ldb, static_cast<int64_t>(len) * ldb), M, N, false, false);
-    if (v == -1) select_config(used, M, N, len, &v, &c, kOpsSplitK, aligned);
+    // slices of equal length are a plain batch to the model (a persistent
+    // candidate then takes them); a shorter last slice is a split-K launch
+    const unsigned sops = K == used * len ? 0u : kOpsSplitK;
+    if (v == -1) select_config(used, M, N, len, &v, &c, sops, aligned);
     int count = 0;
     const ConfigEntry *cfgs = configs_of(v, &count);
     if (cfgs == nullptr) return fail(GEMM_F32_ENOKERNEL, "unknown variant %d", v);
     if (c == -1) {
         int vv = 0;
-        select_config(used, M, N, len, &vv, &c, kOpsSplitK, aligned);
+        select_config(used, M, N, len, &vv, &c, sops, aligned);
         if (vv != v) c = 0;
     }
     if (c < 0 || c >= count)

@@ -734,16 +734,19 @@ hipError_t launch_regs(const Problem &p, hipStream_t stream) {
     const int edge = whole && WHOLE ? 0 : clamp_ok ? 1 : 2;
     const dim3 gd(static_cast<unsigned>(grid)), bd(NT);
     if constexpr (PERSIST) {
-        // one workgroup per CU walks the tiles: no split-K slices (every
-        // tile the same K), a chunk's buffer offsets below 2^31 bytes, and
-        // whole tiles with K whole rounds of D chunks per group, or else
-        // (EDGE form) K and the rows of a k-major operand multiples of 4
-        const bool buf_ok = (p.ta ? 15 * p.lda + BM : (BM - 1) * p.lda + 16) < (int64_t{1} << 28) &&
-                            (p.tb ? (BN - 1) * p.ldb + 16 : 15 * p.ldb + BN) < (int64_t{1} << 28);
-        const bool whole_p = p.M % BM == 0 && p.N % BN == 0 && p.K % (16 * KG * D) == 0;
-        const bool edge_p = p.K % 4 == 0 && (!p.ta || (p.M % 4 == 0 && FM % 4 == 0)) &&
-                            (p.tb || (p.N % 4 == 0 && FN % 4 == 0));
-        if (p.ksplit == 0 && buf_ok && p.K > 0 && (whole_p || edge_p)) {
+        // one workgroup per CU walks the tiles: every tile the same K (split-K
+        // slices of equal length run as a batch of products of that length),
+        // a chunk's buffer offsets below 2^31 bytes, and whole tiles with K
+        // whole rounds of D chunks per group, or else (EDGE form) K and the
+        // rows of a k-major operand multiples of 4
+        Problem q = p;
+        if (p.ksplit > 0 && static_cast<int64_t>(p.batch) * p.ksplit == p.K) q.K = p.ksplit, q.ksplit = 0;
+        const bool buf_ok = (q.ta ? 15 * q.lda + BM : (BM - 1) * q.lda + 16) < (int64_t{1} << 28) &&
+                            (q.tb ? (BN - 1) * q.ldb + 16 : 15 * q.ldb + BN) < (int64_t{1} << 28);
+        const bool whole_p = q.M % BM == 0 && q.N % BN == 0 && q.K % (16 * KG * D) == 0;
+        const bool edge_p = q.K % 4 == 0 && (!q.ta || (q.M % 4 == 0 && FM % 4 == 0)) &&
+                            (q.tb || (q.N % 4 == 0 && FN % 4 == 0));
+        if (q.ksplit == 0 && buf_ok && q.K > 0 && (whole_p || edge_p)) {
             int dev = 0, cus = 0;
             hipError_t e = hipGetDevice(&dev);
             if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -751,8 +754,8 @@ hipError_t launch_regs(const Problem &p, hipStream_t stream) {
             const unsigned wgs = static_cast<unsigned>(grid < cus ? grid : cus);
 #define GEMM_REGS_P1(TA_, TB_, E)                                                                       \
     hipLaunchKernelGGL((gemm_mfma_regs_persistent_kernel<BM, BN, KG, D, TA_, TB_, E>), dim3(wgs), bd, 0, \
-                       stream, p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, p.C, p.ldc, tiles_m, tiles_n,     \
-                       GROUP_M, batch_of(p))
+                       stream, q.M, q.N, q.K, q.A, q.lda, q.B, q.ldb, q.C, q.ldc, tiles_m, tiles_n,     \
+                       GROUP_M, batch_of(q))
 #define GEMM_REGS_P(TA_, TB_)                                                          \
     do {                                                                               \
         if (whole_p) GEMM_REGS_P1(TA_, TB_, false);                                    \

@@ -212,7 +212,7 @@ int gemm_f32_ex(int variant, int config_id, int opA, int opB,
  *   variant, config_id  kernel of the partial products, as in gemm_f32_ex
  *                       (-1, -1: the library's choice)
  *   splits              1 .. 65535, or 0 for the library's choice (enough
- *                       256 x 256 tiles to give every CU of the GPU one, at
+ *                       128 x 128 tiles to give every CU of the GPU one, at
  *                       least 1024 k per split); one slice is the plain
  *                       product and needs no workspace
  *   workspace           device memory of at least

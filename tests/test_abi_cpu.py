@@ -260,8 +260,10 @@ def test_splitk_workspace_size(lib):
     assert f(10, 10, 32, 8) == 0
     assert f(10, 10, 100, 1) == 0
     assert f(0, 10, 100, 4) == 0 and f(-1, 10, 100, 4) == 0 and f(10, 10, 100, -1) == 0
-    # library choice (splits = 0): 16 tiles of 256 x 256 -> 16 splits when K allows
-    assert f(1024, 1024, 65536, 0) == 16 * 1024 * 1024 * 4
+    # library choice (splits = 0): 64 tiles of 128 x 128 -> 4 splits when K allows
+    assert f(1024, 1024, 65536, 0) == 4 * 1024 * 1024 * 4
+    assert f(512, 512, 65536, 0) == 16 * 512 * 512 * 4      # 16 tiles -> 16 splits
+    assert f(256, 128, 8192, 0) == 8 * 256 * 128 * 4        # 2 tiles, 8 by K
     assert f(1024, 1024, 4096, 0) == 4 * 1024 * 1024 * 4   # at least 1024 k per split
     assert f(1000, 1023, 777, 0) == 0                      # too little K: one slice
 

@@ -649,7 +649,8 @@ SPLITK_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4"), (1, 1, "lds_t32"),
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in (
         "mfma_64x64x32_w2x2_pa4_pb0", "mfma3_64x64x16_w2x2_swz_pb0", "mfma3_128x128x16_w2x2_swz_pb0",
         "mfma3d_128x256x16_w2x4_swz", "mfma2d_256x256x32_w4x4_swz", "mfma2d_64x64x64_w2x2_k4_swz",
-        "mfma2d_64x64x128_w2x2_k4_swz", "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2")]
+        "mfma2d_64x64x128_w2x2_k4_swz", "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2",
+        "mfmag_128x128x64_w1x1_k4_d2_p", "mfmag_96x128x64_w1x1_k4_d2_p")]
 
 
 @pytest.mark.parametrize("kernel", SPLITK_KERNELS, ids=[k[2] for k in SPLITK_KERNELS])
@@ -688,11 +689,37 @@ def test_splitk_full_tiles(kernel):
     assert_exact(to_host(out), oracle.gemm(A, B), f"{name} full tiles")
 
 
+# (M, N, K, splits): slices of equal length, which the persistent tiles run as
+# a batch of products (whole tiles, and the edge form)
+SPLITK_EQUAL = [(512, 512, 1024, 4), (300, 260, 1024, 4), (384, 256, 2048, 8), (1024, 1024, 8192, 0)]
+
+
+@pytest.mark.parametrize("kernel", [k for k in SPLITK_KERNELS if k[2] == "select" or k[2].endswith("_p")],
+                         ids=[k[2] for k in SPLITK_KERNELS if k[2] == "select" or k[2].endswith("_p")])
+@pytest.mark.parametrize("shape", SPLITK_EQUAL, ids=["x".join(map(str, s)) for s in SPLITK_EQUAL])
+def test_splitk_equal_slices(kernel, shape):
+    """Split-K whose slices all have the same length: the persistent tiles
+    take the partial products as one batched launch of products over K /
+    splits each.  Exact on integers, C inside a NaN guard band."""
+    import torch
+
+    M, N, K, splits = shape
+    v, c, name = kernel
+    log(f"split-K equal slices {M}x{N}x{K} / {splits} on {name}")
+    A, B = make_inputs(M, N, K, "int4", seed=47)
+    buf = torch.full((M, N + 3), float("nan"), device="cuda:0")
+    b.gemm_splitk(to_dev(A), to_dev(B), splits, buf[:, :N], variant=v, config=c)
+    host = to_host(buf)
+    assert_exact(host[:, :N], oracle.gemm(A, B), f"{name} {shape}")
+    assert np.isnan(host[:, N:]).all()
+
+
 SPLITK_WHOLE_K = [(None, -1, "select")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in (
         "mfma2_64x64x64_w2x2_k4_swz", "mfma2d_64x64x64_w2x2_k4_swz", "mfma2d_64x64x128_w2x2_k4_swz",
         "mfma4d_64x64x64_w2x2_k4_swz", "mfma2d_256x256x32_w4x4_swz_g4_il",
-        "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2")]
+        "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2", "mfmag_128x128x64_w1x1_k4_d2_p",
+        "mfmag_96x128x64_w1x1_k4_d2_p")]
 
 
 @pytest.mark.parametrize("kernel", SPLITK_WHOLE_K, ids=[k[2] for k in SPLITK_WHOLE_K])
