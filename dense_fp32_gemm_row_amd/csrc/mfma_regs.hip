@@ -813,7 +813,10 @@ const ConfigEntry kRegsConfigs[] = {
     // 128 x 128: 256 accumulator floats per lane
     {"mfmag_128x128x64_w1x1_k4_d2", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8>, kCapTransposed},
     // persistent where the shape allows (one workgroup per CU walks its
-    // tiles; for the 64 x 64 tile it gained nothing)
+    // tiles; for the 64 x 64 tile it gained nothing, and a 64 x 128 one, D 2
+    // or 4, ran within 1% of this tile from 2048^3 to 8192^3 and below the
+    // library's two-launch plans where this tile's rounds quantise badly:
+    // 4608^3 139.7 against 144.5, 5120^3 144.7 against 146.9 TFLOP/s)
     {"mfmag_128x128x64_w1x1_k4_d2_p", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8, true>, kCapTransposed},
     // 96 x 128: 768 tiles at 3072^3, three rounds of 256 (its edge form
     // takes A as stored; a transposed A runs whole tiles persistent, the

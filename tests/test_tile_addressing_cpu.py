@@ -487,19 +487,22 @@ def buf_offsets(kmajor, F, il, base, R, ld, K, c, q, edge, kchk):
     """Lane byte offsets (voffset + soffset) of piece q of chunk c, and for
     each of the 4 floats of every lane's 16-byte load the operand element
     (row, k) it stands for; (row-flavour piece q is block q, k-major piece q
-    is k row q, which loads F / 4 pieces)."""
+    is k row q, which loads F / 4 pieces of 4 floats and, when F % 4 == 2,
+    one of 2)."""
     lane = np.arange(64)
     g, i = lane // 16, lane % 16
     out = []
     if kmajor:
+        # runs of F floats: pieces of 4, then one of 2 when F % 4 == 2
         for p in range(0, F, 4):
+            width = min(4, F - p)
             col = base + F * i + p
             v = np.where(col < R, (4 * g * ld + F * i + p) * 4, OUT) if edge else (4 * g * ld + F * i + p) * 4
             k = 16 * c + 4 * g + q
             if edge and kchk:
                 v = np.where(k < K, v, OUT)
             off = np.where(v >= OUT, OUT, v + q * ld * 4)
-            out.append((off, [(col + e, k) for e in range(4)]))
+            out.append((off, [(col + e, k) for e in range(width)]))
     else:
         r = base + (F * i + q if il else 16 * q + i)
         v = np.where(r < R, ((r - base) * ld + 4 * g) * 4, OUT) if edge else ((r - base) * ld + 4 * g) * 4
@@ -568,26 +571,36 @@ def persistent_model(M, N, K, lda, ldb, ta, tb, BM=128, BN=128, KG=4, D=2, no_kc
 
 PERSISTENT_BUF_SHAPES = [  # M, N, K, ld pads
     (128, 128, 128, 0, 0), (256, 128, 384, 4, 8), (130, 132, 100, 0, 0), (300, 260, 388, 3, 0),
-    (4, 4, 20, 0, 0), (128, 132, 4, 0, 4), (129, 256, 256, 0, 0)]
+    (4, 4, 20, 0, 0), (128, 132, 4, 0, 4), (129, 256, 256, 0, 0), (192, 256, 512, 0, 0),
+    (96, 128, 256, 0, 4)]
 
 
+PERSISTENT_TILES = [(128, 128, 2), (96, 128, 2)]  # BM, BN, D of the persistent configurations
+
+
+@pytest.mark.parametrize("tile", PERSISTENT_TILES, ids=lambda t: f"{t[0]}x{t[1]}_d{t[2]}")
 @pytest.mark.parametrize("ops", ["NN", "NT", "TN", "TT"])
-def test_persistent_buffer_loads(ops):
+def test_persistent_buffer_loads(ops, tile):
     """The persistent tile's buffer loads, whole and edge forms: in-range
     lanes read their own element inside the operand, positions past M, N or
     K read zeros through an offset past the resource, and the groups cover
-    every k once.  Shapes the edge form does not take (K, or a k-major row
-    length, not a multiple of 4) are skipped, as the launcher skips them."""
+    every k once.  Shapes neither form takes (the edge form needs K, and a
+    k-major row length with its per-lane run, multiples of 4) are skipped,
+    as the launcher skips them."""
+    BM, BN, D = tile
+    FM, FN = BM // 16, BN // 16
     ta, tb = ops[0] == "T", ops[1] == "T"
     ran = 0
     for M, N, K, pa, pb in PERSISTENT_BUF_SHAPES:
-        whole = M % 128 == 0 and N % 128 == 0 and K % 128 == 0
-        if not whole and not (K % 4 == 0 and (not ta or M % 4 == 0) and (tb or N % 4 == 0)):
+        whole = M % BM == 0 and N % BN == 0 and K % (64 * D) == 0
+        edge_ok = (K % 4 == 0 and (not ta or (M % 4 == 0 and FM % 4 == 0))
+                   and (tb or (N % 4 == 0 and FN % 4 == 0)))
+        if not whole and not edge_ok:
             continue
         lda = (M if ta else K) + pa
         ldb = (K if tb else N) + pb
-        ran += persistent_model(M, N, K, lda, ldb, ta, tb) > 0
-    assert ran >= 5
+        ran += persistent_model(M, N, K, lda, ldb, ta, tb, BM=BM, BN=BN, D=D) > 0
+    assert ran >= (1 if ta and FM % 4 else 5)
 
 
 def test_persistent_buffer_model_sees_an_unchecked_tail():
