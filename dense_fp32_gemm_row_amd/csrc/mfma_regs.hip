@@ -615,8 +615,6 @@ void gemm_mfma_regs_persistent_kernel(
         t_chk = 0;
         while (t_chk + D < ng && CK * chunk_of(t_chk + 2 * D - 1) + CK <= K) t_chk += D;
     }
-    const bool vec_c = ((reinterpret_cast<uintptr_t>(C) | static_cast<uintptr_t>(ldc * 4)) &
-                        (4 * (FN < 4 ? FN : 4) - 1)) == 0;
     auto part = [&](int h, int q) { return red + (h * RP + q) * 64 * FN + lane * FN; };
 
     for (;;) {
@@ -656,6 +654,10 @@ void gemm_mfma_regs_persistent_kernel(
         // one-launch kernel (register r of block (f, j): row 16 f + 4 g + r,
         // or FM (4 g + r) + f with A transposed; column FN i + j)
         const int bcol = n0 + FN * i;
+        // vector stores where this product's C (its batch's, in a batch) and
+        // ldc keep the runs aligned
+        const bool vec_c = ((reinterpret_cast<uintptr_t>(c) | static_cast<uintptr_t>(ldc * 4)) &
+                            (4 * (FN < 4 ? FN : 4) - 1)) == 0;
 #pragma unroll
         for (int pass = 0; pass < FM * 4 / RP; ++pass) {
             lds_barrier();  // the previous reads of the LDS slots are done

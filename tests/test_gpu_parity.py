@@ -838,13 +838,16 @@ def test_persistent_register_direct_far_rows(kernel, operand, ld):
 
 @pytest.mark.parametrize("kernel", PERSISTENT, ids=[k[2] for k in PERSISTENT])
 @pytest.mark.parametrize("shape", [(512, 640, 384), (300, 260, 132)], ids=["whole", "edges"])
-def test_persistent_register_direct_batched(kernel, shape):
+@pytest.mark.parametrize("cpad", [3, 0], ids=["rows_padded", "odd_batch_stride"])
+def test_persistent_register_direct_batched(kernel, shape, cpad):
     """Three products in one persistent launch (tiles of all products on one
-    walk), whole tiles or the edge form, C rows padded, B shared (stride
-    0)."""
+    walk), whole tiles or the edge form, B shared (stride 0), and C either
+    with rows padded to an odd length or with aligned rows whose batch
+    stride is odd (the second and third products' C is then not 16-byte
+    aligned, which decides per product between vector and scalar stores)."""
     (M, N, K), nb = shape, 3
     rng = np.random.default_rng(72)
-    lda, ldb, ldc = K, N, N + 3
+    lda, ldb, ldc = K, N, N + cpad
     sa, sb, sc = M * lda + 5, 0, M * ldc + 7
     A3, As = _layout(rng, nb, M, K, lda, sa, "int4")
     B3, Bs = _layout(rng, 1, K, N, ldb, 0, "int4")
