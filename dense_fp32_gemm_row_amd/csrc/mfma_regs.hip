@@ -474,9 +474,13 @@ void gemm_mfma_regs_kernel(
         }
     };
     if constexpr (KG > 1) {
-        // red[group][wave of group][row of the pass][lane][j]: a lane's FN
-        // values of one row are adjacent
-        auto part = [&](int h, int q) { return red + ((h * NWG + wg) * RP + q) * 64 * FN + lane * FN; };
+        // red[group][wave of group][row of the pass]: a lane's FN values as
+        // FN / 4 pieces of 4 floats, piece p of all 64 lanes contiguous
+        // (16-byte lane stride, no bank conflicts); FN < 4: [lane][j]
+        auto part = [&](int h, int q, int p) {
+            const int slot = (h * NWG + wg) * RP + q;
+            return FN >= 4 ? red + ((slot * (FN / 4) + p) * 64 + lane) * 4 : red + slot * 64 * FN + lane * FN;
+        };
 #pragma unroll
         for (int pass = 0; pass < FM * 4 / RP; ++pass) {
             if (pass > 0) __syncthreads();  // the previous pass's reads are done
@@ -486,7 +490,14 @@ void gemm_mfma_regs_kernel(
                 float v[FN];
 #pragma unroll
                 for (int j = 0; j < FN; ++j) v[j] = acc[fr / 4][j][fr % 4];
-                store_run<FN>(part(kg, q), v);
+                if constexpr (FN >= 4) {
+#pragma unroll
+                    for (int p = 0; p < FN; p += 4)
+                        *reinterpret_cast<floatx4 *>(part(kg, q, p / 4)) =
+                            floatx4{v[p], v[p + 1], v[p + 2], v[p + 3]};
+                } else {
+                    store_run<FN>(part(kg, q, 0), v);
+                }
             }
             __syncthreads();
 #pragma unroll
@@ -496,18 +507,17 @@ void gemm_mfma_regs_kernel(
 #pragma unroll
                 for (int h = 0; h < KG; ++h) {
                     float x[FN];
-                    const float *src = part(h, q);
                     if constexpr (FN >= 4) {
 #pragma unroll
                         for (int p = 0; p < FN; p += 4) {
-                            const floatx4 t4 = *reinterpret_cast<const floatx4 *>(src + p);
+                            const floatx4 t4 = *reinterpret_cast<const floatx4 *>(part(h, q, p / 4));
                             x[p] = t4[0], x[p + 1] = t4[1], x[p + 2] = t4[2], x[p + 3] = t4[3];
                         }
                     } else if constexpr (FN == 2) {
-                        const floatx2 t2 = *reinterpret_cast<const floatx2 *>(src);
+                        const floatx2 t2 = *reinterpret_cast<const floatx2 *>(part(h, q, 0));
                         x[0] = t2[0], x[1] = t2[1];
                     } else {
-                        x[0] = src[0];
+                        x[0] = part(h, q, 0)[0];
                     }
 #pragma unroll
                     for (int j = 0; j < FN; ++j) v[j] = h == 0 ? x[j] : v[j] + x[j];
@@ -615,7 +625,13 @@ void gemm_mfma_regs_persistent_kernel(
         t_chk = 0;
         while (t_chk + D < ng && CK * chunk_of(t_chk + 2 * D - 1) + CK <= K) t_chk += D;
     }
-    auto part = [&](int h, int q) { return red + (h * RP + q) * 64 * FN + lane * FN; };
+    // slot of group h, pass row q: a lane's FN values as FN / 4 pieces of 4
+    // floats, piece p of all 64 lanes contiguous (16-byte lane stride, no
+    // bank conflicts); FN < 4: the lane's values adjacent
+    auto part = [&](int h, int q, int p) {
+        return FN >= 4 ? red + (((h * RP + q) * (FN / 4) + p) * 64 + lane) * 4
+                       : red + (h * RP + q) * 64 * FN + lane * FN;
+    };
 
     for (;;) {
 #pragma unroll
@@ -667,7 +683,14 @@ void gemm_mfma_regs_persistent_kernel(
                 float v[FN];
 #pragma unroll
                 for (int j = 0; j < FN; ++j) v[j] = acc[fr / 4][j][fr % 4];
-                store_run<FN>(part(kg, q), v);
+                if constexpr (FN >= 4) {
+#pragma unroll
+                    for (int p = 0; p < FN; p += 4)
+                        *reinterpret_cast<floatx4 *>(part(kg, q, p / 4)) =
+                            floatx4{v[p], v[p + 1], v[p + 2], v[p + 3]};
+                } else {
+                    store_run<FN>(part(kg, q, 0), v);
+                }
             }
             lds_barrier();
 #pragma unroll
@@ -678,18 +701,17 @@ void gemm_mfma_regs_persistent_kernel(
 #pragma unroll
                 for (int h = 0; h < KG; ++h) {
                     float x[FN];
-                    const float *src = part(h, q);
                     if constexpr (FN >= 4) {
 #pragma unroll
                         for (int p = 0; p < FN; p += 4) {
-                            const floatx4 t4 = *reinterpret_cast<const floatx4 *>(src + p);
+                            const floatx4 t4 = *reinterpret_cast<const floatx4 *>(part(h, q, p / 4));
                             x[p] = t4[0], x[p + 1] = t4[1], x[p + 2] = t4[2], x[p + 3] = t4[3];
                         }
                     } else if constexpr (FN == 2) {
-                        const floatx2 t2 = *reinterpret_cast<const floatx2 *>(src);
+                        const floatx2 t2 = *reinterpret_cast<const floatx2 *>(part(h, q, 0));
                         x[0] = t2[0], x[1] = t2[1];
                     } else {
-                        x[0] = src[0];
+                        x[0] = part(h, q, 0)[0];
                     }
 #pragma unroll
                     for (int j = 0; j < FN; ++j) v[j] = h == 0 ? x[j] : v[j] + x[j];
