@@ -79,14 +79,22 @@ def read_traffic(workload: str, config_name: str) -> float | None:
 
 
 def cpu_model() -> str | None:
+    """The first CPU's model name, with its family and model numbers (a
+    virtualised host may report only a generic name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block only
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
     except OSError:
-        pass
-    return None
+        return None
+    name = fields.get("model name")
+    if name and "cpu family" in fields and "model" in fields:
+        return f"{name} (family {fields['cpu family']}, model {fields['model']})"
+    return name
 
 
 def device_info(dev) -> dict:
