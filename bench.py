@@ -78,12 +78,12 @@ def read_traffic(workload: str, config_name: str) -> float | None:
     return float(val.group(1))
 
 
-def cpu_model() -> str | None:
+def cpu_model(path: str = "/proc/cpuinfo") -> str | None:
     """The first CPU's model name, with its family and model numbers (a
     virtualised host may report only a generic name)."""
     fields = {}
     try:
-        with open("/proc/cpuinfo") as f:
+        with open(path) as f:
             for line in f:
                 if not line.strip():
                     break  # the first processor's block only

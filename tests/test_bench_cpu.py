@@ -88,3 +88,14 @@ def test_oracle_leg_checks_every_cell_and_times_the_run():
     bad[5, 7] = np.nan
     par, _ = bench.oracle_leg(A, B, bad, 90.0, 15.0, check=True, baseline=False)
     assert not par["ok"]
+
+
+def test_cpu_model_reads_the_first_processor(tmp_path):
+    info = tmp_path / "cpuinfo"
+    info.write_text("processor\t: 0\nvendor_id\t: AuthenticAMD\ncpu family\t: 26\nmodel\t\t: 2\n"
+                    "model name\t: AMD EPYC\n\nprocessor\t: 1\ncpu family\t: 25\nmodel\t\t: 17\n"
+                    "model name\t: Other\n")
+    assert bench.cpu_model(str(info)) == "AMD EPYC (family 26, model 2)"
+    info.write_text("processor\t: 0\nmodel name\t: Some CPU\n")
+    assert bench.cpu_model(str(info)) == "Some CPU"
+    assert bench.cpu_model(str(tmp_path / "missing")) is None
