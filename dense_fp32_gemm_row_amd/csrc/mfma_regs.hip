@@ -834,6 +834,10 @@ const ConfigEntry kRegsConfigs[] = {
     // loads; with buffer loads, as the persistent tile runs them, the 64 x 64
     // tile gained nothing and the 128 x 128 one spilled registers).
     {"mfmag_64x64x64_w1x1_k4_d3", launch_regs<64, 64, 1, 1, 4, 3, 1, true, true, 8>, kCapTransposed},
+    // 16 x 16: 256 workgroups at 256^3 (3.64 us median in a kernel trace
+    // against 3.84 for the 16 x 16 LDS-staged tile; D 4 3.72, a 32 x 32
+    // tile 4.64)
+    {"mfmag_16x16x64_w1x1_k4_d2", launch_regs<16, 16, 1, 1, 4, 2, 1, true, true, 8>, kCapTransposed},
     // 128 x 128: 256 accumulator floats per lane
     {"mfmag_128x128x64_w1x1_k4_d2", launch_regs<128, 128, 1, 1, 4, 2, 1, true, false, 8>, kCapTransposed},
     // persistent where the shape allows (one workgroup per CU walks its

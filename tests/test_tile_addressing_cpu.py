@@ -332,7 +332,7 @@ def test_splitk_model_sees_the_unchecked_overrun():
 # clamped kernel (its last chunk a tail)
 REGS_TILES = [(64, 64, 1, 1, 4, True), (128, 128, 1, 1, 4, False), (128, 64, 1, 1, 4, True),
               (64, 64, 4, 1, 4, True), (64, 64, 2, 2, 4, True), (32, 64, 1, 1, 8, True),
-              (64, 64, 1, 1, 2, True), (64, 64, 1, 1, 1, True)]
+              (64, 64, 1, 1, 2, True), (64, 64, 1, 1, 1, True), (16, 16, 1, 1, 4, True)]
 REGS_SHAPES = [  # M, N, K, ld pad of A, ld pad of B
     (257, 259, 97, 0, 0), (64, 64, 64, 0, 0), (128, 64, 48, 0, 0), (65, 67, 17, 0, 0),
     (1, 1, 1, 0, 0), (3, 2, 5, 0, 0), (70, 3, 33, 2, 0), (5, 2, 100, 0, 0), (64, 1, 16, 0, 0),
