@@ -572,7 +572,8 @@ TRANS_CAPABLE = ["mfma2d_256x256x32_w4x4_swz", "mfma3d_256x128x32_w4x2_swz",
                  "mfma3_256x256x16_w4x4_swz_g4_il", "mfma2_64x64x64_w2x2_k4_swz",
                  "mfma2d_128x128x32_w2x2_swz_il", "mfma2r_64x64x64_w2x2_k4_swz",
                  "mfmag_64x64x64_w1x1_k4_d3", "mfmag_128x128x64_w1x1_k4_d2",
-                 "mfmag_128x128x64_w1x1_k4_d2_p", "mfmag_96x128x64_w1x1_k4_d2_p"] + [
+                 "mfmag_128x128x64_w1x1_k4_d2_p", "mfmag_96x128x64_w1x1_k4_d2_p",
+                 "mfmag_16x16x64_w1x1_k4_d2"] + [
     n for n in CONFIG_IDS if "_m16" in n]  # every 16x16x4 configuration takes them
 TRANS_KERNELS = [(None, -1, "select"), (0, 0, "naive_64x4")] + [
     (3, c, n) for v, c, n in ALL_CONFIGS if v == 3 and n in TRANS_CAPABLE]
